@@ -1,0 +1,482 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for the forward pass of one sparse
+ * mixture-of-experts (MoE) layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the bench's CPU-baseline
+ * leg use it.  It shares no code, header, table or constant with the HIP
+ * library; it defines its own descriptor, its own bf16 decoding and its own
+ * exp.  Every floating-point quantity is carried in double precision except
+ * where the method fixes fp32 (the routing key of the sigmoid router, see
+ * orc_sigmoid_key).
+ *
+ * Sources (the pages this follows; cited by title and section):
+ *  [L10]  "第 10 课：专家并行 EP" (learn.payai.win, train/lesson10), section
+ *         "核心概念" item 1 (router score s(x) = Softmax(TopK(x W_g, K)) or a
+ *         sigmoid normalisation; output y = sum over the top-K of s_i FFN_i(x)),
+ *         item 3 (pack rows per destination, group rows by local expert, run the
+ *         experts, return rows and take the gate-weighted sum), item 4 (aux loss
+ *         L_aux = alpha E sum_i f_i P_i, capacity C = CF K T / E with overflow
+ *         tokens dropped), and the worked example under "具体演示与数值推演".
+ *  [HAI]  "HAI-LLM MoE：一键实现大模型的混合专家并行训练" (maimai.cn), section
+ *         "HAI-LLM 上的使用": gate kinds (GShard top-2, Switch top-1), n_expert,
+ *         capacity_factor, alpha, top_k.
+ *  [VI10] "Chương 10: Song song MoE" (infra-guide), item 1 (E experts replace one
+ *         FFN, top-K per token, capacity factor and token dropping) and item 4
+ *         (aux loss, DeepSeek's bias-based balancing, capacity and drop/pad).
+ *  [MH]   "Multi-Head LatentMoE 与 Head 并行" (ai-stack.site), "核心方法与创新":
+ *         the token vector is split into heads and each head routes on its own.
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes): ties in the routing key go to the lower expert index; C is
+ * ceil(CF K T / E), except that a value within 1e-6 (relative) of an integer
+ * counts as that integer, so fp32 noise in CF cannot add a slot;
+ * the capacity queue of an expert is first-come by (sub-)token index; a dropped
+ * assignment contributes zero and the remaining weights are not renormalised;
+ * f_i = counts_i / (T K) counted before drops; P_i averages the full score
+ * distribution over all T tokens; SwiGLU = (silu(x Wg^T) * (x Wu^T)) Wd^T and
+ * GELU uses the exact erf form; no biases; the multi-head layer routes the
+ * contiguous d = h/H slice of each token with its own router and its own E
+ * experts, concatenates the head outputs and applies W_o.
+ *
+ * Layouts (the same bytes the HIP library receives):
+ *   x            [T][h]                  row-major, fp32 or bf16
+ *   w_router     [H][E][d]               one row of d inputs per expert (out-major)
+ *   w_gate,w_up  [H*E][f][d]             per expert: f rows of d inputs
+ *   w_down       [H*E][d][f]             per expert: d rows of f inputs
+ *   shared_*     same as one expert with d = h
+ *   w_o          [h][h]                  out-major
+ * so every linear map computes out[o] = sum_i in[i] * W[o][i].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- descriptor */
+typedef struct {
+    int32_t T, h, H, E, K, f;
+    int32_t n_shared, has_wo;
+    int32_t dtype; /* 0 = fp32, 1 = bf16 (activations and weights) */
+    int32_t score; /* 0 = softmax, 1 = sigmoid */
+    int32_t act;   /* 0 = SwiGLU, 1 = GELU */
+    float capacity_factor; /* <= 0 : no capacity limit */
+    float alpha;
+} orc_desc;
+
+typedef struct {
+    const void *w_router;    /* [H][E][d] */
+    const float *logit_bias; /* [H*E] or NULL: added to the logits (fp32 add) */
+    const float *select_bias;/* [H*E] or NULL: added to the sigmoid key only */
+    const void *w_gate, *w_up, *w_down;
+    const void *sh_gate, *sh_up, *sh_down; /* shared expert or NULL */
+    const void *w_o;                       /* [h][h] or NULL */
+} orc_weights;
+
+/* Optional outputs of orc_layer_forward; any pointer may be NULL. */
+typedef struct {
+    int32_t *topk_idx;  /* [T*H*K] */
+    double *topk_w;     /* [T*H*K] */
+    double *margin;     /* [T*H] */
+    int32_t *counts;    /* [H*E] */
+    int32_t *kept;      /* [H*E] */
+    int32_t *offsets;   /* [H*E+1] */
+    int32_t *dest_row;  /* [T*H*K] */
+    int32_t *src_sub;   /* [T*H*K] (first n_kept entries used) */
+    int32_t *n_kept;    /* [1] */
+    double *f;          /* [H*E] */
+    double *P;          /* [H*E] */
+    double *l_aux;      /* [1] */
+    float *logits;      /* [T*H*E] */
+} orc_aux;
+
+/* ------------------------------------------------------------ element access */
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float v;
+    memcpy(&v, &u, sizeof v);
+    return (double)v;
+}
+
+/* element i of an activation or weight array of the descriptor's dtype */
+static double ld(const void *p, int32_t dtype, int64_t i)
+{
+    if (dtype == 1) return bf16_bits_to_double(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+/* ----------------------------------------------- fp32 exp for the routing key
+ * The sigmoid router selects on sigma(l) + b in fp32.  For that selection to be
+ * reproducible bit for bit on another device, sigma must be a fixed sequence of
+ * fp32 operations.  This follows Cody and Waite's method (Software Manual for
+ * the Elementary Functions, 1980): n = nearest integer to x / ln 2,
+ * r = x - n ln 2 with ln 2 split into a 16-significant-bit head (so n * head is
+ * exact) and an fp32 tail, e^r by its Taylor series through r^7 in Horner form
+ * with fused multiply-adds, then scaling by 2^n.  The constants are the
+ * mathematical values rounded to fp32:
+ *   1/ln 2 -> 0x1.715476p+0, ln 2 head = 45426 / 2^16 = 0x1.62e4p-1,
+ *   ln 2 - head -> 0x1.7f7d1cp-20, 1/k! for k = 2..7.
+ * Defined for |x| <= 80, where 2^n stays a normal number.                   */
+float orc_exp_spec(float x)
+{
+    const float inv_ln2 = 0x1.715476p+0f;
+    const float ln2_hi = 0x1.62e4p-1f;
+    const float ln2_lo = 0x1.7f7d1cp-20f;
+    float n = rintf(x * inv_ln2);
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
+    float p = 0x1.a01a02p-13f;        /* 1/5040 */
+    p = fmaf(p, r, 0x1.6c16c2p-10f);  /* 1/720  */
+    p = fmaf(p, r, 0x1.111112p-7f);   /* 1/120  */
+    p = fmaf(p, r, 0x1.555556p-5f);   /* 1/24   */
+    p = fmaf(p, r, 0x1.555556p-3f);   /* 1/6    */
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)n);
+}
+
+/* sigma(l) = 1 / (1 + e^{-l}) in fp32 with the logit clamped to [-80, 80]. */
+float orc_sigmoid_spec(float l)
+{
+    float c = l < -80.0f ? -80.0f : (l > 80.0f ? 80.0f : l);
+    float e = orc_exp_spec(-c);
+    float den = 1.0f + e;
+    return 1.0f / den;
+}
+
+/* Routing key of the sigmoid router: fp32 sigma(l) plus the per-expert
+ * selection bias, one fp32 add (DeepSeek-style bias balancing, [VI10] item 4). */
+float orc_sigmoid_key(float l, float b)
+{
+    float s = orc_sigmoid_spec(l);
+    return s + b;
+}
+
+/* --------------------------------------------------------------- capacity
+ * [L10] item 4: C = CF * K * T / E per expert.  E is the number of experts a
+ * token chooses among (per head for the multi-head layer, where each head sees
+ * T sub-tokens).  Returns -1 for "no limit" (CF <= 0).                       */
+int64_t orc_capacity(const orc_desc *d)
+{
+    if (d->capacity_factor <= 0.0f) return -1;
+    double v = (double)d->capacity_factor * (double)d->K * (double)d->T / (double)d->E;
+    double r = nearbyint(v);
+    double tol = 1e-6 * (v > 1.0 ? v : 1.0);
+    if (fabs(v - r) <= tol) return (int64_t)r;
+    return (int64_t)ceil(v);
+}
+
+/* --------------------------------------------------------------- router GEMM
+ * [L10] item 1: the affinities of a token are x . W_g, one per expert.  For the
+ * multi-head layer ([MH]) sub-token s = t*H + g uses the g-th slice of x and
+ * router g.  Output logits[s][e] rounded once from fp64 to fp32.           */
+void orc_logits(const orc_desc *d, const void *x, const void *w_router, float *logits)
+{
+    const int32_t T = d->T, H = d->H, E = d->E, dd = d->h / d->H;
+    int64_t s;
+#pragma omp parallel for schedule(static)
+    for (s = 0; s < (int64_t)T * H; ++s) {
+        int64_t t = s / H, g = s % H;
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < dd; ++j)
+                acc += ld(x, d->dtype, t * d->h + g * dd + j) *
+                       ld(w_router, d->dtype, ((int64_t)g * E + e) * dd + j);
+            logits[s * E + e] = (float)acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------ selection and weights
+ * For every sub-token: the biased logit l' = l + logit_bias (one fp32 add),
+ * the routing key (l' for softmax, sigma(l') + select_bias for sigmoid), the K
+ * experts with the largest keys (ties to the lower index), listed by key
+ * descending; the gate weights over the selected set ([L10] item 1):
+ *   softmax: w_k = exp(l'_k) / sum_{j in S} exp(l'_j)
+ *   sigmoid: w_k = sigma(l'_k) / sum_{j in S} sigma(l'_j)   (unbiased sigma)
+ * with sigma in exact double here; the margin key_(K) - key_(K+1) (+inf when
+ * K = E); counts per expert; and psum_e = sum over sub-tokens of the full
+ * score distribution (softmax over all E, or sigma_e / sum_all sigma).      */
+static int key_before(float ka, int ea, float kb, int eb)
+{
+    if (ka > kb) return 1;
+    if (ka < kb) return 0;
+    return ea < eb;
+}
+
+void orc_select(const orc_desc *d, const float *logits, const float *logit_bias,
+                const float *select_bias, int32_t *topk_idx, double *topk_w,
+                double *margin, int32_t *counts, double *psum)
+{
+    const int32_t T = d->T, H = d->H, E = d->E, K = d->K;
+    const int64_t S = (int64_t)T * H;
+    float *keys = (float *)malloc(sizeof(float) * (size_t)S * E);
+    float *lb = (float *)malloc(sizeof(float) * (size_t)S * E);
+    int64_t s;
+#pragma omp parallel for schedule(static)
+    for (s = 0; s < S; ++s) {
+        int64_t g = s % H;
+        for (int32_t e = 0; e < E; ++e) {
+            float l = logits[s * E + e];
+            float lbias = logit_bias ? logit_bias[g * E + e] : 0.0f;
+            float lp = logit_bias ? l + lbias : l;
+            lb[s * E + e] = lp;
+            if (d->score == 1) {
+                float b = select_bias ? select_bias[g * E + e] : 0.0f;
+                keys[s * E + e] = select_bias ? orc_sigmoid_key(lp, b) : orc_sigmoid_spec(lp);
+            } else {
+                keys[s * E + e] = lp;
+            }
+        }
+    }
+    for (s = 0; s < S; ++s) {
+        int64_t g = s % H;
+        const float *ks = keys + s * E;
+        const float *ls = lb + s * E;
+        /* selection by repeated arg-max under the (key desc, index asc) order */
+        int32_t chosen[4096];
+        unsigned char *used = (unsigned char *)calloc((size_t)E, 1);
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (used[e]) continue;
+                if (best < 0 || key_before(ks[e], e, ks[best], best)) best = e;
+            }
+            used[best] = 1;
+            chosen[k] = best;
+        }
+        int32_t next = -1;
+        for (int32_t e = 0; e < E; ++e) {
+            if (used[e]) continue;
+            if (next < 0 || key_before(ks[e], e, ks[next], next)) next = e;
+        }
+        free(used);
+        if (margin)
+            margin[s] = next < 0 ? INFINITY : (double)ks[chosen[K - 1]] - (double)ks[next];
+        /* gate weights over the selected set */
+        double wsum = 0.0, wv[4096];
+        if (d->score == 1) {
+            for (int32_t k = 0; k < K; ++k) {
+                wv[k] = 1.0 / (1.0 + exp(-(double)ls[chosen[k]]));
+                wsum += wv[k];
+            }
+        } else {
+            double m = -INFINITY;
+            for (int32_t k = 0; k < K; ++k) m = fmax(m, (double)ls[chosen[k]]);
+            for (int32_t k = 0; k < K; ++k) {
+                wv[k] = exp((double)ls[chosen[k]] - m);
+                wsum += wv[k];
+            }
+        }
+        for (int32_t k = 0; k < K; ++k) {
+            topk_idx[s * K + k] = (int32_t)(g * E + chosen[k]);
+            topk_w[s * K + k] = wv[k] / wsum;
+            if (counts) counts[g * E + chosen[k]] += 1;
+        }
+        /* full score distribution for the aux statistics */
+        if (psum) {
+            double tot = 0.0;
+            if (d->score == 1) {
+                for (int32_t e = 0; e < E; ++e) tot += 1.0 / (1.0 + exp(-(double)ls[e]));
+                for (int32_t e = 0; e < E; ++e)
+                    psum[g * E + e] += (1.0 / (1.0 + exp(-(double)ls[e]))) / tot;
+            } else {
+                double m = -INFINITY;
+                for (int32_t e = 0; e < E; ++e) m = fmax(m, (double)ls[e]);
+                for (int32_t e = 0; e < E; ++e) tot += exp((double)ls[e] - m);
+                for (int32_t e = 0; e < E; ++e) psum[g * E + e] += exp((double)ls[e] - m) / tot;
+            }
+        }
+    }
+    free(keys);
+    free(lb);
+}
+
+/* ------------------------------------------------------ capacity and permute
+ * [L10] items 3-4: rows are grouped by expert; an expert keeps at most C of the
+ * assignments sent to it and drops the rest.  The queue of expert e is ordered
+ * by sub-token index (an expert appears at most once in a sub-token's top-K),
+ * so pos(s, k) is the number of earlier sub-tokens that chose the same expert.
+ *   counts[e]  assignments to e before drops
+ *   kept[e]    min(counts[e], C)
+ *   offsets    exclusive prefix sum of kept (length H*E+1)
+ *   dest_row   offsets[e] + pos if pos < C else -1
+ *   src_sub    the sub-token that fills each kept row                        */
+void orc_permute(const orc_desc *d, const int32_t *topk_idx, int64_t capacity,
+                 int32_t *counts, int32_t *kept, int32_t *offsets, int32_t *dest_row,
+                 int32_t *src_sub, int32_t *n_kept)
+{
+    const int32_t Et = d->H * d->E, K = d->K;
+    const int64_t S = (int64_t)d->T * d->H;
+    int64_t *seen = (int64_t *)calloc((size_t)Et, sizeof(int64_t));
+    for (int32_t e = 0; e < Et; ++e) counts[e] = 0;
+    for (int64_t a = 0; a < S * K; ++a) counts[topk_idx[a]] += 1;
+    offsets[0] = 0;
+    for (int32_t e = 0; e < Et; ++e) {
+        int64_t c = counts[e];
+        kept[e] = (int32_t)((capacity >= 0 && c > capacity) ? capacity : c);
+        offsets[e + 1] = offsets[e] + kept[e];
+    }
+    for (int64_t s = 0; s < S; ++s) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t e = topk_idx[s * K + k];
+            int64_t pos = seen[e]++;
+            if (capacity >= 0 && pos >= capacity) {
+                dest_row[s * K + k] = -1;
+            } else {
+                int32_t row = offsets[e] + (int32_t)pos;
+                dest_row[s * K + k] = row;
+                src_sub[row] = (int32_t)s;
+            }
+        }
+    }
+    *n_kept = offsets[Et];
+    free(seen);
+}
+
+/* ------------------------------------------------------------- expert FFN
+ * One row through one expert ([VI10] item 1: each expert is an ordinary FFN):
+ *   SwiGLU: a = x W1^T, u = x W3^T, hdn = silu(a) * u, out = hdn W2^T,
+ *           silu(z) = z / (1 + e^{-z})
+ *   GELU:   a = x W1^T, hdn = a * (1 + erf(a / sqrt 2)) / 2, out = hdn W2^T
+ * W1, W3: [f][din]; W2: [din][f]; all in double.                            */
+void orc_expert_ffn(int32_t dtype, int32_t act, int32_t din, int32_t f,
+                    const void *w1, const void *w3, const void *w2,
+                    const double *xin, double *out)
+{
+    double *hdn = (double *)malloc(sizeof(double) * (size_t)f);
+    for (int32_t j = 0; j < f; ++j) {
+        double a = 0.0;
+        for (int32_t i = 0; i < din; ++i) a += xin[i] * ld(w1, dtype, (int64_t)j * din + i);
+        if (act == 0) {
+            double u = 0.0;
+            for (int32_t i = 0; i < din; ++i) u += xin[i] * ld(w3, dtype, (int64_t)j * din + i);
+            hdn[j] = a / (1.0 + exp(-a)) * u;
+        } else {
+            hdn[j] = 0.5 * a * (1.0 + erf(a / sqrt(2.0)));
+        }
+    }
+    for (int32_t o = 0; o < din; ++o) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < f; ++j) acc += hdn[j] * ld(w2, dtype, (int64_t)o * f + j);
+        out[o] = acc;
+    }
+    free(hdn);
+}
+
+/* ------------------------------------------------------------- whole layer
+ * [L10] item 1 and item 3: route every token, apply the capacity, then for each
+ * requested token t: y[t] = sum over kept (k) of w_k FFN_{e_k}(x[t]) (per head
+ * on the head's slice), plus the always-on shared expert (weight 1, no
+ * capacity), then the output projection W_o over the concatenated heads.
+ * tokens == NULL computes every token.  y is written unrounded, in double.
+ * Aux statistics ([L10] item 4): f = counts / (T K), P = psum / T,
+ * L_aux = alpha * E * sum_e f_e P_e, averaged over heads.                     */
+int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
+                      const int32_t *tokens, int32_t n_tokens, double *y, orc_aux *aux)
+{
+    const int32_t T = d->T, h = d->h, H = d->H, E = d->E, K = d->K, f = d->f;
+    const int32_t dd = h / H, Et = H * E;
+    const int64_t S = (int64_t)T * H, A = S * K;
+    if (H <= 0 || h % H != 0 || K <= 0 || K > E || E > 4096) return 1;
+
+    float *logits = (float *)malloc(sizeof(float) * (size_t)(S * E + 1));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    double *wts = (double *)malloc(sizeof(double) * (size_t)(A + 1));
+    double *mrg = (double *)malloc(sizeof(double) * (size_t)(S + 1));
+    int32_t *cnt = (int32_t *)calloc((size_t)Et, sizeof(int32_t));
+    int32_t *kep = (int32_t *)calloc((size_t)Et, sizeof(int32_t));
+    int32_t *off = (int32_t *)calloc((size_t)Et + 1, sizeof(int32_t));
+    int32_t *dst = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    int32_t *src = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    double *psum = (double *)calloc((size_t)Et, sizeof(double));
+    int32_t nk = 0;
+
+    orc_logits(d, x, w->w_router, logits);
+    orc_select(d, logits, w->logit_bias, w->select_bias, idx, wts, mrg, NULL, psum);
+    orc_permute(d, idx, orc_capacity(d), cnt, kep, off, dst, src, &nk);
+
+    int32_t nt = tokens ? n_tokens : T;
+    int32_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nt; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        double *xin = (double *)malloc(sizeof(double) * (size_t)h);
+        double *cat = (double *)calloc((size_t)h, sizeof(double));
+        double *o = (double *)malloc(sizeof(double) * (size_t)h);
+        for (int32_t j = 0; j < h; ++j) xin[j] = ld(x, d->dtype, t * h + j);
+        for (int32_t g = 0; g < H; ++g) {
+            int64_t s = t * H + g;
+            for (int32_t k = 0; k < K; ++k) {
+                if (dst[s * K + k] < 0) continue; /* dropped: contributes 0 */
+                int64_t e = idx[s * K + k];
+                size_t wsz = d->dtype == 1 ? 2 : 4;
+                const char *w1 = (const char *)w->w_gate + (size_t)e * f * dd * wsz;
+                const char *w3 = d->act == 0 ? (const char *)w->w_up + (size_t)e * f * dd * wsz : NULL;
+                const char *w2 = (const char *)w->w_down + (size_t)e * dd * f * wsz;
+                orc_expert_ffn(d->dtype, d->act, dd, f, w1, w3, w2, xin + g * dd, o);
+                for (int32_t j = 0; j < dd; ++j) cat[g * dd + j] += wts[s * K + k] * o[j];
+            }
+        }
+        if (d->n_shared > 0) {
+            orc_expert_ffn(d->dtype, d->act, h, f, w->sh_gate, w->sh_up, w->sh_down, xin, o);
+            for (int32_t j = 0; j < h; ++j) cat[j] += o[j];
+        }
+        if (d->has_wo) {
+            for (int32_t r = 0; r < h; ++r) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < h; ++j) acc += cat[j] * ld(w->w_o, d->dtype, (int64_t)r * h + j);
+                y[(int64_t)i * h + r] = acc;
+            }
+        } else {
+            for (int32_t j = 0; j < h; ++j) y[(int64_t)i * h + j] = cat[j];
+        }
+        free(xin);
+        free(cat);
+        free(o);
+    }
+
+    if (aux) {
+        if (aux->topk_idx) memcpy(aux->topk_idx, idx, sizeof(int32_t) * (size_t)A);
+        if (aux->topk_w) memcpy(aux->topk_w, wts, sizeof(double) * (size_t)A);
+        if (aux->margin) memcpy(aux->margin, mrg, sizeof(double) * (size_t)S);
+        if (aux->counts) memcpy(aux->counts, cnt, sizeof(int32_t) * (size_t)Et);
+        if (aux->kept) memcpy(aux->kept, kep, sizeof(int32_t) * (size_t)Et);
+        if (aux->offsets) memcpy(aux->offsets, off, sizeof(int32_t) * (size_t)(Et + 1));
+        if (aux->dest_row) memcpy(aux->dest_row, dst, sizeof(int32_t) * (size_t)A);
+        if (aux->src_sub) memcpy(aux->src_sub, src, sizeof(int32_t) * (size_t)nk);
+        if (aux->n_kept) *aux->n_kept = nk;
+        if (aux->logits) memcpy(aux->logits, logits, sizeof(float) * (size_t)(S * E));
+        double laux = 0.0;
+        for (int32_t g = 0; g < H; ++g) {
+            double sfp = 0.0;
+            for (int32_t e = 0; e < E; ++e) {
+                double fe = (double)cnt[g * E + e] / ((double)T * K);
+                double pe = T > 0 ? psum[g * E + e] / (double)T : 0.0;
+                if (aux->f) aux->f[g * E + e] = fe;
+                if (aux->P) aux->P[g * E + e] = pe;
+                sfp += fe * pe;
+            }
+            laux += (double)d->alpha * E * sfp;
+        }
+        if (aux->l_aux) *aux->l_aux = laux / H;
+    }
+    free(logits); free(idx); free(wts); free(mrg); free(cnt); free(kep);
+    free(off); free(dst); free(src); free(psum);
+    return 0;
+}
+
+/* number of threads the oracle's parallel loops use */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

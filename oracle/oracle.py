@@ -1,0 +1,286 @@
+"""Python face of the CPU oracle for the forward pass of one sparse MoE layer.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU
+baseline may import this module; the product path (the HIP library and its
+binding) never does.  The arithmetic lives in moe_oracle.c (plain C, fp64);
+this module only marshals numpy arrays, plus the pure-Python load-imbalance
+report of the worked example in lesson 10 of the expert-parallelism course
+("第 10 课：专家并行 EP", learn.payai.win), section "具体演示与数值推演" and its
+code exercise (expert-to-rank map, per-rank load, max/mean imbalance, routed
+volume).
+
+Arrays in bf16 are passed as numpy uint16 holding the raw bf16 bits.
+A layer configuration is a plain dict with keys
+  T, h, H, E, K, f, n_shared, has_wo, dtype ('f32'|'bf16'),
+  score ('softmax'|'sigmoid'), act ('swiglu'|'gelu'), capacity_factor, alpha.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+
+class OrcDesc(C.Structure):
+    _fields_ = [
+        ("T", C.c_int32), ("h", C.c_int32), ("H", C.c_int32), ("E", C.c_int32),
+        ("K", C.c_int32), ("f", C.c_int32), ("n_shared", C.c_int32),
+        ("has_wo", C.c_int32), ("dtype", C.c_int32), ("score", C.c_int32),
+        ("act", C.c_int32), ("capacity_factor", C.c_float), ("alpha", C.c_float),
+    ]
+
+
+class OrcWeights(C.Structure):
+    _fields_ = [
+        ("w_router", C.c_void_p), ("logit_bias", C.c_void_p), ("select_bias", C.c_void_p),
+        ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
+        ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
+        ("w_o", C.c_void_p),
+    ]
+
+
+class OrcAux(C.Structure):
+    _fields_ = [
+        ("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("margin", C.c_void_p),
+        ("counts", C.c_void_p), ("kept", C.c_void_p), ("offsets", C.c_void_p),
+        ("dest_row", C.c_void_p), ("src_sub", C.c_void_p), ("n_kept", C.c_void_p),
+        ("f", C.c_void_p), ("P", C.c_void_p), ("l_aux", C.c_void_p), ("logits", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            import importlib.util
+            spec = importlib.util.spec_from_file_location("_oracle_build", os.path.join(HERE, "build.py"))
+            mod = importlib.util.module_from_spec(spec)
+            spec.loader.exec_module(mod)
+            mod.build()
+        _lib = C.CDLL(LIB_PATH)
+        _lib.orc_exp_spec.restype = C.c_float
+        _lib.orc_exp_spec.argtypes = [C.c_float]
+        _lib.orc_sigmoid_spec.restype = C.c_float
+        _lib.orc_sigmoid_spec.argtypes = [C.c_float]
+        _lib.orc_sigmoid_key.restype = C.c_float
+        _lib.orc_sigmoid_key.argtypes = [C.c_float, C.c_float]
+        _lib.orc_capacity.restype = C.c_int64
+        _lib.orc_capacity.argtypes = [C.POINTER(OrcDesc)]
+        _lib.orc_logits.restype = None
+        _lib.orc_logits.argtypes = [C.POINTER(OrcDesc), C.c_void_p, C.c_void_p, C.c_void_p]
+        _lib.orc_select.restype = None
+        _lib.orc_select.argtypes = [C.POINTER(OrcDesc)] + [C.c_void_p] * 8
+        _lib.orc_permute.restype = None
+        _lib.orc_permute.argtypes = [C.POINTER(OrcDesc), C.c_void_p, C.c_int64] + [C.c_void_p] * 6
+        _lib.orc_expert_ffn.restype = None
+        _lib.orc_expert_ffn.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 5
+        _lib.orc_layer_forward.restype = C.c_int
+        _lib.orc_layer_forward.argtypes = [C.POINTER(OrcDesc), C.POINTER(OrcWeights), C.c_void_p,
+                                           C.c_void_p, C.c_int32, C.c_void_p, C.POINTER(OrcAux)]
+        _lib.orc_num_threads.restype = C.c_int
+        _lib.orc_num_threads.argtypes = []
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def desc(cfg, T=None):
+    return OrcDesc(
+        T=int(cfg["T"] if T is None else T), h=int(cfg["h"]), H=int(cfg.get("H", 1)),
+        E=int(cfg["E"]), K=int(cfg["K"]), f=int(cfg["f"]),
+        n_shared=int(cfg.get("n_shared", 0)), has_wo=int(cfg.get("has_wo", 0)),
+        dtype=1 if cfg["dtype"] == "bf16" else 0,
+        score=1 if cfg.get("score", "softmax") == "sigmoid" else 0,
+        act=1 if cfg.get("act", "swiglu") == "gelu" else 0,
+        capacity_factor=float(cfg.get("capacity_factor", 0.0)),
+        alpha=float(cfg.get("alpha", 0.01)),
+    )
+
+
+def _elem(cfg):
+    return np.uint16 if cfg["dtype"] == "bf16" else np.float32
+
+
+def _chk(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+# ------------------------------------------------------------------ scalars
+def exp_spec(x):
+    """fp32 exp of the sigmoid routing key (Cody-Waite reduction + Taylor)."""
+    x = np.asarray(x, dtype=np.float32).ravel()
+    L = lib()
+    return np.array([L.orc_exp_spec(float(v)) for v in x], dtype=np.float32)
+
+
+def sigmoid_spec(x):
+    x = np.asarray(x, dtype=np.float32).ravel()
+    L = lib()
+    return np.array([L.orc_sigmoid_spec(float(v)) for v in x], dtype=np.float32)
+
+
+def sigmoid_key(l, b):
+    return np.float32(lib().orc_sigmoid_key(float(l), float(b)))
+
+
+def capacity(cfg, T=None):
+    """C = CF*K*T/E rounded up (guarded); None means no limit."""
+    c = lib().orc_capacity(C.byref(desc(cfg, T)))
+    return None if c < 0 else int(c)
+
+
+# ------------------------------------------------------------------ stages
+def logits(cfg, x, w_router, T=None):
+    d = desc(cfg, T)
+    S = d.T * d.H
+    x = _chk(x, _elem(cfg))
+    w_router = _chk(w_router, _elem(cfg))
+    out = np.empty((S, d.E), dtype=np.float32)
+    lib().orc_logits(C.byref(d), _p(x), _p(w_router), _p(out))
+    return out
+
+
+def select(cfg, logits_, logit_bias=None, select_bias=None, T=None):
+    d = desc(cfg, T)
+    S = d.T * d.H
+    lg = _chk(logits_, np.float32)
+    assert lg.size == S * d.E
+    lb = None if logit_bias is None else _chk(logit_bias, np.float32)
+    sb = None if select_bias is None else _chk(select_bias, np.float32)
+    idx = np.empty((S, d.K), dtype=np.int32)
+    w = np.empty((S, d.K), dtype=np.float64)
+    margin = np.empty(S, dtype=np.float64)
+    counts = np.zeros(d.H * d.E, dtype=np.int32)
+    psum = np.zeros(d.H * d.E, dtype=np.float64)
+    lib().orc_select(C.byref(d), _p(lg), _p(lb), _p(sb), _p(idx), _p(w), _p(margin),
+                     _p(counts), _p(psum))
+    return dict(topk_idx=idx, topk_w=w, margin=margin, counts=counts, psum=psum)
+
+
+def permute(cfg, topk_idx, cap, T=None):
+    """cap: int capacity or None for no limit."""
+    d = desc(cfg, T)
+    Et = d.H * d.E
+    A = d.T * d.H * d.K
+    idx = _chk(topk_idx, np.int32).ravel()
+    assert idx.size == A
+    counts = np.zeros(Et, dtype=np.int32)
+    kept = np.zeros(Et, dtype=np.int32)
+    offsets = np.zeros(Et + 1, dtype=np.int32)
+    dest = np.empty(A, dtype=np.int32)
+    src = np.full(max(A, 1), -1, dtype=np.int32)
+    nk = np.zeros(1, dtype=np.int32)
+    lib().orc_permute(C.byref(d), _p(idx), -1 if cap is None else int(cap), _p(counts), _p(kept),
+                      _p(offsets), _p(dest), _p(src), _p(nk))
+    n = int(nk[0])
+    return dict(counts=counts, kept=kept, offsets=offsets, dest_row=dest, src_sub=src[:n], n_kept=n)
+
+
+def expert_ffn(cfg, din, w1, w3, w2, xin):
+    """Rows xin [n, din] (float64) through one expert; returns [n, din] float64."""
+    el = _elem(cfg)
+    act = 1 if cfg.get("act", "swiglu") == "gelu" else 0
+    dt = 1 if cfg["dtype"] == "bf16" else 0
+    w1 = _chk(w1, el)
+    w2 = _chk(w2, el)
+    w3 = None if act == 1 else _chk(w3, el)
+    xin = np.ascontiguousarray(np.atleast_2d(xin), dtype=np.float64)
+    f = w1.size // din
+    out = np.empty_like(xin)
+    L = lib()
+    for r in range(xin.shape[0]):
+        L.orc_expert_ffn(dt, act, din, f, _p(w1), _p(w3), _p(w2), _p(xin[r]), _p(out[r]))
+    return out
+
+
+def layer_forward(cfg, weights, x, tokens=None, T=None):
+    """Whole layer.  weights: dict with numpy arrays (keys as in OrcWeights).
+    Returns dict with y [n_tokens, h] float64 and the routing/aux arrays."""
+    d = desc(cfg, T)
+    el = _elem(cfg)
+    S = d.T * d.H
+    A = S * d.K
+    Et = d.H * d.E
+    keep = []
+
+    def ptr(name, dtype):
+        a = weights.get(name)
+        if a is None:
+            return None
+        a = _chk(a, dtype)
+        keep.append(a)
+        return a.ctypes.data
+
+    W = OrcWeights(
+        w_router=ptr("w_router", el), logit_bias=ptr("logit_bias", np.float32),
+        select_bias=ptr("select_bias", np.float32), w_gate=ptr("w_gate", el),
+        w_up=ptr("w_up", el), w_down=ptr("w_down", el), sh_gate=ptr("sh_gate", el),
+        sh_up=ptr("sh_up", el), sh_down=ptr("sh_down", el), w_o=ptr("w_o", el),
+    )
+    x = _chk(x, el)
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    nt = d.T if tok is None else tok.size
+    y = np.zeros((nt, d.h), dtype=np.float64)
+    out = dict(
+        topk_idx=np.empty((S, d.K), np.int32), topk_w=np.empty((S, d.K), np.float64),
+        margin=np.empty(S, np.float64), counts=np.empty(Et, np.int32), kept=np.empty(Et, np.int32),
+        offsets=np.empty(Et + 1, np.int32), dest_row=np.empty(A, np.int32),
+        src_sub=np.full(max(A, 1), -1, np.int32), n_kept=np.zeros(1, np.int32),
+        f=np.empty(Et, np.float64), P=np.empty(Et, np.float64), l_aux=np.zeros(1, np.float64),
+        logits=np.empty((S, d.E), np.float32),
+    )
+    aux = OrcAux(**{k: _p(v) for k, v in out.items()})
+    rc = lib().orc_layer_forward(C.byref(d), C.byref(W), _p(x), _p(tok), nt, _p(y), C.byref(aux))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer description")
+    out["n_kept"] = int(out["n_kept"][0])
+    out["src_sub"] = out["src_sub"][: out["n_kept"]]
+    out["l_aux"] = float(out["l_aux"][0])
+    out["y"] = y
+    return out
+
+
+def num_threads():
+    return int(lib().orc_num_threads())
+
+
+# ------------------------------------------- expert-parallel load report
+# The course's exercise: expert e lives on rank e // experts_per_rank, a rank's
+# load is the sum of its experts' token counts, the imbalance ratio is
+# max / mean of the per-rank loads, the routed volume (an upper bound on what
+# crosses the network) is the total of the token counts, and the hardware
+# utilisation when every rank waits for the slowest is sum / (ranks * max).
+def expert_to_rank(num_experts, experts_per_rank):
+    return {e: e // experts_per_rank for e in range(num_experts)}
+
+
+def load_per_rank(tokens_per_expert, experts_per_rank):
+    ranks = len(tokens_per_expert) // experts_per_rank
+    loads = [0] * ranks
+    owner = expert_to_rank(len(tokens_per_expert), experts_per_rank)
+    for e, n in enumerate(tokens_per_expert):
+        loads[owner[e]] += n
+    return loads
+
+
+def imbalance(loads):
+    if not loads or sum(loads) == 0:
+        raise ValueError("loads must be non-empty with a positive total")
+    return max(loads) / (sum(loads) / len(loads))
+
+
+def routing_volume(tokens_per_expert):
+    return sum(tokens_per_expert)
+
+
+def utilisation(loads):
+    return sum(loads) / (len(loads) * max(loads))
