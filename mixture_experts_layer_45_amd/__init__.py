@@ -1,7 +1,136 @@
 """MI355X-native forward pass of one sparse mixture-of-experts layer.
 
 The layer runs as hand-written HIP kernels for gfx950 behind a C ABI
-(include/moe.h, built into libmoe.so).  This package is the thin Python
-binding over that ABI (argument marshalling only) plus the seeded input
-generators; PyTorch supplies device memory and streams.
+(include/moe.h, built into libmoe.so).  This module is the thin Python binding
+over that ABI: each function has the name of its C entry point, turns torch
+device tensors into pointers and the current torch stream into a hipStream_t,
+and raises MoeError on a non-zero status.  It computes nothing itself; PyTorch
+only supplies device memory and streams.
 """
+import ctypes as C
+
+from . import _ffi
+from ._ffi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FFN_GEMM1, MOE_FFN_GEMM2, MOE_GELU,  # noqa: F401
+                   MOE_LOGITS_IN, MOE_LOGITS_OUT, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU,
+                   MOE_WS_FFN, MOE_WS_LAYER, MOE_WS_PERMUTE, MOE_WS_ROUTE, MoeAux, MoeDesc,
+                   MoeWeights)
+
+__all__ = [
+    "MoeError", "MoeDesc", "desc_from_cfg", "moe_capacity", "moe_workspace_size", "moe_route",
+    "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_version", "lib",
+    "workspace",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        self.detail = detail
+        name = _ffi.lib().moe_status_string(status).decode()
+        super().__init__(f"{name} (status {status}): {detail}")
+
+
+def lib():
+    return _ffi.lib()
+
+
+def moe_version():
+    return lib().moe_version().decode()
+
+
+def desc_from_cfg(cfg, T=None):
+    """MoeDesc from a workload dict (keys as in inputs.CONFIGS)."""
+    return MoeDesc(
+        T=int(cfg["T"] if T is None else T), h=int(cfg["h"]), H=int(cfg.get("H", 1)),
+        E=int(cfg["E"]), K=int(cfg["K"]), f=int(cfg["f"]), n_shared=int(cfg.get("n_shared", 0)),
+        has_wo=int(cfg.get("has_wo", 0)), dtype=MOE_BF16 if cfg["dtype"] == "bf16" else MOE_F32,
+        score=MOE_SIGMOID if cfg.get("score", "softmax") == "sigmoid" else MOE_SOFTMAX,
+        act=MOE_GELU if cfg.get("act", "swiglu") == "gelu" else MOE_SWIGLU,
+        capacity_factor=float(cfg.get("capacity_factor", 0.0)), aux_alpha=float(cfg.get("alpha", 0.01)),
+    )
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def moe_capacity(desc):
+    return int(lib().moe_capacity(C.byref(desc)))
+
+
+def moe_workspace_size(desc, kind=MOE_WS_LAYER):
+    n = C.c_size_t(0)
+    _check(lib().moe_workspace_size(C.byref(desc), int(kind), C.byref(n)))
+    return int(n.value)
+
+
+def workspace(desc, kind=MOE_WS_LAYER, device="cuda"):
+    """A device byte buffer of moe_workspace_size(desc, kind) bytes."""
+    import torch
+    return torch.empty(max(moe_workspace_size(desc, kind), 1), dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+def moe_route(desc, x, w_router, logit_bias, select_bias, logits, flags, topk_idx, topk_w,
+              counts=None, prob_mean=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_route(C.byref(desc), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+                           _ptr(logits), int(flags), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                           _ptr(prob_mean), wp, wn, _stream(stream)))
+
+
+def moe_permute(desc, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm,
+                n_kept=None, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_permute(C.byref(desc), _ptr(topk_idx), _ptr(x), int(capacity), _ptr(counts),
+                             _ptr(kept), _ptr(offsets), _ptr(dest_row), _ptr(src_token), _ptr(x_perm),
+                             _ptr(n_kept), wp, wn, _stream(stream)))
+
+
+def moe_grouped_ffn(desc, x_perm, offsets, max_rows, w_gate, w_up, w_down, h_tmp, y_perm, flags=0,
+                    ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_grouped_ffn(C.byref(desc), _ptr(x_perm), _ptr(offsets), int(max_rows), _ptr(w_gate),
+                                 _ptr(w_up), _ptr(w_down), _ptr(h_tmp), _ptr(y_perm), int(flags), wp, wn,
+                                 _stream(stream)))
+
+
+def moe_combine(desc, dest_row, topk_w, y_perm, y_shared, y, stream=None):
+    _check(lib().moe_combine(C.byref(desc), _ptr(dest_row), _ptr(topk_w), _ptr(y_perm), _ptr(y_shared),
+                             _ptr(y), _stream(stream)))
+
+
+_WEIGHT_KEYS = ("w_router", "logit_bias", "select_bias", "w_gate", "w_up", "w_down", "sh_gate",
+                "sh_up", "sh_down", "w_o")
+_AUX_KEYS = ("topk_idx", "topk_w", "dest_row", "counts", "kept", "n_kept", "n_dropped", "f", "P", "l_aux")
+
+
+def moe_layer_forward(desc, weights, x, y, aux=None, ws=None, stream=None):
+    """weights: dict with the keys of MoeWeights (missing = NULL); aux: dict with
+    any of the keys of MoeAux (device tensors to fill) or None."""
+    W = MoeWeights(**{k: _ptr(weights.get(k)) for k in _WEIGHT_KEYS})
+    A = MoeAux(**{k: _ptr(aux.get(k)) for k in _AUX_KEYS}) if aux else None
+    wp, wn = _ws(ws)
+    _check(lib().moe_layer_forward(C.byref(desc), C.byref(W), _ptr(x), _ptr(y),
+                                   C.byref(A) if A is not None else None, wp, wn, _stream(stream)))

@@ -1,0 +1,140 @@
+// combine.hip -- gate-weighted unpermute/combine and the aux-loss statistics.
+//
+// Lesson 10 "专家并行 EP" (learn.payai.win), "核心概念" item 1: the output is the
+// gate-weighted sum of the kept experts' outputs; item 3: expert outputs return
+// to their token and are summed with the saved gate weights; item 4: the aux
+// loss L_aux = alpha E sum_i f_i P_i from routing frequency f_i and mean score
+// P_i.  "Multi-Head LatentMoE 与 Head 并行" ("核心方法与创新", determinism): the
+// sums here are gathers in a fixed slot order with no atomics, so the output is
+// bitwise reproducible.
+#include "common.hpp"
+
+namespace moe {
+
+// One sub-token row per `tpr` threads; each thread owns 8 consecutive features
+// (bf16: one 16-byte load per kept slot).  fp32 accumulation in slot order,
+// then + y_shared, then one rounding.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int tpr) {
+    const int rpb = 256 / tpr;
+    const long s = (long)blockIdx.x * rpb + threadIdx.x / tpr;
+    const int c = threadIdx.x % tpr;
+    const long S = (long)a.T * a.H;
+    if (s >= S) return;
+    const int K = a.K, d = a.d;
+    const long t = s / a.H;
+    const int g = (int)(s - t * a.H);
+    const int32_t* dr = a.dest_row + s * K;
+    const float* wr = a.topk_w + s * K;
+    for (int j0 = c * 8; j0 < d; j0 += tpr * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < K; ++k) {
+            const int row = dr[k];
+            if (row < 0) continue;
+            const float w = wr[k];
+            if constexpr (BF16) {
+                const uint4 v = *(const uint4*)((const uint16_t*)a.y_perm + (size_t)row * d + j0);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = fmaf(w, __uint_as_float(u[q] << 16), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(w, __uint_as_float(u[q] & 0xffff0000u), acc[2 * q + 1]);
+                }
+            } else {
+                const float* yp = (const float*)a.y_perm + (size_t)row * d + j0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = fmaf(w, yp[q], acc[q]);
+            }
+        }
+        const size_t o = (size_t)t * a.h + (size_t)g * d + j0;
+        if constexpr (BF16) {
+            if (a.y_shared) {
+                const uint4 v = *(const uint4*)((const uint16_t*)a.y_shared + o);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += __uint_as_float(u[q] << 16);
+                    acc[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
+                }
+            }
+            uint4 out;
+            out.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+            out.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+            out.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+            out.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+            *(uint4*)((uint16_t*)a.y + o) = out;
+        } else {
+            float* yo = (float*)a.y + o;
+            const float* ys = a.y_shared ? (const float*)a.y_shared + o : nullptr;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) yo[q] = ys ? acc[q] + ys[q] : acc[q];
+        }
+    }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+    const long S = (long)a.T * a.H;
+    if (S == 0) return hipSuccess;
+    int tpr = a.d / 8;
+    if (tpr > 256) tpr = 256;
+    int p2 = 1;
+    while (p2 * 2 <= tpr) p2 *= 2;
+    tpr = p2;
+    const int rpb = 256 / tpr;
+    const long blocks = (S + rpb - 1) / rpb;
+    if (a.dtype == MOE_BF16)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, a, tpr);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, a, tpr);
+    return hipGetLastError();
+}
+
+// f_e = counts_e / (T K); P as given; L_aux = mean over heads of alpha E sum_e f_e P_e
+// (fixed-order serial sums; E_tot is small).  One block.
+__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+    const int Et = a.H * a.E;
+    __shared__ float headsum[256];
+    for (int i = threadIdx.x; i < Et; i += 256) {
+        const float fe = (float)a.counts[i] / ((float)a.T * (float)a.K);
+        if (a.f) a.f[i] = fe;
+        if (a.P) a.P[i] = a.prob_mean[i];
+        if (a.kept_out) a.kept_out[i] = a.kept_in[i];
+    }
+    for (int g = threadIdx.x; g < a.H; g += 256) {
+        float s = 0.0f;
+        for (int e = 0; e < a.E; ++e) {
+            const float fe = (float)a.counts[g * a.E + e] / ((float)a.T * (float)a.K);
+            s += fe * a.prob_mean[g * a.E + e];
+        }
+        headsum[g] = a.alpha * (float)a.E * s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        if (a.l_aux) {
+            float s = 0.0f;
+            for (int g = 0; g < a.H; ++g) s += headsum[g];
+            *a.l_aux = s / (float)a.H;
+        }
+        const int32_t nk = a.offsets[Et];
+        if (a.n_kept) *a.n_kept = nk;
+        if (a.n_dropped) *a.n_dropped = a.A - nk;
+    }
+}
+
+hipError_t launch_stats(const StatsArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace moe

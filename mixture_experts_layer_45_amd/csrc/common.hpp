@@ -1,0 +1,130 @@
+// common.hpp -- device helpers and internal launcher declarations of libmoe.
+// gfx950 (CDNA4) only: 64-lane wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte register vector
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ------------------------------------------------------------ wave helpers
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+
+// ------------------------------------------------------- internal launchers
+// Every launcher enqueues on `st` and returns hipGetLastError() of the launch.
+struct RouteArgs {
+    int T, h, H, E, K, dtype, score;
+    uint32_t flags;
+    const void* x;
+    const void* w_router;
+    const float* logit_bias;
+    const float* select_bias;
+    float* logits;
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* counts;      // may be null
+    float* prob_part;     // [n_blocks][H*E] partial sums of the score distribution, may be null
+};
+int route_blocks(int T, int H);  // number of route blocks (= rows of prob_part)
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_prob_mean(const float* prob_part, int n_blocks_per_head, int H, int E, int T,
+                            float* prob_mean, hipStream_t st);
+
+struct PermuteArgs {
+    int A;        // assignments = T*H*K
+    int K, H, Et, d, h, dtype;
+    int capacity;
+    const int32_t* topk_idx;
+    const void* x;        // may be null (no gather)
+    int32_t* counts;
+    int32_t* kept;
+    int32_t* offsets;
+    int32_t* dest_row;
+    int32_t* src_token;
+    void* x_perm;
+    int32_t* n_kept;      // may be null
+    int32_t* hist;        // ws: [n_chunks][Et]
+    int max_rows;         // rows the gather grid covers
+};
+int permute_chunks(int A);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+
+struct GemmTile {
+    int32_t group, row0, row_end, pad;
+};
+struct FfnArgs {
+    int G;          // groups
+    int d, f;       // in/out width of the layer and hidden width
+    int dtype, act;
+    int max_rows;
+    const void* x_perm;
+    const int32_t* offsets;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    void* h_tmp;
+    void* y_perm;
+    uint32_t flags;
+    GemmTile* tiles;  // ws: tile table
+};
+size_t ffn_workspace_bytes(int G, int max_rows, int dtype);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t st);
+// Dense GEMM y[rows][n] = x[rows][k] W^T with W [n][k] (one group; used for W_o).
+hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const void* w, void* y,
+                        GemmTile* tiles, int32_t* offsets2, hipStream_t st);
+
+struct CombineArgs {
+    int T, H, K, d, h, dtype;
+    const int32_t* dest_row;
+    const float* topk_w;
+    const void* y_perm;
+    const void* y_shared;
+    void* y;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+struct StatsArgs {
+    int T, H, E, K, A;
+    float alpha;
+    const int32_t* counts;
+    const int32_t* kept_in;
+    const int32_t* offsets;
+    const float* prob_mean;
+    float* f;
+    float* P;
+    float* l_aux;
+    int32_t* n_kept;
+    int32_t* n_dropped;
+    int32_t* kept_out;
+};
+hipError_t launch_stats(const StatsArgs& a, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
+hipError_t launch_set2(int32_t* p, int32_t a, int32_t b, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,458 @@
+// gemm.hip -- the experts' FFNs as a ragged grouped GEMM.
+//
+// Lesson 10 "专家并行 EP" (learn.payai.win), "核心概念" item 3: once the rows are
+// grouped by expert, the local experts run back to back as one grouped GEMM.
+// "Chương 10: Song song MoE", item 1: each expert is an ordinary FFN.
+//
+// Group g owns rows [offsets[g], offsets[g+1]) of the activation matrix and
+// its own weights W_g [Nout][K] (out-major).  The row ranges live on the
+// device, so the launch is sized from host-side bounds and a one-block kernel
+// first writes a table of the real M-tiles (group, first row, end row); the
+// GEMM blocks read their tile from it and surplus blocks exit.
+//
+// bf16 kernel (gfx950): 256 threads = 4 waves as 2x2, a BM x 256 output tile
+// (for SwiGLU: 128 gate columns and the same 128 up columns, so the epilogue
+// has both halves of silu(g)*u), BK = 64, v_mfma_f32_32x32x16_bf16 with fp32
+// accumulators, A and B staged through LDS in two buffers (the global loads of
+// step k+1 are in flight while step k's MFMAs run), 16-byte chunks XOR-swizzled
+// by row so the fragment reads are bank-conflict free.  The activation is fused
+// into the epilogue and the result is rounded once to bf16.  Blocks are mapped
+// so each XCD (own L2) works through a contiguous run of tiles that share
+// weight columns and rows.
+#include "common.hpp"
+
+namespace moe {
+
+enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_PLAIN = 2 };
+
+// ------------------------------------------------------------- tile table
+// Row ranges are clamped to [0, max_rows) so inconsistent offsets can never send
+// a tile past the buffers the launch was sized for.
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets, int G, int BM, int max_rows,
+                                                          int max_tiles, GemmTile* tiles) {
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    const int per = (G + 1023) / 1024;
+    int32_t nt[4];
+    int32_t run = 0;
+    for (int q = 0; q < per; ++q) {
+        const int g = tid * per + q;
+        int32_t r0 = 0, r1 = 0;
+        if (g < G) {
+            r0 = min(max(offsets[g], 0), max_rows);
+            r1 = min(max(offsets[g + 1], r0), max_rows);
+        }
+        nt[q] = (r1 - r0 + BM - 1) / BM;
+        run += nt[q];
+    }
+    part[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int32_t pos = part[tid] - run;
+    const int32_t total = part[1023];
+    for (int q = 0; q < per; ++q) {
+        const int g = tid * per + q;
+        if (g >= G) break;
+        const int32_t r0 = min(max(offsets[g], 0), max_rows);
+        const int32_t r1 = min(max(offsets[g + 1], r0), max_rows);
+        for (int i = 0; i < nt[q] && pos + i < max_tiles; ++i) {
+            GemmTile t;
+            t.group = g;
+            t.row0 = r0 + i * BM;
+            t.row_end = r1;
+            t.pad = 0;
+            tiles[pos + i] = t;
+        }
+        pos += nt[q];
+    }
+    for (int i = total + tid; i < max_tiles; i += 1024) {
+        GemmTile t;
+        t.group = -1;
+        t.row0 = t.row_end = t.pad = 0;
+        tiles[i] = t;
+    }
+}
+
+struct GArgs {
+    const void* A;   // [rows][K]
+    const void* B0;  // [G][Nout][K]
+    const void* B1;  // [G][Nout][K] (SwiGLU up) or null
+    void* C;         // [rows][Nout]
+    const GemmTile* tiles;
+    int m_tiles, n_tiles, K, Nout, total, per_xcd;
+};
+
+constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together
+
+// block -> (m tile, n tile): blocks are dealt to the 8 XCDs round-robin, so block
+// b runs on XCD b % 8; give each XCD a contiguous range of the schedule, and order
+// the schedule as groups of NGROUP N-tiles sweeping all M-tiles.
+__device__ __forceinline__ bool decode_tile(const GArgs& a, int& mt, int& nt) {
+    const int b = blockIdx.x;
+    const int s = (b & 7) * a.per_xcd + (b >> 3);
+    if (s >= a.total) return false;
+    const int gsz = a.m_tiles * NGROUP;
+    const int nb = s / gsz;
+    const int rem = s - nb * gsz;
+    const int width = min(NGROUP, a.n_tiles - nb * NGROUP);
+    mt = rem / width;
+    nt = nb * NGROUP + (rem - mt * width);
+    return true;
+}
+
+__device__ __forceinline__ float act_silu(float g) { return g / (1.0f + __expf(-g)); }
+// erf by Abramowitz and Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (|error| <= 1.5e-7 for x >= 0, odd extension below 0): inline, so the
+// epilogue keeps its accumulators in registers.  The bf16 rounding of the
+// result (relative 2^-9) dwarfs the approximation error.
+__device__ __forceinline__ float erf_as(float x) {
+    const float ax = fabsf(x);
+    const float t = 1.0f / (1.0f + 0.3275911f * ax);
+    float p = 1.061405429f;
+    p = p * t - 1.453152027f;
+    p = p * t + 1.421413741f;
+    p = p * t - 0.284496736f;
+    p = p * t + 0.254829592f;
+    p = p * t;
+    const float r = 1.0f - p * __expf(-ax * ax);
+    return x < 0.0f ? -r : r;
+}
+__device__ __forceinline__ float act_gelu(float a) { return 0.5f * a * (1.0f + erf_as(a * 0.70710678118654752f)); }
+
+// ------------------------------------------------------------- bf16 MFMA
+template <int BM, int MODE>
+struct TileCfg {
+    static constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
+    static constexpr int BNM = MODE == MODE_SWIGLU ? 128 : 256;  // output columns per matrix
+    static constexpr int WM = BM / 2;
+    static constexpr int WNM = BNM / 2;
+    static constexpr int TM = WM / 32;
+    static constexpr int TN = WNM / 32;
+    static constexpr int NACC = NMAT * TM * TN;
+    static constexpr int A_BYTES = BM * 128;     // BM rows x 64 bf16
+    static constexpr int B_BYTES = 256 * 128;    // 256 weight rows x 64 bf16
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GArgs a) {
+    using C = TileCfg<BM, MODE>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+    int mt, nt;
+    if (!decode_tile(a, mt, nt)) return;
+    const GemmTile tl = a.tiles[mt];
+    if (tl.group < 0) return;
+    const int grp = tl.group, row0 = tl.row0, row_end = tl.row_end;
+    const int K = a.K, Nout = a.Nout;
+    const int n0 = nt * C::BNM;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = tid >> 3, lch = tid & 7;
+
+    const uint16_t* Ab = (const uint16_t*)a.A;
+    const uint16_t* B0 = (const uint16_t*)a.B0 + (size_t)grp * Nout * K;
+    const uint16_t* B1 = MODE == MODE_SWIGLU ? (const uint16_t*)a.B1 + (size_t)grp * Nout * K : B0;
+
+    const uint16_t* pa[BM / 32];
+#pragma unroll
+    for (int p = 0; p < BM / 32; ++p) {
+        const int r = min(row0 + lrow + 32 * p, row_end - 1);
+        pa[p] = Ab + (size_t)r * K + lch * 8;
+    }
+    const uint16_t* pb[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int br = lrow + 32 * p;
+        const int mat = br / C::BNM;
+        const int col = min(n0 + br - mat * C::BNM, Nout - 1);
+        pb[p] = (mat ? B1 : B0) + (size_t)col * K + lch * 8;
+    }
+    const int sw = (lch ^ (lrow & 7)) << 4;
+
+    u32x4 ra[BM / 32], rb[8];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    floatx16 acc[C::NACC];
+#pragma unroll
+    for (int i = 0; i < C::NACC; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+
+    const int nk = (K + 63) / 64;
+    {
+        const bool kin = lch * 8 < K;
+#pragma unroll
+        for (int p = 0; p < BM / 32; ++p) ra[p] = kin ? *(const u32x4*)(pa[p]) : zero;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) rb[p] = kin ? *(const u32x4*)(pb[p]) : zero;
+#pragma unroll
+        for (int p = 0; p < BM / 32; ++p) *(u32x4*)(smem + (lrow + 32 * p) * 128 + sw) = ra[p];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) *(u32x4*)(smem + C::A_BYTES + (lrow + 32 * p) * 128 + sw) = rb[p];
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int k0 = (kt + 1) * 64;
+            const bool kin = k0 + lch * 8 < K;
+#pragma unroll
+            for (int p = 0; p < BM / 32; ++p) ra[p] = kin ? *(const u32x4*)(pa[p] + k0) : zero;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) rb[p] = kin ? *(const u32x4*)(pb[p] + k0) : zero;
+        }
+        const uint8_t* As = smem + (kt & 1) * C::STAGE;
+        const uint8_t* Bs = As + C::A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int ch = kk * 2 + (lane >> 5);
+            bf16x8 af[C::TM], bfr[C::NMAT * C::TN];
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm) {
+                const int r = wm * C::WM + tm * 32 + (lane & 31);
+                af[tm] = *(const bf16x8*)(As + swz(r, ch));
+            }
+#pragma unroll
+            for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn) {
+                    const int r = m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31);
+                    bfr[m * C::TN + tn] = *(const bf16x8*)(Bs + swz(r, ch));
+                }
+#pragma unroll
+            for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+                for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < C::TN; ++tn) {
+                        const int ai = (m * C::TM + tm) * C::TN + tn;
+                        acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[m * C::TN + tn], acc[ai], 0, 0, 0);
+                    }
+        }
+        if (more) {
+            uint8_t* Ad = smem + ((kt + 1) & 1) * C::STAGE;
+            uint8_t* Bd = Ad + C::A_BYTES;
+#pragma unroll
+            for (int p = 0; p < BM / 32; ++p) *(u32x4*)(Ad + (lrow + 32 * p) * 128 + sw) = ra[p];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) *(u32x4*)(Bd + (lrow + 32 * p) * 128 + sw) = rb[p];
+        }
+        __syncthreads();
+    }
+
+    // epilogue: 32x32 accumulator element i of a lane is row 8*(i/4) + 4*(lane/32) + i%4,
+    // column lane%32.  The activation is applied in place first (every index a
+    // compile-time constant, so the accumulators stay in registers).
+    if constexpr (MODE == MODE_SWIGLU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
+    } else if constexpr (MODE == MODE_GELU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
+    }
+    uint16_t* Cp = (uint16_t*)a.C;
+#pragma clang loop unroll(full)
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma clang loop unroll(full)
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const int col = n0 + wn * C::WNM + tn * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) {
+                const int row = row0 + wm * C::WM + tm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                if (row < row_end && col < Nout)
+                    Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
+            }
+        }
+}
+
+// ------------------------------------------------------------- fp32 VALU
+// 64 x 64 output tile per matrix, BK = 16, 256 threads each computing 4x4.
+constexpr int FBM = 64, FBN = 64, FBK = 16;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GArgs a) {
+    constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
+    __shared__ float As[FBK][FBM + 4];
+    __shared__ float Bs[NMAT][FBK][FBN + 4];
+    const int mt = blockIdx.x, nt = blockIdx.y;
+    if (mt >= a.m_tiles) return;
+    const GemmTile tl = a.tiles[mt];
+    if (tl.group < 0) return;
+    const int K = a.K, Nout = a.Nout;
+    const int n0 = nt * FBN;
+    const float* A = (const float*)a.A;
+    const float* Bm[2] = {(const float*)a.B0 + (size_t)tl.group * Nout * K,
+                          MODE == MODE_SWIGLU ? (const float*)a.B1 + (size_t)tl.group * Nout * K : nullptr};
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    float acc[NMAT][4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += FBK) {
+        for (int i = tid; i < FBM * FBK; i += 256) {
+            const int r = i / FBK, k = i % FBK;
+            const int gr = min(tl.row0 + r, tl.row_end - 1);
+            As[k][r] = k0 + k < K ? A[(size_t)gr * K + k0 + k] : 0.0f;
+        }
+        for (int m = 0; m < NMAT; ++m)
+            for (int i = tid; i < FBN * FBK; i += 256) {
+                const int c = i / FBK, k = i % FBK;
+                const int gc = min(n0 + c, Nout - 1);
+                Bs[m][k][c] = k0 + k < K ? Bm[m][(size_t)gc * K + k0 + k] : 0.0f;
+            }
+        __syncthreads();
+        for (int k = 0; k < FBK; ++k)
+            for (int m = 0; m < NMAT; ++m)
+                for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < 4; ++j)
+                        acc[m][i][j] = fmaf(As[k][ty * 4 + i], Bs[m][k][tx * 4 + j], acc[m][i][j]);
+        __syncthreads();
+    }
+    float* Cp = (float*)a.C;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+            const int row = tl.row0 + ty * 4 + i, col = n0 + tx * 4 + j;
+            if (row >= tl.row_end || col >= Nout) continue;
+            float v;
+            if constexpr (MODE == MODE_SWIGLU) {
+                v = acc[0][i][j] / (1.0f + expf(-acc[0][i][j])) * acc[1][i][j];
+            } else if constexpr (MODE == MODE_GELU) {
+                v = act_gelu(acc[0][i][j]);
+            } else {
+                v = acc[0][i][j];
+            }
+            Cp[(size_t)row * Nout + col] = v;
+        }
+}
+
+// ------------------------------------------------------------- launchers
+static int pick_bm(int dtype, int G, int max_rows) {
+    if (dtype != MOE_BF16) return FBM;
+    return (G > 0 && max_rows / G >= 256) ? 256 : 128;
+}
+static int max_m_tiles(int BM, int G, int max_rows) { return (max_rows + BM - 1) / BM + G; }
+
+size_t ffn_workspace_bytes(int G, int max_rows, int dtype) {
+    const int BM = pick_bm(dtype, G, max_rows);
+    return (size_t)max_m_tiles(BM, G, max_rows) * sizeof(GemmTile);
+}
+
+template <int BM, int MODE>
+static hipError_t run_bf16(GArgs g, hipStream_t st) {
+    using C = TileCfg<BM, MODE>;
+    g.n_tiles = (g.Nout + C::BNM - 1) / C::BNM;
+    g.total = g.m_tiles * g.n_tiles;
+    g.per_xcd = (g.total + 7) / 8;
+    const int blocks = g.per_xcd * 8;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, MODE>), dim3(blocks), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t run_f32(GArgs g, hipStream_t st) {
+    g.n_tiles = (g.Nout + FBN - 1) / FBN;
+    if (g.m_tiles == 0 || g.n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_f32_kernel<MODE>), dim3(g.m_tiles, g.n_tiles), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+static hipError_t run_gemm(int dtype, int BM, int mode, const GArgs& g, hipStream_t st) {
+    if (dtype == MOE_BF16) {
+        if (BM == 256) {
+            if (mode == MODE_SWIGLU) return run_bf16<256, MODE_SWIGLU>(g, st);
+            if (mode == MODE_GELU) return run_bf16<256, MODE_GELU>(g, st);
+            return run_bf16<256, MODE_PLAIN>(g, st);
+        }
+        if (mode == MODE_SWIGLU) return run_bf16<128, MODE_SWIGLU>(g, st);
+        if (mode == MODE_GELU) return run_bf16<128, MODE_GELU>(g, st);
+        return run_bf16<128, MODE_PLAIN>(g, st);
+    }
+    if (mode == MODE_SWIGLU) return run_f32<MODE_SWIGLU>(g, st);
+    if (mode == MODE_GELU) return run_f32<MODE_GELU>(g, st);
+    return run_f32<MODE_PLAIN>(g, st);
+}
+
+static hipError_t build_tiles(const int32_t* offsets, int G, int BM, int max_rows, int max_tiles,
+                              GemmTile* tiles, hipStream_t st) {
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, G, BM, max_rows, max_tiles, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
+    if (f.max_rows <= 0 || f.G <= 0) return hipSuccess;
+    const int BM = pick_bm(f.dtype, f.G, f.max_rows);
+    const int mtiles = max_m_tiles(BM, f.G, f.max_rows);
+    hipError_t err = build_tiles(f.offsets, f.G, BM, f.max_rows, mtiles, f.tiles, st);
+    if (err != hipSuccess) return err;
+    const uint32_t fl = f.flags ? f.flags : (MOE_FFN_GEMM1 | MOE_FFN_GEMM2);
+    if (fl & MOE_FFN_GEMM1) {
+        GArgs g{};
+        g.A = f.x_perm;
+        g.B0 = f.w_gate;
+        g.B1 = f.act == MOE_SWIGLU ? f.w_up : nullptr;
+        g.C = f.h_tmp;
+        g.tiles = f.tiles;
+        g.m_tiles = mtiles;
+        g.K = f.d;
+        g.Nout = f.f;
+        err = run_gemm(f.dtype, BM, f.act == MOE_SWIGLU ? MODE_SWIGLU : MODE_GELU, g, st);
+        if (err != hipSuccess) return err;
+    }
+    if (fl & MOE_FFN_GEMM2) {
+        GArgs g{};
+        g.A = f.h_tmp;
+        g.B0 = f.w_down;
+        g.B1 = nullptr;
+        g.C = f.y_perm;
+        g.tiles = f.tiles;
+        g.m_tiles = mtiles;
+        g.K = f.f;
+        g.Nout = f.d;
+        err = run_gemm(f.dtype, BM, MODE_PLAIN, g, st);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+__global__ void set2_kernel(int32_t* p, int32_t a, int32_t b) {
+    p[0] = a;
+    p[1] = b;
+}
+
+hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const void* w, void* y,
+                        GemmTile* tiles, int32_t* offsets2, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(set2_kernel, dim3(1), dim3(1), 0, st, offsets2, 0, rows);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int BM = pick_bm(dtype, 1, rows);
+    const int mtiles = max_m_tiles(BM, 1, rows);
+    if ((err = build_tiles(offsets2, 1, BM, rows, mtiles, tiles, st)) != hipSuccess) return err;
+    GArgs g{};
+    g.A = x;
+    g.B0 = w;
+    g.C = y;
+    g.tiles = tiles;
+    g.m_tiles = mtiles;
+    g.K = k;
+    g.Nout = n;
+    return run_gemm(dtype, BM, MODE_PLAIN, g, st);
+}
+
+hipError_t launch_set2(int32_t* p, int32_t a, int32_t b, hipStream_t st) {
+    hipLaunchKernelGGL(set2_kernel, dim3(1), dim3(1), 0, st, p, a, b);
+    return hipGetLastError();
+}
+
+}  // namespace moe

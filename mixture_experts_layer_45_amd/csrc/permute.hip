@@ -1,0 +1,197 @@
+// permute.hip -- expert histogram, prefix scan under capacity, stable rank and
+// row gather.
+//
+// Lesson 10 "专家并行 EP" (learn.payai.win), "核心概念" item 3: the rows bound
+// for each expert are packed together before the experts run; item 4: an
+// expert keeps at most C = CF K T / E of them and the rest are dropped
+// ("Chương 10: Song song MoE", items 1 and 4: capacity factor, drop/pad).  On
+// one GPU the pack is a permutation of the token rows into expert-major order.
+//
+// The assignment list (T*H*K expert ids, sub-token-major) is cut into chunks of
+// CHUNK ids, one wave per chunk:
+//   1. hist:    per-chunk expert counts (LDS integer atomics; exact).
+//   2. scan:    per expert, the exclusive prefix over chunks (chunk order), the
+//               totals (counts), kept = min(counts, C) and offsets = exclusive
+//               prefix of kept.  One block; fixed order.
+//   3. rank:    each chunk walks its ids 64 at a time in order; lanes holding
+//               the same expert find each other with ballots over the bits of
+//               the id, a lane's rank among them is the popcount of the lower
+//               lanes, and a per-expert running count in LDS carries the queue
+//               position across steps.  pos < C keeps the row at offsets[e]+pos.
+//   4. gather:  x_perm[row] = slice g of x[t] for each kept row, 16-byte copies.
+// No step depends on the order in which blocks run, so the result is unique.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int CHUNK = 1024;       // assignments per chunk (16 steps of 64)
+constexpr int MAX_ET = 4096;      // experts the LDS tables hold
+
+int permute_chunks(int A) { return (A + CHUNK - 1) / CHUNK; }
+
+__global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int Et, int32_t* hist) {
+    __shared__ int cnt[MAX_ET];
+    for (int e = threadIdx.x; e < Et; e += 64) cnt[e] = 0;
+    __syncthreads();
+    const int a0 = blockIdx.x * CHUNK;
+    const int a1 = min(a0 + CHUNK, A);
+    for (int a = a0 + threadIdx.x; a < a1; a += 64) {
+        const int e = idx[a];
+        if ((unsigned)e < (unsigned)Et) atomicAdd(&cnt[e], 1);  // out-of-range ids are dropped
+    }
+    __syncthreads();
+    int32_t* out = hist + (size_t)blockIdx.x * Et;
+    for (int e = threadIdx.x; e < Et; e += 64) out[e] = cnt[e];
+}
+
+// One block of 1024 threads.  hist [nch][Et] is rewritten in place as the
+// per-chunk exclusive base of each expert.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int Et, int capacity,
+                                                    int32_t* counts, int32_t* kept, int32_t* offsets,
+                                                    int32_t* n_kept) {
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    // each thread owns experts [tid*per, tid*per + per)
+    const int per = (Et + 1023) / 1024;
+    int32_t loc[4];
+    int32_t run = 0;
+    for (int q = 0; q < per; ++q) {
+        const int e = tid * per + q;
+        int32_t total = 0;
+        if (e < Et) {
+            for (int c = 0; c < nch; ++c) {
+                const int32_t v = hist[(size_t)c * Et + e];
+                hist[(size_t)c * Et + e] = total;
+                total += v;
+            }
+            counts[e] = total;
+            const int32_t kp = total > capacity ? capacity : total;
+            kept[e] = kp;
+            loc[q] = kp;
+        } else {
+            loc[q] = 0;
+        }
+        run += loc[q];
+    }
+    // exclusive scan of the per-thread totals (Hillis-Steele over 1024 entries)
+    part[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int32_t base = part[tid] - run;
+    for (int q = 0; q < per; ++q) {
+        const int e = tid * per + q;
+        if (e < Et) offsets[e] = base;
+        base += loc[q];
+    }
+    if (tid == 1023) {
+        offsets[Et] = part[1023];
+        if (n_kept) *n_kept = part[1023];
+    }
+}
+
+__global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int K, int Et, int nbits,
+                                                  int capacity, const int32_t* base,
+                                                  const int32_t* offsets, int32_t* dest_row,
+                                                  int32_t* src_token) {
+    __shared__ int32_t run[MAX_ET];
+    __shared__ int32_t off[MAX_ET];
+    const int lane = threadIdx.x;
+    const int32_t* b = base + (size_t)blockIdx.x * Et;
+    for (int e = lane; e < Et; e += 64) {
+        run[e] = b[e];
+        off[e] = offsets[e];
+    }
+    __syncthreads();
+    const uint64_t lt = lanemask_lt();
+    const int a0 = blockIdx.x * CHUNK;
+    for (int step = 0; step < CHUNK / 64; ++step) {
+        const int a = a0 + step * 64 + lane;
+        if (a0 + step * 64 >= A) break;  // uniform
+        const int ev = a < A ? idx[a] : -1;
+        const bool valid = (unsigned)ev < (unsigned)Et;
+        const int e = valid ? ev : 0;
+        // lanes with the same (valid, e)
+        uint64_t peers = __ballot(valid);
+        if (!valid) peers = ~peers;
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool v = (e >> bit) & 1;
+            const uint64_t m = __ballot(v);
+            peers &= v ? m : ~m;
+        }
+        int32_t pos = 0;
+        if (valid) pos = run[e] + __popcll(peers & lt);
+        __builtin_amdgcn_wave_barrier();
+        // the highest lane of each group advances the expert's running count
+        if (valid && (peers >> lane) == 1ull) run[e] = pos + 1;
+        __builtin_amdgcn_wave_barrier();
+        if (a < A && !valid) dest_row[a] = -1;
+        if (valid) {
+            if (pos < capacity) {
+                const int32_t row = off[e] + pos;
+                dest_row[a] = row;
+                src_token[row] = a / K;
+            } else {
+                dest_row[a] = -1;
+            }
+        }
+    }
+}
+
+// x_perm[row][:] = x[t][g*d : g*d+d] with s = src_token[row] = t*H + g.
+// `tpr` threads per row copy 16 bytes each per iteration.
+__global__ __launch_bounds__(256) void gather_kernel(const void* x, int h, int H, int rowbytes,
+                                                     const int32_t* src_token, const int32_t* n_rows_p,
+                                                     int tpr, int max_rows, void* x_perm) {
+    const int n_rows = *n_rows_p;
+    const int rpb = 256 / tpr;
+    const int row = blockIdx.x * rpb + threadIdx.x / tpr;
+    const int c = threadIdx.x % tpr;
+    if (row >= n_rows || row >= max_rows) return;
+    const int s = src_token[row];
+    const int t = s / H, g = s - t * H;
+    const char* src = (const char*)x + (size_t)t * (size_t)(rowbytes * H) + (size_t)g * rowbytes;
+    char* dst = (char*)x_perm + (size_t)row * rowbytes;
+    for (int o = c * 16; o < rowbytes; o += tpr * 16)
+        *(uint4*)(dst + o) = *(const uint4*)(src + o);
+    (void)h;
+}
+
+hipError_t launch_permute(const PermuteArgs& p, hipStream_t st) {
+    const int nch = permute_chunks(p.A);
+    hipError_t err;
+    if (nch > 0) {
+        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.Et, p.hist);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, p.hist, nch, p.Et, p.capacity, p.counts,
+                       p.kept, p.offsets, p.n_kept);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (nch == 0) return hipSuccess;
+    int nbits = 1;
+    while ((1 << nbits) < p.Et) ++nbits;
+    hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.Et, nbits,
+                       p.capacity, p.hist, p.offsets, p.dest_row, p.src_token);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (p.x && p.x_perm && p.max_rows > 0) {
+        const int esz = p.dtype == MOE_BF16 ? 2 : 4;
+        const int rowbytes = p.d * esz;
+        int tpr = rowbytes / 16;
+        if (tpr > 256) tpr = 256;
+        int pow2 = 1;
+        while (pow2 * 2 <= tpr) pow2 *= 2;
+        tpr = pow2;
+        const int rpb = 256 / tpr;
+        const int blocks = (p.max_rows + rpb - 1) / rpb;
+        hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, st, p.x, p.h, p.H, rowbytes, p.src_token,
+                           p.offsets + p.Et, tpr, p.max_rows, p.x_perm);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace moe

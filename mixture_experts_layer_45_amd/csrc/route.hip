@@ -1,0 +1,323 @@
+// route.hip -- router GEMM, scoring, top-K selection and gate weights.
+//
+// Lesson 10 "专家并行 EP" (learn.payai.win), "核心概念" item 1: a token's
+// affinities to the E experts are x . W_g; the K largest are kept and scored
+// with a softmax over the kept logits (GShard/Switch gates of "HAI-LLM MoE",
+// "HAI-LLM 上的使用"), or with sigmoids renormalised over the kept experts, the
+// selection then using sigma + a per-expert bias ("Chương 10: Song song MoE",
+// item 4, DeepSeek's bias balancing).  Multi-head routing ("Multi-Head
+// LatentMoE 与 Head 并行", "核心方法与创新"): head g routes slice g of the token
+// with its own router among its own experts.
+//
+// One block = 16 tokens of one head.  Phase 1: the four waves split the
+// reduction over d, each running 16x16x32 bf16 MFMAs over its quarter; the
+// partial logit tiles are summed in LDS in wave order (fixed order, so the
+// logits are reproducible).  Phase 2: each wave takes four of the 16 tokens;
+// the lanes hold the keys of experts lane, lane+64, ...; K rounds of a wave
+// arg-max (key descending, index ascending) pick the experts.  Gate weights,
+// the per-block score sums for P and the per-block expert histogram follow.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int RT_ROWS = 16;
+constexpr int RT_THREADS = 256;
+
+int route_blocks(int T, int H) { return ((T + RT_ROWS - 1) / RT_ROWS) * H; }
+
+// Routing-key exp: a fixed sequence of fp32 operations (Cody and Waite's range
+// reduction with ln 2 split into a 16-bit head and an fp32 tail, the Taylor
+// series of e^r through r^7 in Horner form with fused multiply-adds, scaling by
+// 2^n).  Constants are the mathematical values rounded to fp32.  Valid for
+// |x| <= 80.
+__device__ __attribute__((noinline)) float key_exp(float x) {
+#pragma clang fp contract(off)
+    const float inv_ln2 = 0x1.715476p+0f;   // 1 / ln 2
+    const float ln2_hi = 0x1.62e4p-1f;      // 45426 / 2^16
+    const float ln2_lo = 0x1.7f7d1cp-20f;   // ln 2 - ln2_hi
+    const float n = __builtin_rintf(x * inv_ln2);
+    float r = __builtin_fmaf(-n, ln2_hi, x);
+    r = __builtin_fmaf(-n, ln2_lo, r);
+    float p = 0x1.a01a02p-13f;                  // 1/7!
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);   // 1/5!
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);   // 1/4!
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);   // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+// sigma(l) = 1 / (1 + e^{-l}) with l clamped to [-80, 80]; IEEE division.
+__device__ __attribute__((noinline)) float key_sigmoid(float l) {
+#pragma clang fp contract(off)
+    const float c = l < -80.0f ? -80.0f : (l > 80.0f ? 80.0f : l);
+    const float e = key_exp(-c);
+    const float den = 1.0f + e;
+    return 1.0f / den;
+}
+
+// (key, index) order: larger key first, lower index on ties.
+__device__ __forceinline__ bool better(float ka, int ea, float kb, int eb) {
+    return ka > kb || (ka == kb && ea < eb);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    // xor butterfly: partners add the same two values, so every lane ends with
+    // the same, order-fixed sum
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// NB = 16-expert column blocks of the logit tile (E <= 16*NB); EJ = E/64 slots per lane.
+template <int NB, bool BF16>
+__global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
+    constexpr int LDE = NB * 16 + 1;
+    constexpr int EJ = (NB * 16 + 63) / 64;
+    __shared__ float part[4][RT_ROWS][LDE];  // per-wave partial logits; part[0] ends as the tile
+    __shared__ int hist[NB * 16];
+    __shared__ float pw[4][NB * 16];
+
+    const int g = blockIdx.y;
+    const int t0 = blockIdx.x * RT_ROWS;
+    const int T = a.T, H = a.H, E = a.E, K = a.K;
+    const int d = a.h / H;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int Et = H * E;
+
+    for (int i = threadIdx.x; i < NB * 16; i += RT_THREADS) hist[i] = 0;
+
+    // ---------------------------------------------------------------- logits
+    if (a.flags & MOE_LOGITS_IN) {
+        for (int i = threadIdx.x; i < RT_ROWS * E; i += RT_THREADS) {
+            const int r = i / E, e = i - r * E, t = t0 + r;
+            part[0][r][e] = t < T ? a.logits[((size_t)t * H + g) * E + e] : 0.0f;
+        }
+    } else if constexpr (BF16) {
+        floatx4 acc[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int row = min(t0 + (lane & 15), T - 1);
+        const uint16_t* xr = (const uint16_t*)a.x + (size_t)row * a.h + (size_t)g * d;
+        const uint16_t* wg = (const uint16_t*)a.w_router + (size_t)g * E * d;
+        const int nks = (d + 31) / 32;
+        const int ks0 = wave * nks / 4, ks1 = (wave + 1) * nks / 4;
+        const int kq = (lane >> 4) * 8;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int ks = ks0; ks < ks1; ++ks) {
+            const int k = ks * 32 + kq;
+            const bool kin = k < d;
+            const u32x4 av = kin ? *(const u32x4*)(xr + k) : zero;
+            u32x4 bv[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int e = j * 16 + (lane & 15);
+                bv[j] = (kin && e < E) ? *(const u32x4*)(wg + (size_t)e * d + k) : zero;
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[j]), acc[j], 0, 0, 0);
+        }
+        // 16x16 result: lane holds rows 4*(lane/16)+i of column lane%16
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[wave][(lane >> 4) * 4 + i][j * 16 + (lane & 15)] = acc[j][i];
+        __syncthreads();
+        for (int i = threadIdx.x; i < RT_ROWS * NB * 16; i += RT_THREADS) {
+            const int r = i / (NB * 16), e = i - r * (NB * 16);
+            float s = part[0][r][e];
+            s += part[1][r][e];
+            s += part[2][r][e];
+            s += part[3][r][e];
+            part[0][r][e] = s;
+        }
+    } else {
+        const float* x = (const float*)a.x;
+        const float* wg = (const float*)a.w_router + (size_t)g * E * d;
+        for (int i = threadIdx.x; i < RT_ROWS * E; i += RT_THREADS) {
+            const int r = i / E, e = i - r * E;
+            const int t = min(t0 + r, T - 1);
+            const float* xr = x + (size_t)t * a.h + (size_t)g * d;
+            const float* wr = wg + (size_t)e * d;
+            float s = 0.0f;
+            for (int k = 0; k < d; ++k) s = fmaf(xr[k], wr[k], s);
+            part[0][r][e] = s;
+        }
+    }
+    __syncthreads();
+    if (a.flags & MOE_LOGITS_OUT) {
+        for (int i = threadIdx.x; i < RT_ROWS * E; i += RT_THREADS) {
+            const int r = i / E, e = i - r * E, t = t0 + r;
+            if (t < T) a.logits[((size_t)t * H + g) * E + e] = part[0][r][e];
+        }
+    }
+
+    // --------------------------------------------------- selection and weights
+    float pacc[EJ];
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) pacc[j] = 0.0f;
+    const float NEG = -__builtin_inff();
+    for (int rr = 0; rr < RT_ROWS / 4; ++rr) {
+        const int r = wave * (RT_ROWS / 4) + rr;
+        const int t = t0 + r;
+        if (t >= T) break;
+        const size_t s = (size_t)t * H + g;
+        float lp[EJ], key[EJ], sg[EJ];
+        bool used[EJ];
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) {
+            const int e = lane + 64 * j;
+            const bool valid = e < E;
+            float l = valid ? part[0][r][e] : NEG;
+            if (valid && a.logit_bias) l = l + a.logit_bias[g * E + e];
+            lp[j] = l;
+            if (a.score == MOE_SIGMOID) {
+                sg[j] = valid ? key_sigmoid(l) : 0.0f;
+                key[j] = valid ? (a.select_bias ? sg[j] + a.select_bias[g * E + e] : sg[j]) : NEG;
+            } else {
+                sg[j] = 0.0f;
+                key[j] = l;
+            }
+            used[j] = !valid;
+        }
+        // K rounds of wave arg-max; slot k is kept by lane k % 64
+        int my_e[4] = {0, 0, 0, 0};
+        float my_v[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < K; ++k) {
+            float bk = NEG;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) {
+                const int e = lane + 64 * j;
+                if (!used[j] && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ok = __shfl_xor(bk, off);
+                const int oe = __shfl_xor(be, off);
+                if (better(ok, oe, bk, be)) { bk = ok; be = oe; }
+            }
+            // the owner of `be` marks it used and broadcasts the value the weight needs
+            float v = 0.0f;
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) {
+                if (lane + 64 * j == be) {
+                    used[j] = true;
+                    v = a.score == MOE_SIGMOID ? sg[j] : lp[j];
+                }
+            }
+            v = __shfl(v, be & 63);
+            if ((k & 63) == lane) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if ((k >> 6) == q) { my_e[q] = be; my_v[q] = v; }
+            }
+        }
+        // gate weights: softmax over the kept biased logits (the first kept is the
+        // largest), or kept sigmoids over their sum
+        const float vmax = __shfl(my_v[0], 0);
+        float u[4], loc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool mine = lane + 64 * q < K;
+            u[q] = mine ? (a.score == MOE_SIGMOID ? my_v[q] : expf(my_v[q] - vmax)) : 0.0f;
+            loc += u[q];
+        }
+        const float den = wave_sum(loc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = lane + 64 * q;
+            if (k < K) {
+                a.topk_idx[s * K + k] = g * E + my_e[q];
+                a.topk_w[s * K + k] = u[q] / den;
+                atomicAdd(&hist[my_e[q]], 1);
+            }
+        }
+        // full score distribution for P
+        if (a.prob_part) {
+            if (a.score == MOE_SIGMOID) {
+                float sl = 0.0f;
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) sl += sg[j];
+                const float tot = wave_sum(sl);
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) pacc[j] += sg[j] / tot;
+            } else {
+                float ml = NEG;
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) ml = fmaxf(ml, lp[j]);
+                const float m = wave_max(ml);
+                float ex[EJ], sl = 0.0f;
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) {
+                    ex[j] = lane + 64 * j < E ? expf(lp[j] - m) : 0.0f;
+                    sl += ex[j];
+                }
+                const float tot = wave_sum(sl);
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) pacc[j] += ex[j] / tot;
+            }
+        }
+    }
+    if (a.prob_part) {
+#pragma unroll
+        for (int j = 0; j < EJ; ++j)
+            if (lane + 64 * j < NB * 16) pw[wave][lane + 64 * j] = pacc[j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += RT_THREADS) {
+        if (a.counts && hist[e]) atomicAdd(&a.counts[g * E + e], hist[e]);
+        if (a.prob_part) {
+            float s = pw[0][e];
+            s += pw[1][e];
+            s += pw[2][e];
+            s += pw[3][e];
+            a.prob_part[((size_t)g * gridDim.x + blockIdx.x) * E + e] = s;
+        }
+    }
+    (void)Et;
+}
+
+// P_e = (sum over the head's blocks, in block order) / T
+__global__ void prob_mean_kernel(const float* part, int nbx, int H, int E, int T, float* out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= H * E) return;
+    const int g = i / E, e = i - g * E;
+    float s = 0.0f;
+    for (int b = 0; b < nbx; ++b) s += part[((size_t)g * nbx + b) * E + e];
+    out[i] = T > 0 ? s / (float)T : 0.0f;
+}
+
+template <int NB>
+static hipError_t launch_nb(const RouteArgs& a, hipStream_t st) {
+    dim3 grid((a.T + RT_ROWS - 1) / RT_ROWS, a.H);
+    if (a.dtype == MOE_BF16)
+        hipLaunchKernelGGL((route_kernel<NB, true>), grid, dim3(RT_THREADS), 0, st, a);
+    else
+        hipLaunchKernelGGL((route_kernel<NB, false>), grid, dim3(RT_THREADS), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+    if (a.E <= 16) return launch_nb<1>(a, st);
+    if (a.E <= 32) return launch_nb<2>(a, st);
+    if (a.E <= 64) return launch_nb<4>(a, st);
+    if (a.E <= 128) return launch_nb<8>(a, st);
+    return launch_nb<16>(a, st);
+}
+
+hipError_t launch_prob_mean(const float* part, int nbx, int H, int E, int T, float* out, hipStream_t st) {
+    const int n = H * E;
+    hipLaunchKernelGGL(prob_mean_kernel, dim3((n + 255) / 256), dim3(256), 0, st, part, nbx, H, E, T, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

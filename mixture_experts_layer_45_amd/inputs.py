@@ -101,19 +101,7 @@ def make_inputs(cfg, device="cpu", seed=0, with_weights=True):
         return out
     out["w_router"] = _normal((H, E, d), 1.0 / math.sqrt(d), device, dt,
                               _gen(device, seed, _TENSOR_ID["w_router"]))
-    lb = cfg.get("logit_bias")
-    if lb == "zipf":
-        # expert e (rank e+1 in popularity) gets 2*ln(1/(e+1)), the same in every head
-        ranks = torch.arange(1, E + 1, dtype=torch.float64)
-        out["logit_bias"] = (2.0 * torch.log(1.0 / ranks)).to(torch.float32).repeat(H).to(device)
-    else:
-        out["logit_bias"] = None
-    sb = cfg.get("select_bias")
-    if sb == "uniform0.1":
-        g = _gen(device, seed, _TENSOR_ID["bias"])
-        out["select_bias"] = (torch.rand((Et,), generator=g, device=device, dtype=torch.float32) * 0.2 - 0.1)
-    else:
-        out["select_bias"] = None
+    out.update(make_biases(cfg, device, seed))
     gelu = cfg.get("act", "swiglu") == "gelu"
     out["w_gate"] = _per_expert(Et, (f, d), 1.0 / math.sqrt(d), device, dt, seed, _TENSOR_ID["w_gate"])
     out["w_up"] = None if gelu else _per_expert(Et, (f, d), 1.0 / math.sqrt(d), device, dt, seed,
@@ -128,6 +116,24 @@ def make_inputs(cfg, device="cpu", seed=0, with_weights=True):
         out["sh_gate"] = out["sh_up"] = out["sh_down"] = None
     out["w_o"] = (_normal((h, h), 1.0 / math.sqrt(h), device, dt, _gen(device, seed, _TENSOR_ID["w_o"]))
                   if cfg.get("has_wo", 0) else None)
+    return out
+
+
+def make_biases(cfg, device="cpu", seed=0):
+    """logit_bias and select_bias of a workload (None where it has none)."""
+    E, Et = cfg["E"], cfg.get("H", 1) * cfg["E"]
+    out = {}
+    if cfg.get("logit_bias") == "zipf":
+        # expert e (rank e+1 in popularity) gets 2*ln(1/(e+1)), the same in every head
+        ranks = torch.arange(1, E + 1, dtype=torch.float64)
+        out["logit_bias"] = (2.0 * torch.log(1.0 / ranks)).to(torch.float32).repeat(cfg.get("H", 1)).to(device)
+    else:
+        out["logit_bias"] = None
+    if cfg.get("select_bias") == "uniform0.1":
+        g = _gen(device, seed, _TENSOR_ID["bias"])
+        out["select_bias"] = torch.rand((Et,), generator=g, device=device, dtype=torch.float32) * 0.2 - 0.1
+    else:
+        out["select_bias"] = None
     return out
 
 

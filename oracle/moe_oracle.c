@@ -344,10 +344,14 @@ void orc_permute(const orc_desc *d, const int32_t *topk_idx, int64_t capacity,
  *   SwiGLU: a = x W1^T, u = x W3^T, hdn = silu(a) * u, out = hdn W2^T,
  *           silu(z) = z / (1 + e^{-z})
  *   GELU:   a = x W1^T, hdn = a * (1 + erf(a / sqrt 2)) / 2, out = hdn W2^T
- * W1, W3: [f][din]; W2: [din][f]; all in double.                            */
+ * W1, W3: [f][din]; W2: [din][f]; all in double.
+ * out_abs (may be NULL) receives sum_j |hdn_j| |W2[o][j]|, the magnitude of the
+ * terms of the last contraction: an evaluation that rounds hdn and out to a
+ * format with unit roundoff u errs by at most about 2u times it (the scale of
+ * the stated parity bound; it plays no part in out).                         */
 void orc_expert_ffn(int32_t dtype, int32_t act, int32_t din, int32_t f,
                     const void *w1, const void *w3, const void *w2,
-                    const double *xin, double *out)
+                    const double *xin, double *out, double *out_abs)
 {
     double *hdn = (double *)malloc(sizeof(double) * (size_t)f);
     for (int32_t j = 0; j < f; ++j) {
@@ -362,11 +366,43 @@ void orc_expert_ffn(int32_t dtype, int32_t act, int32_t din, int32_t f,
         }
     }
     for (int32_t o = 0; o < din; ++o) {
-        double acc = 0.0;
-        for (int32_t j = 0; j < f; ++j) acc += hdn[j] * ld(w2, dtype, (int64_t)o * f + j);
+        double acc = 0.0, mag = 0.0;
+        for (int32_t j = 0; j < f; ++j) {
+            double w = ld(w2, dtype, (int64_t)o * f + j);
+            acc += hdn[j] * w;
+            mag += fabs(hdn[j]) * fabs(w);
+        }
         out[o] = acc;
+        if (out_abs) out_abs[o] = mag;
     }
     free(hdn);
+}
+
+/* ------------------------------------------------------------- combine
+ * [L10] item 1 (output formula) and item 3 (returned rows times the saved gate
+ * weights, summed): y[t][g*d + j] = sum over kept slots k of w[s][k] *
+ * y_perm[dest_row[s][k]][j], plus y_shared[t][j] (weight 1) when given, in
+ * double.  y_perm and y_shared are arrays of the descriptor's dtype.         */
+void orc_combine(const orc_desc *d, const int32_t *dest_row, const double *topk_w,
+                 const void *y_perm, const void *y_shared, double *y)
+{
+    const int32_t T = d->T, H = d->H, K = d->K, h = d->h, dd = d->h / d->H;
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < h; ++j) y[t * h + j] = 0.0;
+        for (int32_t g = 0; g < H; ++g) {
+            int64_t s = t * H + g;
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t row = dest_row[s * K + k];
+                if (row < 0) continue;
+                for (int32_t j = 0; j < dd; ++j)
+                    y[t * h + g * dd + j] += topk_w[s * K + k] * ld(y_perm, d->dtype, (int64_t)row * dd + j);
+            }
+        }
+        if (y_shared)
+            for (int32_t j = 0; j < h; ++j) y[t * h + j] += ld(y_shared, d->dtype, t * h + j);
+    }
 }
 
 /* ------------------------------------------------------------- whole layer
@@ -375,10 +411,14 @@ void orc_expert_ffn(int32_t dtype, int32_t act, int32_t din, int32_t f,
  * on the head's slice), plus the always-on shared expert (weight 1, no
  * capacity), then the output projection W_o over the concatenated heads.
  * tokens == NULL computes every token.  y is written unrounded, in double.
+ * ymag (may be NULL) gets the magnitude that scales the rounding error of an
+ * evaluation in a narrower format: sum over kept k of w_k * sum_j |hdn_j||W2_j|
+ * (plus the shared expert's), and through W_o sum_i (|cat_i| + mag_i)|W_o[r][i]|.
  * Aux statistics ([L10] item 4): f = counts / (T K), P = psum / T,
  * L_aux = alpha * E * sum_e f_e P_e, averaged over heads.                     */
 int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
-                      const int32_t *tokens, int32_t n_tokens, double *y, orc_aux *aux)
+                      const int32_t *tokens, int32_t n_tokens, double *y, double *ymag,
+                      orc_aux *aux)
 {
     const int32_t T = d->T, h = d->h, H = d->H, E = d->E, K = d->K, f = d->f;
     const int32_t dd = h / H, Et = H * E;
@@ -409,6 +449,8 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
         double *xin = (double *)malloc(sizeof(double) * (size_t)h);
         double *cat = (double *)calloc((size_t)h, sizeof(double));
         double *o = (double *)malloc(sizeof(double) * (size_t)h);
+        double *om = (double *)malloc(sizeof(double) * (size_t)h);
+        double *cm = (double *)calloc((size_t)h, sizeof(double));
         for (int32_t j = 0; j < h; ++j) xin[j] = ld(x, d->dtype, t * h + j);
         for (int32_t g = 0; g < H; ++g) {
             int64_t s = t * H + g;
@@ -419,26 +461,42 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
                 const char *w1 = (const char *)w->w_gate + (size_t)e * f * dd * wsz;
                 const char *w3 = d->act == 0 ? (const char *)w->w_up + (size_t)e * f * dd * wsz : NULL;
                 const char *w2 = (const char *)w->w_down + (size_t)e * dd * f * wsz;
-                orc_expert_ffn(d->dtype, d->act, dd, f, w1, w3, w2, xin + g * dd, o);
-                for (int32_t j = 0; j < dd; ++j) cat[g * dd + j] += wts[s * K + k] * o[j];
+                orc_expert_ffn(d->dtype, d->act, dd, f, w1, w3, w2, xin + g * dd, o, om);
+                for (int32_t j = 0; j < dd; ++j) {
+                    cat[g * dd + j] += wts[s * K + k] * o[j];
+                    cm[g * dd + j] += wts[s * K + k] * om[j];
+                }
             }
         }
         if (d->n_shared > 0) {
-            orc_expert_ffn(d->dtype, d->act, h, f, w->sh_gate, w->sh_up, w->sh_down, xin, o);
-            for (int32_t j = 0; j < h; ++j) cat[j] += o[j];
+            orc_expert_ffn(d->dtype, d->act, h, f, w->sh_gate, w->sh_up, w->sh_down, xin, o, om);
+            for (int32_t j = 0; j < h; ++j) {
+                cat[j] += o[j];
+                cm[j] += om[j];
+            }
         }
         if (d->has_wo) {
             for (int32_t r = 0; r < h; ++r) {
-                double acc = 0.0;
-                for (int32_t j = 0; j < h; ++j) acc += cat[j] * ld(w->w_o, d->dtype, (int64_t)r * h + j);
+                double acc = 0.0, mag = 0.0;
+                for (int32_t j = 0; j < h; ++j) {
+                    double wo = ld(w->w_o, d->dtype, (int64_t)r * h + j);
+                    acc += cat[j] * wo;
+                    mag += (fabs(cat[j]) + cm[j]) * fabs(wo);
+                }
                 y[(int64_t)i * h + r] = acc;
+                if (ymag) ymag[(int64_t)i * h + r] = mag;
             }
         } else {
-            for (int32_t j = 0; j < h; ++j) y[(int64_t)i * h + j] = cat[j];
+            for (int32_t j = 0; j < h; ++j) {
+                y[(int64_t)i * h + j] = cat[j];
+                if (ymag) ymag[(int64_t)i * h + j] = cm[j];
+            }
         }
         free(xin);
         free(cat);
         free(o);
+        free(om);
+        free(cm);
     }
 
     if (aux) {

@@ -78,10 +78,13 @@ def lib():
         _lib.orc_permute.restype = None
         _lib.orc_permute.argtypes = [C.POINTER(OrcDesc), C.c_void_p, C.c_int64] + [C.c_void_p] * 6
         _lib.orc_expert_ffn.restype = None
-        _lib.orc_expert_ffn.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 5
+        _lib.orc_expert_ffn.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 6
+        _lib.orc_combine.restype = None
+        _lib.orc_combine.argtypes = [C.POINTER(OrcDesc)] + [C.c_void_p] * 5
         _lib.orc_layer_forward.restype = C.c_int
         _lib.orc_layer_forward.argtypes = [C.POINTER(OrcDesc), C.POINTER(OrcWeights), C.c_void_p,
-                                           C.c_void_p, C.c_int32, C.c_void_p, C.POINTER(OrcAux)]
+                                           C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                           C.POINTER(OrcAux)]
         _lib.orc_num_threads.restype = C.c_int
         _lib.orc_num_threads.argtypes = []
     return _lib
@@ -185,8 +188,9 @@ def permute(cfg, topk_idx, cap, T=None):
     return dict(counts=counts, kept=kept, offsets=offsets, dest_row=dest, src_sub=src[:n], n_kept=n)
 
 
-def expert_ffn(cfg, din, w1, w3, w2, xin):
-    """Rows xin [n, din] (float64) through one expert; returns [n, din] float64."""
+def expert_ffn(cfg, din, w1, w3, w2, xin, with_mag=False):
+    """Rows xin [n, din] (float64) through one expert; returns [n, din] float64
+    (and, with with_mag, the magnitude sum_j |hdn_j||W2[o][j]| per output)."""
     el = _elem(cfg)
     act = 1 if cfg.get("act", "swiglu") == "gelu" else 0
     dt = 1 if cfg["dtype"] == "bf16" else 0
@@ -196,10 +200,24 @@ def expert_ffn(cfg, din, w1, w3, w2, xin):
     xin = np.ascontiguousarray(np.atleast_2d(xin), dtype=np.float64)
     f = w1.size // din
     out = np.empty_like(xin)
+    mag = np.empty_like(xin)
     L = lib()
     for r in range(xin.shape[0]):
-        L.orc_expert_ffn(dt, act, din, f, _p(w1), _p(w3), _p(w2), _p(xin[r]), _p(out[r]))
-    return out
+        L.orc_expert_ffn(dt, act, din, f, _p(w1), _p(w3), _p(w2), _p(xin[r]), _p(out[r]), _p(mag[r]))
+    return (out, mag) if with_mag else out
+
+
+def combine(cfg, dest_row, topk_w, y_perm, y_shared=None, T=None):
+    """Gate-weighted combine of expert output rows; returns y [T, h] float64."""
+    d = desc(cfg, T)
+    el = _elem(cfg)
+    dr = _chk(dest_row, np.int32).ravel()
+    w = np.ascontiguousarray(topk_w, dtype=np.float64).ravel()
+    yp = _chk(y_perm, el)
+    ys = None if y_shared is None else _chk(y_shared, el)
+    y = np.empty((d.T, d.h), dtype=np.float64)
+    lib().orc_combine(C.byref(d), _p(dr), _p(w), _p(yp), _p(ys), _p(y))
+    return y
 
 
 def layer_forward(cfg, weights, x, tokens=None, T=None):
@@ -230,6 +248,7 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
     nt = d.T if tok is None else tok.size
     y = np.zeros((nt, d.h), dtype=np.float64)
+    ymag = np.zeros((nt, d.h), dtype=np.float64)
     out = dict(
         topk_idx=np.empty((S, d.K), np.int32), topk_w=np.empty((S, d.K), np.float64),
         margin=np.empty(S, np.float64), counts=np.empty(Et, np.int32), kept=np.empty(Et, np.int32),
@@ -239,13 +258,14 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
         logits=np.empty((S, d.E), np.float32),
     )
     aux = OrcAux(**{k: _p(v) for k, v in out.items()})
-    rc = lib().orc_layer_forward(C.byref(d), C.byref(W), _p(x), _p(tok), nt, _p(y), C.byref(aux))
+    rc = lib().orc_layer_forward(C.byref(d), C.byref(W), _p(x), _p(tok), nt, _p(y), _p(ymag), C.byref(aux))
     if rc != 0:
         raise ValueError("oracle rejected the layer description")
     out["n_kept"] = int(out["n_kept"][0])
     out["src_sub"] = out["src_sub"][: out["n_kept"]]
     out["l_aux"] = float(out["l_aux"][0])
     out["y"] = y
+    out["ymag"] = ymag
     return out
 
 

@@ -298,6 +298,16 @@ def test_full_layer_brute_force_tiny():
         y[t] = (p[:, None] * outs[t, order]).sum(0)
         assert r["topk_idx"][t].tolist() == order.tolist()
     assert np.allclose(r["y"], y, rtol=1e-9, atol=1e-12)
+    # the error magnitude: sum over kept k of w_k * (|H_k| |W2_k|^T), and >= |y|
+    mags = []
+    for e in range(E):
+        a = X @ decode(inp["w_gate"][e]).T
+        hdn = np.abs(a * expit(a) * (X @ decode(inp["w_up"][e]).T))
+        mags.append(hdn @ np.abs(decode(inp["w_down"][e])).T)
+    mags = np.stack(mags, 1)
+    ym = np.stack([(r["topk_w"][t][:, None] * mags[t, r["topk_idx"][t]]).sum(0) for t in range(cfg["T"])])
+    assert np.allclose(r["ymag"], ym, rtol=1e-9)
+    assert np.all(r["ymag"] >= np.abs(r["y"]) * (1 - 1e-12))
     # f, P and L_aux from their definitions
     f = np.bincount(r["topk_idx"].ravel(), minlength=E) / (cfg["T"] * K)
     P = softmax(lg.astype(np.float64)).mean(0)
