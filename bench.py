@@ -1,0 +1,264 @@
+"""Throughput of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of moe_layer_forward (route -> permute -> grouped FFN ->
+combine -> aux statistics) over one batch of synthetic inputs already resident
+in HBM.  W untimed steps, then exactly K steps bracketed by device
+synchronisation and timed with HIP events on the stream the library launches
+on; value = tokens per second.  Per-stage times come from the stage entry
+points timed the same way.  The dominant kernel (the grouped gate/up GEMM with
+the fused activation) is timed on its own for the roofline figure.  The CPU
+oracle is timed on a bounded sample of the same workload for the CPU baseline.
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_45_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the baseline sample")
+    p.add_argument("--stage-reps", type=int, default=10)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed(fn, reps, stream):
+    import torch
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps  # ms
+
+
+def traffic_from_profile(kernel_tag, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current GEMM source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if fields.get("gemm_source_sha256") != src_hash:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "expert/head-parallel path is a design, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_45_amd as moe
+    from mixture_experts_layer_45_amd import inputs
+
+    name = args.workload or inputs.BENCH_WORKLOAD
+    cfg = inputs.variant(name)
+    T, h, H, E, K, f = cfg["T"], cfg["h"], cfg["H"], cfg["E"], cfg["K"], cfg["f"]
+    d = h // H
+    Et, A = H * E, T * H * K
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] workload {name}: generating inputs on the device")
+    inp = inputs.make_inputs(cfg, dev, seed=0)
+    desc = moe.desc_from_cfg(cfg)
+    ws = moe.workspace(desc)
+    y = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    aux = dict(topk_idx=torch.empty((T * H, K), **i32), topk_w=torch.empty((T * H, K), **f32),
+               dest_row=torch.empty(A, **i32), counts=torch.empty(Et, **i32), kept=torch.empty(Et, **i32),
+               n_kept=torch.empty(1, **i32), n_dropped=torch.empty(1, **i32), f=torch.empty(Et, **f32),
+               P=torch.empty(Et, **f32), l_aux=torch.empty(1, **f32))
+
+    def step():
+        moe.moe_layer_forward(desc, inp, inp["x"], y, aux, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    tok_s = T / (ms_step * 1e-3)
+
+    # ---- routing facts of this batch (N, non-empty experts)
+    n_kept = int(aux["n_kept"].item())
+    kept = aux["kept"].cpu().numpy()
+    nonempty = int((kept > 0).sum())
+    l_aux = float(aux["l_aux"].item())
+
+    # ---- stages, each through its own entry point on the same buffers
+    cap = moe.moe_capacity(desc)
+    max_rows = min(A, Et * cap) if cap < moe.INT32_MAX else A
+    topk_idx, topk_w, dest_row = aux["topk_idx"], aux["topk_w"], aux["dest_row"]
+    counts, keptb, offsets = torch.empty(Et, **i32), torch.empty(Et, **i32), torch.empty(Et + 1, **i32)
+    src = torch.empty(A, **i32)
+    x_perm = torch.empty((max_rows, d), dtype=inputs.torch_dtype(cfg), device=dev)
+    h_tmp = torch.empty((max_rows, f), dtype=inputs.torch_dtype(cfg), device=dev)
+    y_perm = torch.empty((max_rows, d), dtype=inputs.torch_dtype(cfg), device=dev)
+    pm = torch.empty(Et, **f32)
+    ws_r = moe.workspace(desc, moe.MOE_WS_ROUTE)
+    ws_p = moe.workspace(desc, moe.MOE_WS_PERMUTE)
+    ws_f = moe.workspace(desc, moe.MOE_WS_FFN)
+    R = args.stage_reps
+
+    def route():
+        moe.moe_route(desc, inp["x"], inp["w_router"], inp["logit_bias"], inp["select_bias"], None, 0,
+                      topk_idx, topk_w, None, pm, ws_r)
+
+    def permute():
+        moe.moe_permute(desc, topk_idx, inp["x"], cap, counts, keptb, offsets, dest_row, src, x_perm, None, ws_p)
+
+    def gemm1():
+        moe.moe_grouped_ffn(desc, x_perm, offsets, max_rows, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
+                            y_perm, moe.MOE_FFN_GEMM1, ws_f)
+
+    def gemm2():
+        moe.moe_grouped_ffn(desc, x_perm, offsets, max_rows, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
+                            y_perm, moe.MOE_FFN_GEMM2, ws_f)
+
+    def combine():
+        moe.moe_combine(desc, dest_row, topk_w, y_perm, None, y)
+
+    route()
+    permute()
+    gemm1()
+    gemm2()
+    t_route = timed(route, R, stream)
+    t_perm = timed(permute, R, stream)
+    t_g1 = timed(gemm1, R, stream)
+    t_g2 = timed(gemm2, R, stream)
+    t_comb = timed(combine, R, stream) if not cfg.get("n_shared") and not cfg.get("has_wo") else None
+
+    # algorithmic work (bytes moved / flops the method needs), with this batch's N
+    n_act = 2 if cfg["act"] == "swiglu" else 1
+    gemm1_flops = 2.0 * n_act * n_kept * d * f
+    gemm2_flops = 2.0 * n_kept * f * d
+    route_bytes = T * h * esz + Et * d * esz + A * 8
+    distinct_rows = n_kept  # every kept row is a distinct (token, expert) pair; x rows read once per row
+    permute_bytes = distinct_rows * d * esz + n_kept * d * esz + A * 4 * 2
+    combine_bytes = n_kept * d * esz + A * 8 + T * h * esz
+    w_bytes = nonempty * (n_act + 1) * d * f * esz
+
+    def frac(x, peak):
+        return None if x is None else x / peak
+
+    g1_tfs = gemm1_flops / (t_g1 * 1e-3) / 1e12
+    g2_tfs = gemm2_flops / (t_g2 * 1e-3) / 1e12
+    stages = {
+        "route_ms": t_route, "route_hbm_frac": frac(route_bytes / (t_route * 1e-3) / 1e9, HBM_PEAK_GBS),
+        "permute_ms": t_perm, "permute_hbm_frac": frac(permute_bytes / (t_perm * 1e-3) / 1e9, HBM_PEAK_GBS),
+        "gemm1_ms": t_g1, "gemm1_tflops": g1_tfs, "gemm1_mfma_frac": g1_tfs / MFMA_BF16_PEAK_TFS,
+        "gemm2_ms": t_g2, "gemm2_tflops": g2_tfs, "gemm2_mfma_frac": g2_tfs / MFMA_BF16_PEAK_TFS,
+        "combine_ms": t_comb,
+        "combine_hbm_frac": None if t_comb is None else combine_bytes / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "ffn_mfma_frac": (gemm1_flops + gemm2_flops) / ((t_g1 + t_g2) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+        "ffn_weight_bytes": w_bytes,
+    }
+    total_flops = gemm1_flops + gemm2_flops + 2.0 * T * H * d * E
+    if cfg.get("has_wo"):
+        total_flops += 2.0 * T * h * h
+    if cfg.get("n_shared"):
+        total_flops += 2.0 * (n_act + 1) * T * h * f
+
+    roofline = {
+        "kernel": "gemm_bf16_kernel (grouped gate/up GEMM + SwiGLU)" if n_act == 2 else
+                  "gemm_bf16_kernel (grouped GEMM + GELU)",
+        "bound": "mfma", "achieved": g1_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+        "frac": g1_tfs / MFMA_BF16_PEAK_TFS, "traffic": traffic_from_profile("gemm1", name),
+        "flops_per_launch": gemm1_flops, "launch_ms": t_g1,
+    }
+
+    # ---- CPU oracle baseline on a bounded sample: the first Ts tokens as a batch
+    cpu = None
+    if not args.no_cpu:
+        from oracle import oracle as orc
+
+        def to_np(t):
+            if t is None:
+                return None
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+        log("[bench] copying weights to the host for the CPU oracle")
+        host = {k: to_np(v) for k, v in inp.items()}
+        threads = orc.num_threads()
+        Ts = 2
+        elapsed = 0.0
+        while True:
+            t0 = time.perf_counter()
+            orc.layer_forward(cfg, host, host["x"][:Ts], T=Ts)
+            elapsed = time.perf_counter() - t0
+            if elapsed >= args.cpu_seconds / 4 or Ts >= T:
+                break
+            Ts = min(T, max(Ts * 2, int(Ts * args.cpu_seconds / max(elapsed, 1e-3) / 2)))
+        log(f"[bench] oracle: {Ts} tokens in {elapsed:.2f} s on {threads} threads")
+        cpu = {"value": Ts / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {Ts} tokens of the {name} batch as their own batch (capacity for {Ts} "
+                         f"tokens), full weights; fp64 C oracle, {elapsed:.1f} s"}
+
+    out = {
+        "metric": "MoE-layer fwd tokens/sec on 1 GPU (grouped-FFN % MFMA peak; route/permute % HBM BW)",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg["dtype"], "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": name, "tokens": T, "hidden": h, "heads": H, "experts": E, "top_k": K,
+                   "ffn": f, "act": cfg["act"], "score": cfg["score"], "capacity_factor": cfg["capacity_factor"],
+                   "parallelism": "single GPU"},
+        "tflops": total_flops / (ms_step * 1e-3) / 1e12,
+        "n_kept": n_kept, "n_dropped": A - n_kept, "nonempty_experts": nonempty, "l_aux": l_aux,
+        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
