@@ -85,6 +85,7 @@ struct GArgs {
     void* C;         // [rows][Nout]
     const GemmTile* tiles;
     int m_tiles, n_tiles, K, Nout, total, per_xcd;
+    long long a_bytes;  // bytes of A the tiles may address (buffer bound of the 8-wave kernel)
 };
 
 constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together
@@ -278,6 +279,209 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GArgs a) {
         }
 }
 
+// ------------------------------------------------- bf16 MFMA, 8 waves, LDS ring
+// 512 threads = 8 waves as 2 (M) x 4 (N), two waves per SIMD, each owning a
+// (BM/2) x 64 sub-tile of the BM x 256 block tile (SwiGLU: 32 gate + 32 up
+// columns), accumulators in registers.  A ring of NS = 4 LDS stages of BK = 32
+// is filled by buffer loads that write straight into LDS.  Only waves 0-3 issue
+// loads (a whole stage: BM/4 A rows and 64 weight rows each), so the MFMAs of
+// waves 4-7 keep the matrix cores busy while a loading wave waits to issue; the
+// four loads of a 4 KB run share one M0 value and differ by the instruction
+// offset, which advances the global and the LDS address alike.  The 16-byte
+// chunks of each 64-byte row are XOR-permuted by (row/2)%4 so that the 32x32x16
+// fragment reads (8 lanes = 8 consecutive rows, one chunk) hit 8 distinct
+// 16-byte bank groups; a load lane fetches the logical chunk its LDS slot holds.
+// Iteration kt multiplies stage kt; the first fragments of stage kt+1 are read
+// while the second half of stage kt is multiplied; stage kt+3 is loaded into the
+// slot the barrier ending iteration kt-1 freed.  Needs K % 32 == 0 and every
+// byte offset below 2^31 (checked by the launcher).
+template <int BM, int MODE>
+struct Ring8Cfg {
+    static constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
+    static constexpr int BNM = MODE == MODE_SWIGLU ? 128 : 256;  // output columns per matrix
+    static constexpr int WM = BM / 2;
+    static constexpr int WNM = BNM / 4;
+    static constexpr int TM = WM / 32;
+    static constexpr int TN = WNM / 32;
+    static constexpr int NACC = NMAT * TM * TN;
+    static constexpr int A_BYTES = BM * 64;
+    static constexpr int B_BYTES = 256 * 64;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int NS = 4;
+    static constexpr int A_LOADS = BM / 64;  // per loading wave: BM/4 rows in 16-row loads
+    static constexpr int B_LOADS = 4;        // 64 weight rows per loading wave
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+};
+
+__device__ __forceinline__ int swz32(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt/lgkmcnt at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// gfx9 buffer descriptor word 3 for raw 32-bit-format buffer access
+constexpr int kBufWord3 = 0x00020000;
+
+// N buffer loads into consecutive 1 KB LDS runs sharing one M0 value: load i
+// carries immediate offset 1024*i (a compile-time constant, as the instruction
+// requires), which moves both its global and its LDS address.
+template <int N>
+struct LdsRun {
+    static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t r, lds_void_ptr lds, const uint32_t* v, int soff) {
+        LdsRun<N - 1>::go(r, lds, v, soff);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, v[N - 1], soff, (N - 1) * 1024, 0);
+    }
+};
+template <>
+struct LdsRun<0> {
+    static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t, lds_void_ptr, const uint32_t*, int) {}
+};
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
+    // device pass only: the LDS address-space casts and the buffer-to-LDS loads
+    // have no host meaning; the host pass needs nothing but the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = Ring8Cfg<BM, MODE>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
+
+    int mt, nt;
+    if (!decode_tile(a, mt, nt)) return;
+    const GemmTile tl = a.tiles[mt];
+    if (tl.group < 0) return;
+    const int grp = tl.group, row0 = tl.row0, row_end = tl.row_end;
+    const int K = a.K, Nout = a.Nout;
+    const int n0 = nt * C::BNM;
+    const uint32_t rowbytes = (uint32_t)K * 2u;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const bool loader = wu < 4;
+
+    const uint8_t* Ab = (const uint8_t*)a.A;
+    const uint8_t* B0 = (const uint8_t*)a.B0 + (size_t)grp * Nout * rowbytes;
+    const uint8_t* B1 = MODE == MODE_SWIGLU ? (const uint8_t*)a.B1 + (size_t)grp * Nout * rowbytes : B0;
+    const bool upper = ((wu & 3) * 64) / C::BNM != 0;  // this loader's weight rows come from B1
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rB =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
+
+    // per-lane byte offsets of this loader's rows; load i is issued with
+    // immediate offset 1024*i, so the offset here is reduced by that amount
+    uint32_t va[C::A_LOADS], vb[C::B_LOADS];
+    {
+        const int w4 = wu & 3, lr = lane >> 2, pc = lane & 3;
+#pragma unroll
+        for (int i = 0; i < C::A_LOADS; ++i) {
+            const int r = w4 * (BM / 4) + 16 * i + lr;
+            const int c = pc ^ ((r >> 1) & 3);
+            const int gr = min(row0 + r, row_end - 1);
+            va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+            const int r = w4 * 64 + 16 * i + lr;
+            const int c = pc ^ ((r >> 1) & 3);
+            const int mat = r / C::BNM;
+            const int col = min(n0 + r - mat * C::BNM, Nout - 1);
+            vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+        }
+    }
+    const int a_dst = (wu & 3) * (BM / 4) * 64;
+    const int b_dst = C::A_BYTES + (wu & 3) * 64 * 64;
+    const int nk = K / 32;
+
+    auto issue = [&](int ks, int st) __attribute__((always_inline)) {
+        if (!loader) return;
+        const int koff = ks * 64;
+        uint8_t* la = smem + st * C::STAGE + a_dst;
+        uint8_t* lb = smem + st * C::STAGE + b_dst;
+        LdsRun<C::A_LOADS>::go(rA, (lds_void_ptr)la, va, koff);
+        LdsRun<C::B_LOADS>::go(rB, (lds_void_ptr)lb, vb, koff);
+    };
+    auto load_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
+        const uint8_t* As = smem + st * C::STAGE;
+        const uint8_t* Bs = As + C::A_BYTES;
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+            af[tm] = *(const bf16x8*)(As + swz32(wm * C::WM + tm * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn)
+                bfr[m * C::TN + tn] = *(const bf16x8*)(Bs + swz32(m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31), ch));
+    };
+
+    floatx16 acc[C::NACC];
+#pragma unroll
+    for (int i = 0; i < C::NACC; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+    auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn) {
+                    const int ai = (m * C::TM + tm) * C::TN + tn;
+                    acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[m * C::TN + tn], acc[ai], 0, 0, 0);
+                }
+    };
+
+    // Loads past the last k step re-read it (clamped) into slots nothing reads,
+    // so every iteration has the same shape and the same wait count.
+#pragma unroll
+    for (int s = 0; s < C::NS - 1; ++s) issue(min(s, nk - 1), s);
+    bf16x8 a0[C::TM], b0[C::NMAT * C::TN], a1[C::TM], b1[C::NMAT * C::TN];
+    wait_vmcnt<(C::NS - 3) * C::LOADS>();  // stages 0 and 1 landed (loaders; others have none)
+    __builtin_amdgcn_s_barrier();
+    load_frags(0, 0, a0, b0);
+    for (int kt = 0; kt < nk; ++kt) {
+        issue(min(kt + C::NS - 1, nk - 1), (kt + C::NS - 1) % C::NS);
+        load_frags(kt % C::NS, 1, a1, b1);
+        mfmas(a0, b0);
+        load_frags((kt + 1) % C::NS, 0, a0, b0);  // last step: a valid slot, values unused
+        mfmas(a1, b1);
+        wait_vmcnt<(C::NS - 3) * C::LOADS>();  // stage kt+2 landed
+        __builtin_amdgcn_s_barrier();
+    }
+    wait_vmcnt<0>();
+
+    if constexpr (MODE == MODE_SWIGLU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
+    } else if constexpr (MODE == MODE_GELU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
+    }
+    uint16_t* Cp = (uint16_t*)a.C;
+#pragma clang loop unroll(full)
+    for (int tm = 0; tm < C::TM; ++tm)
+#pragma clang loop unroll(full)
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const int col = n0 + wn * C::WNM + tn * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) {
+                const int row = row0 + wm * C::WM + tm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                if (row < row_end && col < Nout)
+                    Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
+            }
+        }
+#endif
+}
+
 // ------------------------------------------------------------- fp32 VALU
 // 64 x 64 output tile per matrix, BK = 16, 256 threads each computing 4x4.
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -355,7 +559,11 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     g.per_xcd = (g.total + 7) / 8;
     const int blocks = g.per_xcd * 8;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, MODE>), dim3(blocks), dim3(256), 0, st, g);
+    const long long b_bytes = (long long)g.Nout * g.K * 2;
+    if (g.K % 32 == 0 && g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31))
+        hipLaunchKernelGGL((gemm_bf16_ring8_kernel<BM, MODE>), dim3(blocks), dim3(512), 0, st, g);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, MODE>), dim3(blocks), dim3(256), 0, st, g);
     return hipGetLastError();
 }
 
@@ -406,6 +614,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.m_tiles = mtiles;
         g.K = f.d;
         g.Nout = f.f;
+        g.a_bytes = (long long)f.max_rows * f.d * 2;
         err = run_gemm(f.dtype, BM, f.act == MOE_SWIGLU ? MODE_SWIGLU : MODE_GELU, g, st);
         if (err != hipSuccess) return err;
     }
@@ -419,6 +628,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.m_tiles = mtiles;
         g.K = f.f;
         g.Nout = f.d;
+        g.a_bytes = (long long)f.max_rows * f.f * 2;
         err = run_gemm(f.dtype, BM, MODE_PLAIN, g, st);
         if (err != hipSuccess) return err;
     }
@@ -447,6 +657,7 @@ hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const 
     g.m_tiles = mtiles;
     g.K = k;
     g.Nout = n;
+    g.a_bytes = (long long)rows * k * 2;
     return run_gemm(dtype, BM, MODE_PLAIN, g, st);
 }
 
