@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the baseline sample")
     p.add_argument("--stage-reps", type=int, default=10)
+    p.add_argument("--counters", action="store_true",
+                   help="for rocprofv3 --pmc runs: a 1 GiB device copy (counter calibration), then the "
+                        "dominant kernel three times; prints nothing else")
     return p.parse_args()
 
 
@@ -165,18 +168,56 @@ def main():
         moe.moe_grouped_ffn(desc, x_perm, offsets, max_rows, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
                             y_perm, moe.MOE_FFN_GEMM2, ws_f)
 
+    y_sh = None
+    shared_fn = wo_fn = None
+    if cfg.get("n_shared"):
+        # the shared expert is one group of all T rows of x: a dense descriptor
+        dsh = moe.desc_from_cfg(dict(cfg, H=1, E=1, K=1, n_shared=0, has_wo=0, capacity_factor=0.0))
+        off_sh = torch.tensor([0, T], **i32)
+        h_sh = torch.empty((T, f), dtype=inputs.torch_dtype(cfg), device=dev)
+        y_sh = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev)
+        ws_sh = moe.workspace(dsh, moe.MOE_WS_FFN)
+
+        def shared_fn():
+            moe.moe_grouped_ffn(dsh, inp["x"], off_sh, T, inp["sh_gate"], inp["sh_up"], inp["sh_down"], h_sh,
+                                y_sh, 0, ws_sh)
+    y_cat = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev) if cfg.get("has_wo") else None
+    if cfg.get("has_wo"):
+        # W_o is the second GEMM of a one-group descriptor with f = h
+        dwo = moe.desc_from_cfg(dict(cfg, H=1, E=1, K=1, f=h, n_shared=0, has_wo=0, capacity_factor=0.0))
+        off_wo = torch.tensor([0, T], **i32)
+        ws_wo = moe.workspace(dwo, moe.MOE_WS_FFN)
+
+        def wo_fn():
+            moe.moe_grouped_ffn(dwo, None, off_wo, T, None, None, inp["w_o"], y_cat, y, moe.MOE_FFN_GEMM2, ws_wo)
+
     def combine():
-        moe.moe_combine(desc, dest_row, topk_w, y_perm, None, y)
+        moe.moe_combine(desc, dest_row, topk_w, y_perm, y_sh, y_cat if y_cat is not None else y)
 
     route()
     permute()
+    if args.counters:
+        torch.cuda.synchronize()
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            gemm1()
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": name, "copy_bytes": 1 << 30}), flush=True)
+        return
     gemm1()
     gemm2()
+    if shared_fn:
+        shared_fn()
     t_route = timed(route, R, stream)
     t_perm = timed(permute, R, stream)
     t_g1 = timed(gemm1, R, stream)
     t_g2 = timed(gemm2, R, stream)
-    t_comb = timed(combine, R, stream) if not cfg.get("n_shared") and not cfg.get("has_wo") else None
+    t_comb = timed(combine, R, stream)
+    t_sh = timed(shared_fn, R, stream) if shared_fn else None
+    t_wo = timed(wo_fn, R, stream) if wo_fn else None
 
     # algorithmic work (bytes moved / flops the method needs), with this batch's N
     n_act = 2 if cfg["act"] == "swiglu" else 1
@@ -185,7 +226,7 @@ def main():
     route_bytes = T * h * esz + Et * d * esz + A * 8
     distinct_rows = n_kept  # every kept row is a distinct (token, expert) pair; x rows read once per row
     permute_bytes = distinct_rows * d * esz + n_kept * d * esz + A * 4 * 2
-    combine_bytes = n_kept * d * esz + A * 8 + T * h * esz
+    combine_bytes = n_kept * d * esz + A * 8 + T * h * esz + (T * h * esz if cfg.get("n_shared") else 0)
     w_bytes = nonempty * (n_act + 1) * d * f * esz
 
     def frac(x, peak):
@@ -199,7 +240,12 @@ def main():
         "gemm1_ms": t_g1, "gemm1_tflops": g1_tfs, "gemm1_mfma_frac": g1_tfs / MFMA_BF16_PEAK_TFS,
         "gemm2_ms": t_g2, "gemm2_tflops": g2_tfs, "gemm2_mfma_frac": g2_tfs / MFMA_BF16_PEAK_TFS,
         "combine_ms": t_comb,
-        "combine_hbm_frac": None if t_comb is None else combine_bytes / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "combine_hbm_frac": combine_bytes / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "shared_ffn_ms": t_sh,
+        "shared_ffn_tflops": None if t_sh is None else 2.0 * (n_act + 1) * T * h * f / (t_sh * 1e-3) / 1e12,
+        "w_o_ms": t_wo,
+        "w_o_tflops": None if t_wo is None else 2.0 * T * h * h / (t_wo * 1e-3) / 1e12,
+        "sum_of_stages_ms": t_route + t_perm + t_g1 + t_g2 + t_comb + (t_sh or 0.0) + (t_wo or 0.0),
         "ffn_mfma_frac": (gemm1_flops + gemm2_flops) / ((t_g1 + t_g2) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "ffn_weight_bytes": w_bytes,
     }

@@ -76,6 +76,12 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
         t.row0 = t.row_end = t.pad = 0;
         tiles[i] = t;
     }
+    if (tid == 0) {  // header after the table: the number of real tiles
+        GemmTile h;
+        h.group = min(total, max_tiles);
+        h.row0 = h.row_end = h.pad = 0;
+        tiles[max_tiles] = h;
+    }
 }
 
 struct GArgs {
@@ -307,7 +313,9 @@ struct Ring8Cfg {
     static constexpr int A_BYTES = BM * 64;
     static constexpr int B_BYTES = 256 * 64;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int NS = 4;
+    // ring depth: as many 32-wide k steps as fit in 160 KB of LDS (4 x 32 KB for
+    // BM = 256, 6 x 24 KB for BM = 128), so NS-2 steps of loads are in flight
+    static constexpr int NS = BM == 256 ? 4 : 6;
     static constexpr int A_LOADS = BM / 64;  // per loading wave: BM/4 rows in 16-row loads
     static constexpr int B_LOADS = 4;        // 64 weight rows per loading wave
     static constexpr int LOADS = A_LOADS + B_LOADS;
@@ -342,6 +350,13 @@ struct LdsRun<0> {
     static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t, lds_void_ptr, const uint32_t*, int) {}
 };
 
+// Persistent form: one block per CU.  XCD x (blocks b with b % 8 == x) takes a
+// contiguous slice of the tile schedule and its 32 CUs walk it round-robin, so
+// the tiles running at once on an XCD are neighbours in the schedule (groups of
+// NGROUP weight-column tiles sweeping one expert's row tiles) and share their
+// rows in that XCD's L2.  When a tile's k loop ends, every LDS slot is free:
+// the first stages of the block's next tile are loaded before the current
+// tile's epilogue, which hides their latency.
 template <int BM, int MODE>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     // device pass only: the LDS address-space casts and the buffer-to-LDS loads
@@ -350,60 +365,90 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     using C = Ring8Cfg<BM, MODE>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
 
-    int mt, nt;
-    if (!decode_tile(a, mt, nt)) return;
-    const GemmTile tl = a.tiles[mt];
-    if (tl.group < 0) return;
-    const int grp = tl.group, row0 = tl.row0, row_end = tl.row_end;
-    const int K = a.K, Nout = a.Nout;
-    const int n0 = nt * C::BNM;
-    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int n_m = a.tiles[a.m_tiles].group;  // real row tiles (header of the table)
+    const int total = n_m * a.n_tiles;
+    const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
+    const int q = (total + 7) / 8;
+    const int s_end = min((xcd + 1) * q, total);
+    int s = xcd * q + (blockIdx.x >> 3);
+    if (s >= s_end) return;
 
+    const int K = a.K, Nout = a.Nout;
+    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int nk = K / 32;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const bool loader = wu < 4;
-
+    const int w4 = wu & 3;
+    const bool upper = (w4 * 64) / C::BNM != 0;  // this loader's weight rows come from B1 (SwiGLU up)
+    const int a_dst = w4 * (BM / 4) * 64;
+    const int b_dst = C::A_BYTES + w4 * 64 * 64;
     const uint8_t* Ab = (const uint8_t*)a.A;
-    const uint8_t* B0 = (const uint8_t*)a.B0 + (size_t)grp * Nout * rowbytes;
-    const uint8_t* B1 = MODE == MODE_SWIGLU ? (const uint8_t*)a.B1 + (size_t)grp * Nout * rowbytes : B0;
-    const bool upper = ((wu & 3) * 64) / C::BNM != 0;  // this loader's weight rows come from B1
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
-    const __amdgpu_buffer_rsrc_t rB =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
 
+    // schedule index -> (row tile, column tile): groups of NGROUP column tiles,
+    // each sweeping every real row tile
+    auto decode = [&](int si, int& mt, int& nt) __attribute__((always_inline)) {
+        const int gsz = n_m * NGROUP;
+        const int nb = si / gsz;
+        const int rem = si - nb * gsz;
+        const int width = min(NGROUP, a.n_tiles - nb * NGROUP);
+        mt = rem / width;
+        nt = nb * NGROUP + (rem - mt * width);
+    };
+    struct Tile {
+        int row0, row_end, n0;
+        __amdgpu_buffer_rsrc_t rB;
+        uint32_t va[C::A_LOADS], vb[C::B_LOADS];
+    };
     // per-lane byte offsets of this loader's rows; load i is issued with
     // immediate offset 1024*i, so the offset here is reduced by that amount
-    uint32_t va[C::A_LOADS], vb[C::B_LOADS];
-    {
-        const int w4 = wu & 3, lr = lane >> 2, pc = lane & 3;
+    auto setup = [&](int si, Tile& t) __attribute__((always_inline)) {
+        int mt, nt;
+        decode(si, mt, nt);
+        const GemmTile tl = a.tiles[mt];
+        t.row0 = tl.row0;
+        t.row_end = tl.row_end;
+        t.n0 = nt * C::BNM;
+        const uint8_t* B0 = (const uint8_t*)a.B0 + (size_t)tl.group * Nout * rowbytes;
+        const uint8_t* B1 = MODE == MODE_SWIGLU ? (const uint8_t*)a.B1 + (size_t)tl.group * Nout * rowbytes : B0;
+        t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
+        const int lr = lane >> 2, pc = lane & 3;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
             const int r = w4 * (BM / 4) + 16 * i + lr;
             const int c = pc ^ ((r >> 1) & 3);
-            const int gr = min(row0 + r, row_end - 1);
-            va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+            const int gr = min(t.row0 + r, t.row_end - 1);
+            t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
             const int r = w4 * 64 + 16 * i + lr;
             const int c = pc ^ ((r >> 1) & 3);
             const int mat = r / C::BNM;
-            const int col = min(n0 + r - mat * C::BNM, Nout - 1);
-            vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+            const int col = min(t.n0 + r - mat * C::BNM, Nout - 1);
+            t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
-    }
-    const int a_dst = (wu & 3) * (BM / 4) * 64;
-    const int b_dst = C::A_BYTES + (wu & 3) * 64 * 64;
-    const int nk = K / 32;
-
-    auto issue = [&](int ks, int st) __attribute__((always_inline)) {
+    };
+    auto issue = [&](const Tile& t, int ks, int st) __attribute__((always_inline)) {
         if (!loader) return;
         const int koff = ks * 64;
-        uint8_t* la = smem + st * C::STAGE + a_dst;
-        uint8_t* lb = smem + st * C::STAGE + b_dst;
-        LdsRun<C::A_LOADS>::go(rA, (lds_void_ptr)la, va, koff);
-        LdsRun<C::B_LOADS>::go(rB, (lds_void_ptr)lb, vb, koff);
+        uint8_t* base = smem + st * C::STAGE;
+        LdsRun<C::A_LOADS>::go(rA, (lds_void_ptr)(base + a_dst), t.va, koff);
+        LdsRun<C::B_LOADS>::go(t.rB, (lds_void_ptr)(base + b_dst), t.vb, koff);
+    };
+    auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < C::NS - 1; ++st)
+            if (st < nk) issue(t, st, st);
+    };
+    // wait until at most `n` k steps of this wave's loads are still in flight
+    auto wait_steps = [&](int n) __attribute__((always_inline)) {
+        if (n >= 3) wait_vmcnt<3 * C::LOADS>();
+        else if (n == 2) wait_vmcnt<2 * C::LOADS>();
+        else if (n == 1) wait_vmcnt<C::LOADS>();
+        else wait_vmcnt<0>();
     };
     auto load_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
         const uint8_t* As = smem + st * C::STAGE;
@@ -418,12 +463,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
             for (int tn = 0; tn < C::TN; ++tn)
                 bfr[m * C::TN + tn] = *(const bf16x8*)(Bs + swz32(m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31), ch));
     };
-
     floatx16 acc[C::NACC];
-#pragma unroll
-    for (int i = 0; i < C::NACC; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
     auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
@@ -436,49 +476,65 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
                 }
     };
 
-    // Loads past the last k step re-read it (clamped) into slots nothing reads,
-    // so every iteration has the same shape and the same wait count.
-#pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s) issue(min(s, nk - 1), s);
+    Tile cur;
+    setup(s, cur);
+    prologue(cur);
     bf16x8 a0[C::TM], b0[C::NMAT * C::TN], a1[C::TM], b1[C::NMAT * C::TN];
-    wait_vmcnt<(C::NS - 3) * C::LOADS>();  // stages 0 and 1 landed (loaders; others have none)
-    __builtin_amdgcn_s_barrier();
-    load_frags(0, 0, a0, b0);
-    for (int kt = 0; kt < nk; ++kt) {
-        issue(min(kt + C::NS - 1, nk - 1), (kt + C::NS - 1) % C::NS);
-        load_frags(kt % C::NS, 1, a1, b1);
-        mfmas(a0, b0);
-        load_frags((kt + 1) % C::NS, 0, a0, b0);  // last step: a valid slot, values unused
-        mfmas(a1, b1);
-        wait_vmcnt<(C::NS - 3) * C::LOADS>();  // stage kt+2 landed
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < C::NACC; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+        wait_steps(min(C::NS - 3, nk - 2));  // steps 0 and 1 landed
         __builtin_amdgcn_s_barrier();
+        load_frags(0, 0, a0, b0);
+        for (int kt = 0; kt < nk; ++kt) {
+            if (kt + C::NS - 1 < nk) issue(cur, kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+            load_frags(kt % C::NS, 1, a1, b1);
+            mfmas(a0, b0);
+            load_frags((kt + 1) % C::NS, 0, a0, b0);  // last step: a valid slot, values unused
+            mfmas(a1, b1);
+            wait_steps(min(C::NS - 3, nk - 3 - kt));  // step kt+2 landed
+            __builtin_amdgcn_s_barrier();
+        }
+        // every slot is free: start the next tile's loads, then store this one
+        const int s_next = s + per;
+        const bool more = s_next < s_end;
+        Tile nxt;
+        if (more) {
+            setup(s_next, nxt);
+            prologue(nxt);
+        }
+        const int row0 = cur.row0, row_end = cur.row_end, n0 = cur.n0;
+        if constexpr (MODE == MODE_SWIGLU) {
+#pragma clang loop unroll(full)
+            for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+                for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
+        } else if constexpr (MODE == MODE_GELU) {
+#pragma clang loop unroll(full)
+            for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+                for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
+        }
+        uint16_t* Cp = (uint16_t*)a.C;
+#pragma clang loop unroll(full)
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma clang loop unroll(full)
+            for (int tn = 0; tn < C::TN; ++tn) {
+                const int col = n0 + wn * C::WNM + tn * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+                for (int i = 0; i < 16; ++i) {
+                    const int row = row0 + wm * C::WM + tm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                    if (row < row_end && col < Nout)
+                        Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
+                }
+            }
+        if (!more) break;
+        cur = nxt;
+        s = s_next;
     }
     wait_vmcnt<0>();
-
-    if constexpr (MODE == MODE_SWIGLU) {
-#pragma clang loop unroll(full)
-        for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
-    } else if constexpr (MODE == MODE_GELU) {
-#pragma clang loop unroll(full)
-        for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
-    }
-    uint16_t* Cp = (uint16_t*)a.C;
-#pragma clang loop unroll(full)
-    for (int tm = 0; tm < C::TM; ++tm)
-#pragma clang loop unroll(full)
-        for (int tn = 0; tn < C::TN; ++tn) {
-            const int col = n0 + wn * C::WNM + tn * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) {
-                const int row = row0 + wm * C::WM + tm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                if (row < row_end && col < Nout)
-                    Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
-            }
-        }
 #endif
 }
 
@@ -540,15 +596,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GArgs a) {
 }
 
 // ------------------------------------------------------------- launchers
+// 256-row tiles when groups average 512 rows or more; otherwise 128-row tiles,
+// which waste less of a ragged group and keep a deeper load ring
 static int pick_bm(int dtype, int G, int max_rows) {
     if (dtype != MOE_BF16) return FBM;
-    return (G > 0 && max_rows / G >= 256) ? 256 : 128;
+    return (G > 0 && max_rows / G >= 512) ? 256 : 128;
 }
 static int max_m_tiles(int BM, int G, int max_rows) { return (max_rows + BM - 1) / BM + G; }
 
 size_t ffn_workspace_bytes(int G, int max_rows, int dtype) {
     const int BM = pick_bm(dtype, G, max_rows);
-    return (size_t)max_m_tiles(BM, G, max_rows) * sizeof(GemmTile);
+    return (size_t)(max_m_tiles(BM, G, max_rows) + 1) * sizeof(GemmTile);  // + header
+}
+
+// one block per compute unit of the current device (a multiple of the 8 XCDs)
+static int persistent_blocks() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus < 8 ? 8 : cus - cus % 8;
+    }
+    return cached[dev];
 }
 
 template <int BM, int MODE>
@@ -560,9 +631,11 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     const int blocks = g.per_xcd * 8;
     if (blocks == 0) return hipSuccess;
     const long long b_bytes = (long long)g.Nout * g.K * 2;
-    if (g.K % 32 == 0 && g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31))
-        hipLaunchKernelGGL((gemm_bf16_ring8_kernel<BM, MODE>), dim3(blocks), dim3(512), 0, st, g);
-    else
+    if (g.K % 32 == 0 && g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31)) {
+        using R = Ring8Cfg<BM, MODE>;
+        g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+        hipLaunchKernelGGL((gemm_bf16_ring8_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+    } else
         hipLaunchKernelGGL((gemm_bf16_kernel<BM, MODE>), dim3(blocks), dim3(256), 0, st, g);
     return hipGetLastError();
 }

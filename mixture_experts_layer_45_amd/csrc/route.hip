@@ -286,14 +286,22 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     (void)Et;
 }
 
-// P_e = (sum over the head's blocks, in block order) / T
-__global__ void prob_mean_kernel(const float* part, int nbx, int H, int E, int T, float* out) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= H * E) return;
+// P_e = (sum over the head's block partials) / T.  One block per expert: thread
+// i sums partials i, i+256, ... in order, then a fixed LDS tree; the order
+// depends only on the sizes, so P is reproducible.
+__global__ __launch_bounds__(256) void prob_mean_kernel(const float* part, int nbx, int H, int E, int T, float* out) {
+    __shared__ float red[256];
+    const int i = blockIdx.x;  // global expert g*E + e
     const int g = i / E, e = i - g * E;
     float s = 0.0f;
-    for (int b = 0; b < nbx; ++b) s += part[((size_t)g * nbx + b) * E + e];
-    out[i] = T > 0 ? s / (float)T : 0.0f;
+    for (int b = threadIdx.x; b < nbx; b += 256) s += part[((size_t)g * nbx + b) * E + e];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[i] = T > 0 ? red[0] / (float)T : 0.0f;
 }
 
 template <int NB>
@@ -316,7 +324,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 
 hipError_t launch_prob_mean(const float* part, int nbx, int H, int E, int T, float* out, hipStream_t st) {
     const int n = H * E;
-    hipLaunchKernelGGL(prob_mean_kernel, dim3((n + 255) / 256), dim3(256), 0, st, part, nbx, H, E, T, out);
+    hipLaunchKernelGGL(prob_mean_kernel, dim3(n), dim3(256), 0, st, part, nbx, H, E, T, out);
     return hipGetLastError();
 }
 
