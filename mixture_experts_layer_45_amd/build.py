@@ -27,7 +27,12 @@ COMMON = [
     "-fno-gpu-rdc", "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"),
 ]
-PER_FILE = {"route.hip": ["-ffp-contract=off"]}
+# route.hip: the selection keys must round exactly as specified (no contraction).
+# gemm.hip: the one-lane tile claim must stay a plain atomic whose result is
+# waited for only where it is used, not rewritten into a wave-wide reduction
+# that waits (and drains the wave's in-flight loads) right after it.
+PER_FILE = {"route.hip": ["-ffp-contract=off"],
+            "gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src, verbose):

@@ -10,20 +10,26 @@
 // first writes a table of the real M-tiles (group, first row, end row); the
 // GEMM blocks read their tile from it and surplus blocks exit.
 //
-// bf16 kernel (gfx950): 256 threads = 4 waves as 2x2, a BM x 256 output tile
-// (for SwiGLU: 128 gate columns and the same 128 up columns, so the epilogue
-// has both halves of silu(g)*u), BK = 64, v_mfma_f32_32x32x16_bf16 with fp32
-// accumulators, A and B staged through LDS in two buffers (the global loads of
-// step k+1 are in flight while step k's MFMAs run), 16-byte chunks XOR-swizzled
-// by row so the fragment reads are bank-conflict free.  The activation is fused
-// into the epilogue and the result is rounded once to bf16.  Blocks are mapped
-// so each XCD (own L2) works through a contiguous run of tiles that share
-// weight columns and rows.
+// Three bf16 kernels for gfx950 share the tile table, the XCD-aware schedule
+// and the fused epilogue (activation in fp32, one rounding to bf16):
+//   * gemm_bf16_k64_kernel  -- plain products (down projection, W_o) when K is a
+//     multiple of 64: persistent, 8 waves, BM x 256 tiles, 64-wide k stages of
+//     whole 128-byte rows, 16-byte row stores;
+//   * gemm_bf16_ring8_kernel -- gated products (SwiGLU gate/up, GELU) and plain
+//     ones with K % 64 != 0 but K % 32 == 0: persistent, 8 waves, a deeper ring
+//     of 32-wide k stages;
+//   * gemm_bf16_kernel -- any K (zero-filled tail), 4 waves, one tile per block.
+// On the top-2 8-expert shapes the ring kernel measured ahead on the gated
+// product (K = 4096) and the 64-wide kernel on the down projection (K = 14336).
 #include "common.hpp"
 
 namespace moe {
 
 enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_PLAIN = 2 };
+
+// tile-claim counters after the tile table's header: 4 GemmTile entries = 16
+// counters, 8 (one per XCD) for each of the two GEMM launches sharing a table
+constexpr int kClaimSets = 4;
 
 // ------------------------------------------------------------- tile table
 // Row ranges are clamped to [0, max_rows) so inconsistent offsets can never send
@@ -82,6 +88,10 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
         h.row0 = h.row_end = h.pad = 0;
         tiles[max_tiles] = h;
     }
+    // then the tile-claim counters of the GEMM launches that use this table
+    // (8 per launch, one per XCD), cleared here because the table is rebuilt
+    // in stream order before every such launch
+    if (tid < 4 * kClaimSets) ((int32_t*)(tiles + max_tiles + 1))[tid] = 0;
 }
 
 struct GArgs {
@@ -92,6 +102,7 @@ struct GArgs {
     const GemmTile* tiles;
     int m_tiles, n_tiles, K, Nout, total, per_xcd;
     long long a_bytes;  // bytes of A the tiles may address (buffer bound of the 8-wave kernel)
+    int32_t* claim;     // 8 zeroed tile-claim counters for this launch (persistent kernels)
 };
 
 constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together
@@ -112,14 +123,17 @@ __device__ __forceinline__ bool decode_tile(const GArgs& a, int& mt, int& nt) {
     return true;
 }
 
-__device__ __forceinline__ float act_silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (about 1 ulp in fp32):
+// the result is rounded to bf16 (relative 2^-9) right after, so an IEEE
+// division sequence per element would buy nothing but epilogue time
+__device__ __forceinline__ float act_silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 // erf by Abramowitz and Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26 (|error| <= 1.5e-7 for x >= 0, odd extension below 0): inline, so the
 // epilogue keeps its accumulators in registers.  The bf16 rounding of the
 // result (relative 2^-9) dwarfs the approximation error.
 __device__ __forceinline__ float erf_as(float x) {
     const float ax = fabsf(x);
-    const float t = 1.0f / (1.0f + 0.3275911f * ax);
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
     float p = 1.061405429f;
     p = p * t - 1.453152027f;
     p = p * t + 1.421413741f;
@@ -301,6 +315,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GArgs a) {
 // while the second half of stage kt is multiplied; stage kt+3 is loaded into the
 // slot the barrier ending iteration kt-1 freed.  Needs K % 32 == 0 and every
 // byte offset below 2^31 (checked by the launcher).
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
 template <int BM, int MODE>
 struct Ring8Cfg {
     static constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
@@ -351,10 +370,13 @@ struct LdsRun<0> {
 };
 
 // Persistent form: one block per CU.  XCD x (blocks b with b % 8 == x) takes a
-// contiguous slice of the tile schedule and its 32 CUs walk it round-robin, so
-// the tiles running at once on an XCD are neighbours in the schedule (groups of
-// NGROUP weight-column tiles sweeping one expert's row tiles) and share their
-// rows in that XCD's L2.  When a tile's k loop ends, every LDS slot is free:
+// contiguous slice of the tile schedule: its blocks start on the slice's first
+// tiles and then claim the next unclaimed one from the XCD's counter (claimed at
+// the start of a tile, so the atomic's latency hides under the k loop).  Tiles
+// running at once on an XCD stay neighbours in the schedule (groups of NGROUP
+// weight-column tiles sweeping one expert's row tiles) and share their rows in
+// that XCD's L2, and a block that drew short tiles (the ragged last row tile
+// of an expert) simply takes more of them.  When a tile's k loop ends, every LDS slot is free:
 // the first stages of the block's next tile are loaded before the current
 // tile's epilogue, which hides their latency.
 template <int BM, int MODE>
@@ -363,7 +385,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     // have no host meaning; the host pass needs nothing but the launch stub
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Ring8Cfg<BM, MODE>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
+    // the stages, then one word for the tile this block claimed for after the
+    // current one (inside the same LDS array, so the compiler sees a single
+    // LDS object and does not order fragment reads behind in-flight loads)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + 16];
+    int32_t& next_tile = *(int32_t*)(smem + C::NS * C::STAGE);
 
     const int n_m = a.tiles[a.m_tiles].group;  // real row tiles (header of the table)
     const int total = n_m * a.n_tiles;
@@ -450,13 +476,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
         else if (n == 1) wait_vmcnt<C::LOADS>();
         else wait_vmcnt<0>();
     };
-    auto load_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
+    // nv: this wave's 32-row blocks that hold rows of the tile (the others are
+    // neither read nor multiplied; their accumulators stay zero, stores skip them)
+    auto load_frags = [&](int st, int kk, bf16x8* af, bf16x8* bfr, int nv) __attribute__((always_inline)) {
         const uint8_t* As = smem + st * C::STAGE;
         const uint8_t* Bs = As + C::A_BYTES;
         const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm)
-            af[tm] = *(const bf16x8*)(As + swz32(wm * C::WM + tm * 32 + (lane & 31), ch));
+            if (tm < nv) af[tm] = *(const bf16x8*)(As + swz32(wm * C::WM + tm * 32 + (lane & 31), ch));
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
@@ -464,13 +492,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
                 bfr[m * C::TN + tn] = *(const bf16x8*)(Bs + swz32(m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31), ch));
     };
     floatx16 acc[C::NACC];
-    auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) __attribute__((always_inline)) {
+    auto mfmas = [&](const bf16x8* af, const bf16x8* bfr, int nv) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
                 for (int tn = 0; tn < C::TN; ++tn) {
+                    if (tm >= nv) continue;
                     const int ai = (m * C::TM + tm) * C::TN + tn;
                     acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[m * C::TN + tn], acc[ai], 0, 0, 0);
                 }
@@ -480,25 +509,44 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     setup(s, cur);
     prologue(cur);
     bf16x8 a0[C::TM], b0[C::NMAT * C::TN], a1[C::TM], b1[C::NMAT * C::TN];
+    int32_t claim = 0;  // lane 0 of wave 0: the claim counter's answer for the current tile
     while (true) {
 #pragma unroll
         for (int i = 0; i < C::NACC; ++i)
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+        // claim the block's next tile now; the answer is needed only after the k loop
+        if (tid == 0) claim = __hip_atomic_fetch_add(a.claim + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         wait_steps(min(C::NS - 3, nk - 2));  // steps 0 and 1 landed
         __builtin_amdgcn_s_barrier();
-        load_frags(0, 0, a0, b0);
-        for (int kt = 0; kt < nk; ++kt) {
-            if (kt + C::NS - 1 < nk) issue(cur, kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
-            load_frags(kt % C::NS, 1, a1, b1);
-            mfmas(a0, b0);
-            load_frags((kt + 1) % C::NS, 0, a0, b0);  // last step: a valid slot, values unused
-            mfmas(a1, b1);
-            wait_steps(min(C::NS - 3, nk - 3 - kt));  // step kt+2 landed
-            __builtin_amdgcn_s_barrier();
+        auto kloop = [&](auto NV) __attribute__((always_inline)) {
+            constexpr int nv = decltype(NV)::value;
+            load_frags(0, 0, a0, b0, nv);
+            for (int kt = 0; kt < nk; ++kt) {
+                if (kt + C::NS - 1 < nk) issue(cur, kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+                load_frags(kt % C::NS, 1, a1, b1, nv);
+                mfmas(a0, b0, nv);
+                load_frags((kt + 1) % C::NS, 0, a0, b0, nv);  // last step: a valid slot, values unused
+                mfmas(a1, b1, nv);
+                wait_steps(min(C::NS - 3, nk - 3 - kt));  // step kt+2 landed
+                if (kt == nk - 1) {  // this wave's loads (and the claim) have landed
+                    if (tid == 0) next_tile = xcd * q + per + claim;
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the write is visible at the barrier
+                }
+                __builtin_amdgcn_s_barrier();
+            }
+        };
+        // a ragged last row tile of a group leaves some waves' row blocks empty
+        const int nvb = __builtin_amdgcn_readfirstlane(min(max((cur.row_end - cur.row0 - wm * C::WM + 31) / 32, 0), C::TM));
+        if (nvb == C::TM) kloop(IntC<C::TM>{});
+        else if (nvb == 0) kloop(IntC<0>{});
+        else if (nvb == 1) kloop(IntC<1>{});
+        else if constexpr (C::TM > 2) {
+            if (nvb == 2) kloop(IntC<2>{});
+            else kloop(IntC<3>{});
         }
         // every slot is free: start the next tile's loads, then store this one
-        const int s_next = s + per;
+        const int s_next = __builtin_amdgcn_readfirstlane(next_tile);
         const bool more = s_next < s_end;
         Tile nxt;
         if (more) {
@@ -530,6 +578,264 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
                         Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
                 }
             }
+        if (!more) break;
+        cur = nxt;
+        s = s_next;
+    }
+    wait_vmcnt<0>();
+#endif
+}
+
+// ------------------------------------- bf16 MFMA, 8 waves, 64-wide k stages
+// The block tile and wave grid of the ring kernel, but each LDS stage holds 64
+// k values: every row of a stage is one whole 128-byte line of global memory,
+// so a load instruction (64 lanes x 16 bytes = 8 rows) asks the L2 for full
+// lines and no later k step re-requests the other half of a line.  The 16-byte
+// chunks of a 128-byte row are XOR-permuted by (row/2)%8: the 16 lanes that the
+// LDS serves together in a fragment read (16 consecutive rows, one chunk) then
+// cover all 16 distinct 16-byte bank groups.  Two stages (BM = 256, 128 KB) or
+// three (BM = 128, 144 KB); all eight waves load.
+//
+// The MFMA takes the weight fragment as its first operand, so a lane's
+// accumulators run along an output row: lane l holds row l%32 and, in group q
+// of four, columns 8q + 4*(l/32) + 0..3.  One v_permlane32_swap per register
+// pair hands lane l the partner lane's half, after which every lane stores 8
+// consecutive bf16 (16 bytes) -- two stores per 32x32 tile instead of sixteen.
+template <int BM, int MODE>
+struct K64Cfg {
+    static constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
+    static constexpr int BNM = MODE == MODE_SWIGLU ? 128 : 256;  // output columns per matrix
+    static constexpr int WM = BM / 2;
+    static constexpr int WNM = BNM / 4;
+    static constexpr int TM = WM / 32;
+    static constexpr int TN = WNM / 32;
+    static constexpr int NACC = NMAT * TM * TN;
+    static constexpr int NFR = TM + NMAT * TN;  // fragments per 16-wide k step
+    static constexpr int A_BYTES = BM * 128;
+    static constexpr int B_BYTES = 256 * 128;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int NS = BM == 256 ? 2 : 3;
+    static constexpr int A_PW = BM / 64;  // activation loads per wave per stage (8 rows each)
+    static constexpr int B_PW = 4;        // weight loads per wave per stage (32 rows)
+    static constexpr int LPW = A_PW + B_PW;
+};
+
+__device__ __forceinline__ int swz64(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = K64Cfg<BM, MODE>;
+    constexpr int NS = C::NS;
+    // the stages, then one word for the tile this block claimed for after the
+    // current one (inside the same LDS array, so the compiler sees a single
+    // LDS object and does not order fragment reads behind in-flight loads)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE + 16];
+    int32_t& next_tile = *(int32_t*)(smem + NS * C::STAGE);
+
+    const int n_m = a.tiles[a.m_tiles].group;  // real row tiles (header of the table)
+    const int total = n_m * a.n_tiles;
+    const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
+    const int q = (total + 7) / 8;
+    const int s_end = min((xcd + 1) * q, total);
+    int s = xcd * q + (blockIdx.x >> 3);
+    if (s >= s_end) return;
+
+    const int K = a.K, Nout = a.Nout;
+    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int nk = K / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const bool upper = (wu * 32) / C::BNM != 0;  // this wave's weight rows come from B1 (SwiGLU up)
+    const int a_dst = wu * (BM / 8) * 128;
+    const int b_dst = C::A_BYTES + wu * 32 * 128;
+    const uint8_t* Ab = (const uint8_t*)a.A;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
+
+    auto decode = [&](int si, int& mt, int& nt) __attribute__((always_inline)) {
+        const int gsz = n_m * NGROUP;
+        const int nb = si / gsz;
+        const int rem = si - nb * gsz;
+        const int width = min(NGROUP, a.n_tiles - nb * NGROUP);
+        mt = rem / width;
+        nt = nb * NGROUP + (rem - mt * width);
+    };
+    struct Tile {
+        int row0, row_end, n0;
+        __amdgpu_buffer_rsrc_t rB;
+        uint32_t va[C::A_PW], vb[C::B_PW];
+    };
+    // per-lane byte offsets: lane l fills LDS chunk l%8 of row l/8 of its 8-row
+    // run, so it fetches the logical chunk stored there; load i carries
+    // immediate offset 1024*i, which is taken off here
+    auto setup = [&](int si, Tile& t) __attribute__((always_inline)) {
+        int mt, nt;
+        decode(si, mt, nt);
+        const GemmTile tl = a.tiles[mt];
+        t.row0 = tl.row0;
+        t.row_end = tl.row_end;
+        t.n0 = nt * C::BNM;
+        const uint8_t* B0 = (const uint8_t*)a.B0 + (size_t)tl.group * Nout * rowbytes;
+        const uint8_t* B1 = MODE == MODE_SWIGLU ? (const uint8_t*)a.B1 + (size_t)tl.group * Nout * rowbytes : B0;
+        t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
+        const int lr = lane >> 3, pc = lane & 7;
+#pragma unroll
+        for (int i = 0; i < C::A_PW; ++i) {
+            const int r = wu * (BM / 8) + 8 * i + lr;
+            const int c = pc ^ ((r >> 1) & 7);
+            const int gr = min(t.row0 + r, t.row_end - 1);
+            t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_PW; ++i) {
+            const int r = wu * 32 + 8 * i + lr;
+            const int c = pc ^ ((r >> 1) & 7);
+            const int mat = r / C::BNM;
+            const int col = min(t.n0 + r - mat * C::BNM, Nout - 1);
+            t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+        }
+    };
+    auto issue_a = [&](const Tile& t, int ks) __attribute__((always_inline)) {
+        LdsRun<C::A_PW>::go(rA, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + a_dst), t.va, ks * 128);
+    };
+    auto issue_b = [&](const Tile& t, int ks) __attribute__((always_inline)) {
+        LdsRun<C::B_PW>::go(t.rB, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + b_dst), t.vb, ks * 128);
+    };
+    auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st)
+            if (st < nk) {
+                issue_a(t, st);
+                issue_b(t, st);
+            }
+    };
+    // wait until at most n stages of this wave's loads are in flight (n <= 1)
+    auto wait_stages = [&](int n) __attribute__((always_inline)) {
+        if (n >= 1) wait_vmcnt<C::LPW>();
+        else wait_vmcnt<0>();
+    };
+    // nv: this wave's 32-row blocks that hold rows of the tile (the others are
+    // neither read nor multiplied; their accumulators stay zero, stores skip them)
+    auto read_frags = [&](int st, int kk, bf16x8* fr, int nv) __attribute__((always_inline)) {
+        const uint8_t* As = smem + st * C::STAGE;
+        const uint8_t* Bs = As + C::A_BYTES;
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+            if (tm < nv) fr[tm] = *(const bf16x8*)(As + swz64(wm * C::WM + tm * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn)
+                fr[C::TM + m * C::TN + tn] = *(const bf16x8*)(Bs + swz64(m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31), ch));
+    };
+    floatx16 acc[C::NACC];
+    auto mfmas = [&](const bf16x8* fr, int nv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn) {
+                    if (tm >= nv) continue;
+                    const int ai = (m * C::TM + tm) * C::TN + tn;
+                    acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[C::TM + m * C::TN + tn], fr[tm], acc[ai], 0, 0, 0);
+                }
+    };
+
+    Tile cur;
+    setup(s, cur);
+    prologue(cur);
+    bf16x8 fa[C::NFR], fb[C::NFR];
+    int32_t claim = 0;  // lane 0 of wave 0: the claim counter's answer for the current tile
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < C::NACC; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+        // claim the block's next tile now; the answer is needed only after the k loop
+        if (tid == 0) claim = __hip_atomic_fetch_add(a.claim + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_stages(min(NS - 2, nk - 1));  // stage 0 landed
+        __builtin_amdgcn_s_barrier();
+        auto kloop = [&](auto NV) __attribute__((always_inline)) {
+            constexpr int nv = decltype(NV)::value;
+            read_frags(0, 0, fa, nv);
+            for (int kt = 0; kt < nk; ++kt) {
+                const int slot = kt % NS;
+                const int ls = kt + NS - 1;  // stage loaded during this one, into the slot freed by the last barrier
+                if (ls < nk) issue_a(cur, ls);
+                read_frags(slot, 1, fb, nv);
+                mfmas(fa, nv);
+                if (ls < nk) issue_b(cur, ls);
+                read_frags(slot, 2, fa, nv);
+                mfmas(fb, nv);
+                read_frags(slot, 3, fb, nv);
+                mfmas(fa, nv);
+                mfmas(fb, nv);
+                wait_stages(min(NS - 2, nk - 2 - kt));  // stage kt+1 landed
+                if (kt == nk - 1) {  // this wave's loads (and the claim) have landed
+                    if (tid == 0) next_tile = xcd * q + per + claim;
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the write is visible at the barrier
+                }
+                __builtin_amdgcn_s_barrier();
+                if (kt + 1 < nk) read_frags((kt + 1) % NS, 0, fa, nv);
+            }
+        };
+        // a ragged last row tile of a group leaves some waves' row blocks empty
+        const int nvb = __builtin_amdgcn_readfirstlane(min(max((cur.row_end - cur.row0 - wm * C::WM + 31) / 32, 0), C::TM));
+        if (nvb == C::TM) kloop(IntC<C::TM>{});
+        else if (nvb == 0) kloop(IntC<0>{});
+        else if (nvb == 1) kloop(IntC<1>{});
+        else if constexpr (C::TM > 2) {
+            if (nvb == 2) kloop(IntC<2>{});
+            else kloop(IntC<3>{});
+        }
+        // every slot is free: start the next tile's loads, then store this one
+        const int s_next = __builtin_amdgcn_readfirstlane(next_tile);
+        const bool more = s_next < s_end;
+        Tile nxt;
+        if (more) {
+            setup(s_next, nxt);
+            prologue(nxt);
+        }
+        if constexpr (MODE == MODE_SWIGLU) {
+#pragma clang loop unroll(full)
+            for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+                for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
+        } else if constexpr (MODE == MODE_GELU) {
+#pragma clang loop unroll(full)
+            for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+                for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
+        }
+        uint8_t* Cp = (uint8_t*)a.C;
+        const bool hi = lane >= 32;
+#pragma clang loop unroll(full)
+        for (int tm = 0; tm < C::TM; ++tm) {
+            const int row = cur.row0 + wm * C::WM + tm * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+            for (int tn = 0; tn < C::TN; ++tn) {
+                const floatx16& v = acc[tm * C::TN + tn];
+#pragma clang loop unroll(full)
+                for (int pp = 0; pp < 2; ++pp) {
+                    // groups 2pp (columns 16pp + 0..7) and 2pp+1 (16pp + 8..15)
+                    uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+                    uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                    const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
+                    const int col = cur.n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+                    if (row < cur.row_end && col < Nout)
+                        *(u32x4*)(Cp + ((size_t)row * Nout + col) * 2) = o;
+                }
+            }
+        }
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -606,7 +912,7 @@ static int max_m_tiles(int BM, int G, int max_rows) { return (max_rows + BM - 1)
 
 size_t ffn_workspace_bytes(int G, int max_rows, int dtype) {
     const int BM = pick_bm(dtype, G, max_rows);
-    return (size_t)(max_m_tiles(BM, G, max_rows) + 1) * sizeof(GemmTile);  // + header
+    return (size_t)(max_m_tiles(BM, G, max_rows) + 1 + kClaimSets) * sizeof(GemmTile);  // + header, counters
 }
 
 // one block per compute unit of the current device (a multiple of the 8 XCDs)
@@ -631,7 +937,18 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     const int blocks = g.per_xcd * 8;
     if (blocks == 0) return hipSuccess;
     const long long b_bytes = (long long)g.Nout * g.K * 2;
-    if (g.K % 32 == 0 && g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31)) {
+    const bool offsets_fit = g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
+    // plain products (down projection, W_o): 64-wide k stages with 16-byte row
+    // stores, when K is a multiple of 64 and every output row is 16-byte aligned
+    if constexpr (MODE == MODE_PLAIN) {
+        if (offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
+            using R = K64Cfg<BM, MODE>;
+            g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+            hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+            return hipGetLastError();
+        }
+    }
+    if (g.K % 32 == 0 && offsets_fit) {
         using R = Ring8Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
         hipLaunchKernelGGL((gemm_bf16_ring8_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
@@ -684,6 +1001,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.B1 = f.act == MOE_SWIGLU ? f.w_up : nullptr;
         g.C = f.h_tmp;
         g.tiles = f.tiles;
+        g.claim = (int32_t*)(f.tiles + mtiles + 1);
         g.m_tiles = mtiles;
         g.K = f.d;
         g.Nout = f.f;
@@ -698,6 +1016,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.B1 = nullptr;
         g.C = f.y_perm;
         g.tiles = f.tiles;
+        g.claim = (int32_t*)(f.tiles + mtiles + 1) + 8;
         g.m_tiles = mtiles;
         g.K = f.f;
         g.Nout = f.d;
@@ -727,6 +1046,7 @@ hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const 
     g.B0 = w;
     g.C = y;
     g.tiles = tiles;
+    g.claim = (int32_t*)(tiles + mtiles + 1);
     g.m_tiles = mtiles;
     g.K = k;
     g.Nout = n;
