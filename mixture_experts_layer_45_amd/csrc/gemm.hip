@@ -12,15 +12,15 @@
 //
 // Three bf16 kernels for gfx950 share the tile table, the XCD-aware schedule
 // and the fused epilogue (activation in fp32, one rounding to bf16):
-//   * gemm_bf16_k64_kernel  -- plain products (down projection, W_o) when K is a
-//     multiple of 64: persistent, 8 waves, BM x 256 tiles, 64-wide k stages of
-//     whole 128-byte rows, 16-byte row stores;
-//   * gemm_bf16_ring8_kernel -- gated products (SwiGLU gate/up, GELU) and plain
-//     ones with K % 64 != 0 but K % 32 == 0: persistent, 8 waves, a deeper ring
-//     of 32-wide k stages;
+//   * gemm_bf16_k64_kernel  -- when K is a multiple of 64: persistent, 8 waves,
+//     BM x 256 tiles, 64-wide k stages of whole 128-byte rows, 16-byte row
+//     stores;
+//   * gemm_bf16_ring8_kernel -- gated products on 256-row tiles with K >= 4096
+//     (where it measured a few percent ahead) and any K % 32 == 0 otherwise:
+//     persistent, 8 waves, a deeper ring of 32-wide k stages;
 //   * gemm_bf16_kernel -- any K (zero-filled tail), 4 waves, one tile per block.
-// On the top-2 8-expert shapes the ring kernel measured ahead on the gated
-// product (K = 4096) and the 64-wide kernel on the down projection (K = 14336).
+// Measured on one MI355X: the 64-wide kernel is 10-25 % faster on 128-row tiles
+// (256 experts x ~128 rows, d = 7168) and on short K (d = 512, f = 1024).
 #include "common.hpp"
 
 namespace moe {
@@ -940,13 +940,14 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     const bool offsets_fit = g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
     // plain products (down projection, W_o): 64-wide k stages with 16-byte row
     // stores, when K is a multiple of 64 and every output row is 16-byte aligned
-    if constexpr (MODE == MODE_PLAIN) {
-        if (offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
-            using R = K64Cfg<BM, MODE>;
-            g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
-            hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
-            return hipGetLastError();
-        }
+    // the 64-wide-stage kernel whenever K allows it, except for a gated product
+    // on 256-row tiles with a long K, where the ring kernel measured ahead
+    const bool ring_first = MODE != MODE_PLAIN && BM == 256 && g.K >= 4096;
+    if (!ring_first && offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
+        using R = K64Cfg<BM, MODE>;
+        g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+        return hipGetLastError();
     }
     if (g.K % 32 == 0 && offsets_fit) {
         using R = Ring8Cfg<BM, MODE>;
