@@ -75,6 +75,8 @@ struct PermuteArgs {
 int permute_chunks(int A);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
+// one row tile of a grouped GEMM: rows [row0, row_end) of group `group`
+// (group -1: an unused slot of the table)
 struct GemmTile {
     int32_t group, row0, row_end, pad;
 };
