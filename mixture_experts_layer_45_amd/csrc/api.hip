@@ -99,7 +99,7 @@ Plan plan_of(const moe_desc* d) {
     p.cap = capacity_of(d);
     const int64_t byc = p.cap >= INT32_MAX ? (int64_t)p.A : (int64_t)p.Et * p.cap;
     p.max_rows = (int)(byc < p.A ? byc : p.A);
-    p.route_nbx = (d->T + 15) / 16;
+    p.route_nbx = route_blocks(d->T, d->E, d->dtype);
     p.nch = permute_chunks(p.A);
     return p;
 }

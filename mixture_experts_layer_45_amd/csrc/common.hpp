@@ -51,7 +51,7 @@ struct RouteArgs {
     int32_t* counts;      // may be null
     float* prob_part;     // [n_blocks][H*E] partial sums of the score distribution, may be null
 };
-int route_blocks(int T, int H);  // number of route blocks (= rows of prob_part)
+int route_blocks(int T, int E, int dtype);  // route blocks per head (= rows of prob_part per head)
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_prob_mean(const float* prob_part, int n_blocks_per_head, int H, int E, int T,
                             float* prob_mean, hipStream_t st);

@@ -9,7 +9,9 @@
 // LatentMoE 与 Head 并行", "核心方法与创新"): head g routes slice g of the token
 // with its own router among its own experts.
 //
-// One block = 16 tokens of one head.  Phase 1: the four waves split the
+// Routers with at most 64 bf16 experts per head use route_small_kernel (below);
+// the others use route_kernel.  route_kernel: one block = 16 tokens of one
+// head.  Phase 1: the four waves split the
 // reduction over d, each running 16x16x32 bf16 MFMAs over its quarter; the
 // partial logit tiles are summed in LDS in wave order (fixed order, so the
 // logits are reproducible).  Phase 2: each wave takes four of the 16 tokens;
@@ -23,7 +25,12 @@ namespace moe {
 constexpr int RT_ROWS = 16;
 constexpr int RT_THREADS = 256;
 
-int route_blocks(int T, int H) { return ((T + RT_ROWS - 1) / RT_ROWS) * H; }
+// tokens per route block: 16, except for bf16 routers with 17..64 experts
+int route_rows(int E, int dtype) {
+    if (dtype != MOE_BF16 || E <= 16 || E > 64) return RT_ROWS;
+    return E <= 32 ? 2 * RT_ROWS : 4 * RT_ROWS;
+}
+int route_blocks(int T, int E, int dtype) { return (T + route_rows(E, dtype) - 1) / route_rows(E, dtype); }
 
 // Routing-key exp: a fixed sequence of fp32 operations (Cody and Waite's range
 // reduction with ln 2 split into a 16-bit head and an fp32 tail, the Taylor
@@ -111,19 +118,27 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         const int ks0 = wave * nks / 4, ks1 = (wave + 1) * nks / 4;
         const int kq = (lane >> 4) * 8;
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (int ks = ks0; ks < ks1; ++ks) {
-            const int k = ks * 32 + kq;
-            const bool kin = k < d;
-            const u32x4 av = kin ? *(const u32x4*)(xr + k) : zero;
-            u32x4 bv[NB];
+        // U k steps of loads are issued before their MFMAs, so a wave keeps
+        // U*(1+NB) 16-byte loads in flight instead of one step's worth
+        constexpr int U = NB <= 2 ? 8 : (NB <= 4 ? 4 : 2);
+        for (int kb = ks0; kb < ks1; kb += U) {
+            u32x4 av[U], bv[U][NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int e = j * 16 + (lane & 15);
-                bv[j] = (kin && e < E) ? *(const u32x4*)(wg + (size_t)e * d + k) : zero;
+            for (int u = 0; u < U; ++u) {
+                const int k = (kb + u) * 32 + kq;
+                const bool kin = kb + u < ks1 && k < d;
+                av[u] = kin ? *(const u32x4*)(xr + k) : zero;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int e = j * 16 + (lane & 15);
+                    bv[u][j] = (kin && e < E) ? *(const u32x4*)(wg + (size_t)e * d + k) : zero;
+                }
             }
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv[j]), acc[j], 0, 0, 0);
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][j]), acc[j], 0, 0, 0);
         }
         // 16x16 result: lane holds rows 4*(lane/16)+i of column lane%16
 #pragma unroll
@@ -286,6 +301,185 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     (void)Et;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 routers with at most 64 experts per head: RS = 16*R tokens of one head
+// per block (R = 1, 2, 4 for E <= 16, 32, 64, so that the router rows a block
+// reads stay small next to its token rows).  Phase 1 as above, the four waves
+// splitting the reduction over d, with R x NB MFMA tiles per wave and U k steps
+// of loads in flight.  Phase 2 gives each token one lane: the lane reads its
+// row of logits from LDS into registers and selects sequentially (key
+// descending, index ascending), with no cross-lane traffic; its full score
+// distribution goes to an LDS tile whose columns are summed in token order.
+template <int NB, int R, bool SIG>
+__global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
+    constexpr int RS = 16 * R;
+    constexpr int EP = NB * 16;
+    constexpr int LDE = EP + 1;
+    __shared__ float part[4][RS][LDE];  // per-wave partial logits; part[0] ends as the tile, part[1] holds P rows
+    __shared__ int hist[EP];
+
+    const int g = blockIdx.y;
+    const int t0 = blockIdx.x * RS;
+    const int T = a.T, H = a.H, E = a.E, K = a.K;
+    const int d = a.h / H;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < EP; i += RT_THREADS) hist[i] = 0;
+
+    if (a.flags & MOE_LOGITS_IN) {
+        for (int i = threadIdx.x; i < RS * E; i += RT_THREADS) {
+            const int r = i / E, e = i - r * E, t = t0 + r;
+            part[0][r][e] = t < T ? a.logits[((size_t)t * H + g) * E + e] : 0.0f;
+        }
+    } else {
+        floatx4 acc[R][NB];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[r][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* xr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(t0 + 16 * r + (lane & 15), T - 1);
+            xr[r] = (const uint16_t*)a.x + (size_t)row * a.h + (size_t)g * d;
+        }
+        const uint16_t* wg = (const uint16_t*)a.w_router + (size_t)g * E * d;
+        const int nks = (d + 31) / 32;
+        const int ks0 = wave * nks / 4, ks1 = (wave + 1) * nks / 4;
+        const int kq = (lane >> 4) * 8;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        constexpr int U = 16 / (R + NB) > 0 ? 16 / (R + NB) : 1;
+        for (int kb = ks0; kb < ks1; kb += U) {
+            u32x4 av[U][R], bv[U][NB];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = (kb + u) * 32 + kq;
+                const bool kin = kb + u < ks1 && k < d;
+#pragma unroll
+                for (int r = 0; r < R; ++r) av[u][r] = kin ? *(const u32x4*)(xr[r] + k) : zero;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int e = j * 16 + (lane & 15);
+                    bv[u][j] = (kin && e < E) ? *(const u32x4*)(wg + (size_t)e * d + k) : zero;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u][r]), as_bf16x8(bv[u][j]), acc[r][j], 0, 0, 0);
+        }
+        // 16x16 result: lane holds rows 4*(lane/16)+i of column lane%16
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part[wave][16 * r + (lane >> 4) * 4 + i][j * 16 + (lane & 15)] = acc[r][j][i];
+        __syncthreads();
+        for (int i = threadIdx.x; i < RS * EP; i += RT_THREADS) {
+            const int r = i / EP, e = i - r * EP;
+            float v = part[0][r][e];
+            v += part[1][r][e];
+            v += part[2][r][e];
+            v += part[3][r][e];
+            part[0][r][e] = v;
+        }
+    }
+    __syncthreads();
+    if (a.flags & MOE_LOGITS_OUT) {
+        for (int i = threadIdx.x; i < RS * E; i += RT_THREADS) {
+            const int r = i / E, e = i - r * E, t = t0 + r;
+            if (t < T) a.logits[((size_t)t * H + g) * E + e] = part[0][r][e];
+        }
+    }
+
+    // ------------------------------------------ selection: one lane per token
+    const float NEG = -__builtin_inff();
+    const int r = threadIdx.x;
+    const int t = t0 + r;
+    if (r < RS && t < T) {
+        const size_t sidx = (size_t)t * H + g;
+        // softmax router: key = biased logit; sigmoid router: key = sigma + bias,
+        // weights from sigma
+        float key[EP], sg[SIG ? EP : 1];
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            const bool valid = e < E;
+            float l = valid ? part[0][r][e] : NEG;
+            if (valid && a.logit_bias) l = l + a.logit_bias[g * E + e];
+            if constexpr (SIG) {
+                sg[e] = valid ? key_sigmoid(l) : 0.0f;
+                key[e] = valid ? (a.select_bias ? sg[e] + a.select_bias[g * E + e] : sg[e]) : NEG;
+            } else {
+                key[e] = l;
+            }
+        }
+        // two passes of K sequential arg-max rounds: the first sums the kept
+        // scores, the second writes the normalised weights
+        float den = 0.0f, vmax = 0.0f;
+        for (int pass = 0; pass < 2; ++pass) {
+            uint64_t used = 0;
+            for (int k = 0; k < K; ++k) {
+                float bk = NEG, bv = 0.0f;
+                int be = EP;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) {
+                    const bool free_e = e < E && !((used >> e) & 1ull);
+                    if (free_e && better(key[e], e, bk, be)) {
+                        bk = key[e];
+                        be = e;
+                        if constexpr (SIG) bv = sg[e];
+                        else bv = key[e];
+                    }
+                }
+                used |= 1ull << be;
+                if (k == 0) vmax = bv;  // the first kept has the largest biased logit
+                const float u = SIG ? bv : expf(bv - vmax);
+                if (pass == 0) {
+                    den += u;
+                } else {
+                    a.topk_idx[sidx * K + k] = g * E + be;
+                    a.topk_w[sidx * K + k] = u / den;
+                    atomicAdd(&hist[be], 1);
+                }
+            }
+        }
+        // full score distribution of this token, for P
+        if (a.prob_part) {
+            if constexpr (SIG) {
+                float tot = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) tot += sg[e];
+#pragma unroll
+                for (int e = 0; e < EP; ++e)
+                    if (e < E) part[1][r][e] = sg[e] / tot;
+            } else {
+                float m = NEG;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) m = fmaxf(m, key[e]);
+                float tot = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) tot += e < E ? expf(key[e] - m) : 0.0f;
+#pragma unroll
+                for (int e = 0; e < EP; ++e)
+                    if (e < E) part[1][r][e] = expf(key[e] - m) / tot;
+            }
+        }
+    }
+    __syncthreads();
+    const int rows = min(RS, T - t0);
+    for (int e = threadIdx.x; e < E; e += RT_THREADS) {
+        if (a.counts && hist[e]) atomicAdd(&a.counts[g * E + e], hist[e]);
+        if (a.prob_part) {
+            float v = 0.0f;
+            for (int q = 0; q < rows; ++q) v += part[1][q][e];
+            a.prob_part[((size_t)g * gridDim.x + blockIdx.x) * E + e] = v;
+        }
+    }
+}
+
 // P_e = (sum over the head's block partials) / T.  One block per expert: thread
 // i sums partials i, i+256, ... in order, then a fixed LDS tree; the order
 // depends only on the sizes, so P is reproducible.
@@ -314,7 +508,22 @@ static hipError_t launch_nb(const RouteArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int NB, int R>
+static hipError_t launch_small(const RouteArgs& a, hipStream_t st) {
+    dim3 grid((a.T + 16 * R - 1) / (16 * R), a.H);
+    if (a.score == MOE_SIGMOID)
+        hipLaunchKernelGGL((route_small_kernel<NB, R, true>), grid, dim3(RT_THREADS), 0, st, a);
+    else
+        hipLaunchKernelGGL((route_small_kernel<NB, R, false>), grid, dim3(RT_THREADS), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+    if (a.dtype == MOE_BF16 && a.E <= 64) {
+        if (a.E <= 16) return launch_small<1, 1>(a, st);
+        if (a.E <= 32) return launch_small<2, 2>(a, st);
+        return launch_small<4, 4>(a, st);
+    }
     if (a.E <= 16) return launch_nb<1>(a, st);
     if (a.E <= 32) return launch_nb<2>(a, st);
     if (a.E <= 64) return launch_nb<4>(a, st);
