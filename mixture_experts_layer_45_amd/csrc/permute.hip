@@ -9,16 +9,22 @@
 //
 // The assignment list (T*H*K expert ids, sub-token-major) is cut into chunks of
 // CHUNK ids, one wave per chunk:
-//   1. hist:    per-chunk expert counts (LDS integer atomics; exact).
+//   1. hist:    per-chunk expert counts (LDS integer atomics; exact):
+//               hist[chunk][e].
 //   2. scan:    per expert, the exclusive prefix over chunks (chunk order), the
 //               totals (counts), kept = min(counts, C) and offsets = exclusive
-//               prefix of kept.  One block; fixed order.
+//               prefix of kept.  One block; each expert's column of chunk
+//               counts is cut into segments, one thread each (consecutive lanes
+//               take consecutive experts, so every access is coalesced):
+//               segment sums, their prefix, then each segment rewritten in
+//               place.  Integer sums: exact.
 //   3. rank:    each chunk walks its ids 64 at a time in order; lanes holding
 //               the same expert find each other with ballots over the bits of
 //               the id, a lane's rank among them is the popcount of the lower
 //               lanes, and a per-expert running count in LDS carries the queue
 //               position across steps.  pos < C keeps the row at offsets[e]+pos.
-//   4. gather:  x_perm[row] = slice g of x[t] for each kept row, 16-byte copies.
+//   4. gather:  token-major: the slice of each sub-token is read once and
+//               copied to each of its kept rows (16-byte copies).
 // No step depends on the order in which blocks run, so the result is unique.
 #include "common.hpp"
 
@@ -29,7 +35,7 @@ constexpr int MAX_ET = 4096;      // experts the LDS tables hold
 
 int permute_chunks(int A) { return (A + CHUNK - 1) / CHUNK; }
 
-__global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int Et, int32_t* hist) {
+__global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int Et, int nch, int32_t* hist) {
     __shared__ int cnt[MAX_ET];
     for (int e = threadIdx.x; e < Et; e += 64) cnt[e] = 0;
     __syncthreads();
@@ -40,40 +46,68 @@ __global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int
         if ((unsigned)e < (unsigned)Et) atomicAdd(&cnt[e], 1);  // out-of-range ids are dropped
     }
     __syncthreads();
-    int32_t* out = hist + (size_t)blockIdx.x * Et;
-    for (int e = threadIdx.x; e < Et; e += 64) out[e] = cnt[e];
+    for (int e = threadIdx.x; e < Et; e += 64) hist[(size_t)blockIdx.x * Et + e] = cnt[e];
 }
 
 // One block of 1024 threads.  hist [nch][Et] is rewritten in place as the
-// per-chunk exclusive base of each expert.
+// per-chunk exclusive base of each expert.  S threads per expert (S a power of
+// two, S * Et <= 1024 when Et <= 1024), each owning a contiguous run of the
+// chunks; larger Et loop over experts with S = 1.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int Et, int capacity,
                                                     int32_t* counts, int32_t* kept, int32_t* offsets,
                                                     int32_t* n_kept) {
+    __shared__ int32_t seg[1024];
     __shared__ int32_t part[1024];
     const int tid = threadIdx.x;
-    // each thread owns experts [tid*per, tid*per + per)
+    int S = 1;
+    while (S * 2 * Et <= 1024 && S * 2 <= nch) S *= 2;
+    const int epp = 1024 / S;              // experts per pass
+    const int L = (nch + S - 1) / S;       // chunks per segment
+    const int el = tid % epp, sg = tid / epp;  // expert within the pass, segment
+    for (int e0 = 0; e0 < Et; e0 += epp) {
+        const int e = e0 + el;
+        const int c0 = min(sg * L, nch), c1 = min(c0 + L, nch);
+        int32_t* col = hist + e;  // chunk c of expert e at col[c * Et]
+        // segments are read 16 counts at a time, so 16 loads are in flight
+        constexpr int B = 16;
+        int32_t sum = 0;
+        if (e < Et)
+            for (int cb = c0; cb < c1; cb += B) {
+                int32_t v[B];
+#pragma unroll
+                for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? col[(size_t)(cb + j) * Et] : 0;
+#pragma unroll
+                for (int j = 0; j < B; ++j) sum += v[j];
+            }
+        seg[tid] = sum;
+        __syncthreads();
+        int32_t base = 0;  // chunks of this expert before the segment
+        for (int q = 0; q < sg; ++q) base += seg[q * epp + el];
+        if (e < Et) {
+            for (int cb = c0; cb < c1; cb += B) {
+                int32_t v[B];
+#pragma unroll
+                for (int j = 0; j < B; ++j) v[j] = cb + j < c1 ? col[(size_t)(cb + j) * Et] : 0;
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    if (cb + j < c1) col[(size_t)(cb + j) * Et] = base;
+                    base += v[j];
+                }
+            }
+            if (sg == S - 1) {
+                counts[e] = base;
+                kept[e] = base > capacity ? capacity : base;
+            }
+        }
+        __syncthreads();
+    }
+    // offsets: exclusive prefix of kept over experts (each thread owns a run)
     const int per = (Et + 1023) / 1024;
-    int32_t loc[4];
     int32_t run = 0;
     for (int q = 0; q < per; ++q) {
         const int e = tid * per + q;
-        int32_t total = 0;
-        if (e < Et) {
-            for (int c = 0; c < nch; ++c) {
-                const int32_t v = hist[(size_t)c * Et + e];
-                hist[(size_t)c * Et + e] = total;
-                total += v;
-            }
-            counts[e] = total;
-            const int32_t kp = total > capacity ? capacity : total;
-            kept[e] = kp;
-            loc[q] = kp;
-        } else {
-            loc[q] = 0;
-        }
-        run += loc[q];
+        if (e < Et) run += kept[e];
     }
-    // exclusive scan of the per-thread totals (Hillis-Steele over 1024 entries)
     part[tid] = run;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -82,11 +116,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int 
         part[tid] += v;
         __syncthreads();
     }
-    int32_t base = part[tid] - run;
+    int32_t b2 = part[tid] - run;
     for (int q = 0; q < per; ++q) {
         const int e = tid * per + q;
-        if (e < Et) offsets[e] = base;
-        base += loc[q];
+        if (e < Et) {
+            offsets[e] = b2;
+            b2 += kept[e];
+        }
     }
     if (tid == 1023) {
         offsets[Et] = part[1023];
@@ -101,9 +137,8 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int
     __shared__ int32_t run[MAX_ET];
     __shared__ int32_t off[MAX_ET];
     const int lane = threadIdx.x;
-    const int32_t* b = base + (size_t)blockIdx.x * Et;
     for (int e = lane; e < Et; e += 64) {
-        run[e] = b[e];
+        run[e] = base[(size_t)blockIdx.x * Et + e];
         off[e] = offsets[e];
     }
     __syncthreads();
@@ -142,30 +177,36 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int
     }
 }
 
-// x_perm[row][:] = x[t][g*d : g*d+d] with s = src_token[row] = t*H + g.
-// `tpr` threads per row copy 16 bytes each per iteration.
-__global__ __launch_bounds__(256) void gather_kernel(const void* x, int h, int H, int rowbytes,
-                                                     const int32_t* src_token, const int32_t* n_rows_p,
-                                                     int tpr, int max_rows, void* x_perm) {
-    const int n_rows = *n_rows_p;
-    const int rpb = 256 / tpr;
-    const int row = blockIdx.x * rpb + threadIdx.x / tpr;
-    const int c = threadIdx.x % tpr;
-    if (row >= n_rows || row >= max_rows) return;
-    const int s = src_token[row];
+// Token-major copy: sub-token s = t*H + g reads its slice x[t][g*d : g*d+d]
+// once and stores it to x_perm[dest_row[s*K + k]] for each kept slot k.
+// `tps` threads per sub-token (a power of two, at most 256) copy 16 bytes each
+// per step; 256/tps sub-tokens per block.
+__global__ __launch_bounds__(256) void gather_kernel(const void* x, int H, int rowbytes, int K, int S,
+                                                     const int32_t* dest_row, int tps, int max_rows, void* x_perm) {
+    const int spb = 256 / tps;
+    const int s = blockIdx.x * spb + threadIdx.x / tps;
+    const int c = threadIdx.x % tps;
+    if (s >= S) return;
     const int t = s / H, g = s - t * H;
     const char* src = (const char*)x + (size_t)t * (size_t)(rowbytes * H) + (size_t)g * rowbytes;
-    char* dst = (char*)x_perm + (size_t)row * rowbytes;
-    for (int o = c * 16; o < rowbytes; o += tpr * 16)
-        *(uint4*)(dst + o) = *(const uint4*)(src + o);
-    (void)h;
+    const int32_t* dr = dest_row + (size_t)s * K;
+    bool any = false;  // a sub-token whose every slot was dropped is not read at all
+    for (int k = 0; k < K; ++k) any |= dr[k] >= 0;
+    if (!any) return;
+    for (int o = c * 16; o < rowbytes; o += tps * 16) {
+        const uint4 v = *(const uint4*)(src + o);
+        for (int k = 0; k < K; ++k) {
+            const int row = dr[k];
+            if (row >= 0 && row < max_rows) *(uint4*)((char*)x_perm + (size_t)row * rowbytes + o) = v;
+        }
+    }
 }
 
 hipError_t launch_permute(const PermuteArgs& p, hipStream_t st) {
     const int nch = permute_chunks(p.A);
     hipError_t err;
     if (nch > 0) {
-        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.Et, p.hist);
+        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.Et, nch, p.hist);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, p.hist, nch, p.Et, p.capacity, p.counts,
@@ -180,15 +221,13 @@ hipError_t launch_permute(const PermuteArgs& p, hipStream_t st) {
     if (p.x && p.x_perm && p.max_rows > 0) {
         const int esz = p.dtype == MOE_BF16 ? 2 : 4;
         const int rowbytes = p.d * esz;
-        int tpr = rowbytes / 16;
-        if (tpr > 256) tpr = 256;
-        int pow2 = 1;
-        while (pow2 * 2 <= tpr) pow2 *= 2;
-        tpr = pow2;
-        const int rpb = 256 / tpr;
-        const int blocks = (p.max_rows + rpb - 1) / rpb;
-        hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, st, p.x, p.h, p.H, rowbytes, p.src_token,
-                           p.offsets + p.Et, tpr, p.max_rows, p.x_perm);
+        int tps = 1;
+        while (tps < 256 && tps * 16 < rowbytes) tps *= 2;
+        const int S = p.A / p.K;  // sub-tokens
+        const int spb = 256 / tps;
+        const int blocks = (S + spb - 1) / spb;
+        hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, st, p.x, p.H, rowbytes, p.K, S, p.dest_row, tps,
+                           p.max_rows, p.x_perm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
