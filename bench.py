@@ -256,8 +256,8 @@ def main():
         total_flops += 2.0 * (n_act + 1) * T * h * f
 
     roofline = {
-        "kernel": "gemm_bf16_kernel (grouped gate/up GEMM + SwiGLU)" if n_act == 2 else
-                  "gemm_bf16_kernel (grouped GEMM + GELU)",
+        "kernel": "grouped GEMM1: gate/up projections + SwiGLU" if n_act == 2 else
+                  "grouped GEMM1: projection + GELU",
         "bound": "mfma", "achieved": g1_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
         "frac": g1_tfs / MFMA_BF16_PEAK_TFS, "traffic": traffic_from_profile("gemm1", name),
         "flops_per_launch": gemm1_flops, "launch_ms": t_g1,
@@ -283,9 +283,9 @@ def main():
             t0 = time.perf_counter()
             orc.layer_forward(cfg, host, host["x"][:Ts], T=Ts)
             elapsed = time.perf_counter() - t0
-            if elapsed >= args.cpu_seconds / 4 or Ts >= T:
+            if elapsed >= args.cpu_seconds * 0.6 or Ts >= T:
                 break
-            Ts = min(T, max(Ts * 2, int(Ts * args.cpu_seconds / max(elapsed, 1e-3) / 2)))
+            Ts = min(T, Ts * 4, max(Ts + 1, int(Ts * args.cpu_seconds / max(elapsed, 1e-3))))
         log(f"[bench] oracle: {Ts} tokens in {elapsed:.2f} s on {threads} threads")
         cpu = {"value": Ts / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"first {Ts} tokens of the {name} batch as their own batch (capacity for {Ts} "
