@@ -94,6 +94,8 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
     if (tid < 4 * kClaimSets) ((int32_t*)(tiles + max_tiles + 1))[tid] = 0;
 }
 
+constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together
+
 struct GArgs {
     const void* A;   // [rows][K]
     const void* B0;  // [G][Nout][K]
@@ -103,9 +105,35 @@ struct GArgs {
     int m_tiles, n_tiles, K, Nout, total, per_xcd;
     long long a_bytes;  // bytes of A the tiles may address (buffer bound of the 8-wave kernel)
     int32_t* claim;     // 8 zeroed tile-claim counters for this launch (persistent kernels)
+    float* partial;     // fp32 partial tiles of the split last round (64-wide kernel), or null
 };
 
-constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together
+// The last round of an XCD's slice is usually short (r < B tiles for B blocks):
+// the 64-wide kernel then splits each of those r tiles into S pieces along K,
+// one block each, that store fp32 partial tiles; a follow-up kernel adds each
+// tile's pieces in piece order and runs the epilogue.  S <= B / r, at most
+// kTailSlots pieces per XCD and at least kMinPieceStages k stages per piece.
+constexpr int kTailSlots = 32;
+constexpr int kMinPieceStages = 4;
+__device__ __forceinline__ void tail_split(int Tx, int B, int nk, bool enabled, int& r, int& S) {
+    r = B > 0 ? Tx % B : 0;
+    S = 1;
+    if (enabled && r > 0) {
+        S = min(min(B / r, kTailSlots / r), nk / kMinPieceStages);
+        if (S < 2) S = 1;
+    }
+}
+// schedule index -> (row tile, column tile): groups of NGROUP column tiles,
+// each sweeping every real row tile
+__device__ __forceinline__ void sched_decode(int si, int n_m, int n_tiles, int& mt, int& nt) {
+    const int gsz = n_m * NGROUP;
+    const int nb = si / gsz;
+    const int rem = si - nb * gsz;
+    const int width = min(NGROUP, n_tiles - nb * NGROUP);
+    mt = rem / width;
+    nt = nb * NGROUP + (rem - mt * width);
+}
+
 
 // block -> (m tile, n tile): blocks are dealt to the 8 XCDs round-robin, so block
 // b runs on XCD b % 8; give each XCD a contiguous range of the schedule, and order
@@ -626,6 +654,60 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Epilogue of a 64-wide-stage tile: activation in fp32, one rounding to bf16,
+// then (lane l holding row l%32 and, per group q of four, columns 8q + 4*(l/32)
+// + 0..3) one v_permlane32_swap per register pair so that every lane stores 8
+// consecutive outputs (16 bytes).
+template <int BM, int MODE>
+__device__ __forceinline__ void k64_epilogue(floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
+                                             int wm, int wn, int lane) {
+    using C = K64Cfg<BM, MODE>;
+    if constexpr (MODE == MODE_SWIGLU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
+    } else if constexpr (MODE == MODE_GELU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
+    }
+    const bool hi = lane >= 32;
+#pragma clang loop unroll(full)
+    for (int tm = 0; tm < C::TM; ++tm) {
+        const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const floatx16& v = acc[tm * C::TN + tn];
+#pragma clang loop unroll(full)
+            for (int pp = 0; pp < 2; ++pp) {
+                // groups 2pp (columns 16pp + 0..7) and 2pp+1 (16pp + 8..15)
+                uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+                uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
+                const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+                if (row < row_end && col < Nout) *(u32x4*)(Cp + ((size_t)row * Nout + col) * 2) = o;
+            }
+        }
+    }
+}
+
+// fp32 partial tile of one piece: register (ai, 4q..4q+3) of thread tid at
+// float4 index (ai*4 + q)*512 + tid of the slot (coalesced 16-byte stores)
+template <int BM, int MODE>
+__device__ __forceinline__ void k64_store_partial(const floatx16* acc, float* partial, int slot, int tid) {
+    using C = K64Cfg<BM, MODE>;
+    floatx4* P = (floatx4*)partial + (size_t)slot * (C::NACC * 4 * 512);
+#pragma clang loop unroll(full)
+    for (int ai = 0; ai < C::NACC; ++ai)
+#pragma clang loop unroll(full)
+        for (int q = 0; q < 4; ++q)
+            P[(ai * 4 + q) * 512 + tid] = floatx4{acc[ai][4 * q], acc[ai][4 * q + 1], acc[ai][4 * q + 2], acc[ai][4 * q + 3]};
+}
+
 template <int BM, int MODE>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -637,17 +719,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE + 16];
     int32_t& next_tile = *(int32_t*)(smem + NS * C::STAGE);
 
+    const int K = a.K, Nout = a.Nout;
+    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int nk = K / 64;
     const int n_m = a.tiles[a.m_tiles].group;  // real row tiles (header of the table)
     const int total = n_m * a.n_tiles;
     const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
     const int q = (total + 7) / 8;
-    const int s_end = min((xcd + 1) * q, total);
-    int s = xcd * q + (blockIdx.x >> 3);
+    const int tx0 = xcd * q;                     // this XCD's slice of the schedule
+    const int Tx = max(0, min(q, total - tx0));
+    int r_tail, S;
+    tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
+    const int n_whole = S > 1 ? Tx - r_tail : Tx;  // items: whole tiles, then S pieces of each tail tile
+    const int s_end = n_whole + (S > 1 ? r_tail * S : 0);
+    int s = blockIdx.x >> 3;  // first item static, later ones claimed
     if (s >= s_end) return;
-
-    const int K = a.K, Nout = a.Nout;
-    const uint32_t rowbytes = (uint32_t)K * 2u;
-    const int nk = K / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
@@ -657,25 +743,29 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     const uint8_t* Ab = (const uint8_t*)a.A;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
 
-    auto decode = [&](int si, int& mt, int& nt) __attribute__((always_inline)) {
-        const int gsz = n_m * NGROUP;
-        const int nb = si / gsz;
-        const int rem = si - nb * gsz;
-        const int width = min(NGROUP, a.n_tiles - nb * NGROUP);
-        mt = rem / width;
-        nt = nb * NGROUP + (rem - mt * width);
-    };
     struct Tile {
         int row0, row_end, n0;
+        int kb, nkl, slot;  // first k stage, k stages, partial slot (-1: a whole tile)
         __amdgpu_buffer_rsrc_t rB;
         uint32_t va[C::A_PW], vb[C::B_PW];
     };
     // per-lane byte offsets: lane l fills LDS chunk l%8 of row l/8 of its 8-row
     // run, so it fetches the logical chunk stored there; load i carries
     // immediate offset 1024*i, which is taken off here
-    auto setup = [&](int si, Tile& t) __attribute__((always_inline)) {
+    auto setup = [&](int item, Tile& t) __attribute__((always_inline)) {
+        int si = tx0 + item;
+        t.kb = 0;
+        t.nkl = nk;
+        t.slot = -1;
+        if (item >= n_whole) {  // piece p of tail tile jt
+            const int j = item - n_whole, jt = j / S, p = j - jt * S;
+            si = tx0 + n_whole + jt;
+            t.kb = p * nk / S;
+            t.nkl = (p + 1) * nk / S - t.kb;
+            t.slot = xcd * kTailSlots + j;
+        }
         int mt, nt;
-        decode(si, mt, nt);
+        sched_decode(si, n_m, a.n_tiles, mt, nt);
         const GemmTile tl = a.tiles[mt];
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
@@ -700,16 +790,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
     };
+    // stage ks of the tile's k range
     auto issue_a = [&](const Tile& t, int ks) __attribute__((always_inline)) {
-        LdsRun<C::A_PW>::go(rA, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + a_dst), t.va, ks * 128);
+        LdsRun<C::A_PW>::go(rA, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + a_dst), t.va, (t.kb + ks) * 128);
     };
     auto issue_b = [&](const Tile& t, int ks) __attribute__((always_inline)) {
-        LdsRun<C::B_PW>::go(t.rB, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + b_dst), t.vb, ks * 128);
+        LdsRun<C::B_PW>::go(t.rB, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + b_dst), t.vb, (t.kb + ks) * 128);
     };
     auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < NS - 1; ++st)
-            if (st < nk) {
+            if (st < t.nkl) {
                 issue_a(t, st);
                 issue_b(t, st);
             }
@@ -760,30 +851,31 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
         // claim the block's next tile now; the answer is needed only after the k loop
         if (tid == 0) claim = __hip_atomic_fetch_add(a.claim + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait_stages(min(NS - 2, nk - 1));  // stage 0 landed
+        const int nkl = cur.nkl;
+        wait_stages(min(NS - 2, nkl - 1));  // stage 0 landed
         __builtin_amdgcn_s_barrier();
         auto kloop = [&](auto NV) __attribute__((always_inline)) {
             constexpr int nv = decltype(NV)::value;
             read_frags(0, 0, fa, nv);
-            for (int kt = 0; kt < nk; ++kt) {
+            for (int kt = 0; kt < nkl; ++kt) {
                 const int slot = kt % NS;
                 const int ls = kt + NS - 1;  // stage loaded during this one, into the slot freed by the last barrier
-                if (ls < nk) issue_a(cur, ls);
+                if (ls < nkl) issue_a(cur, ls);
                 read_frags(slot, 1, fb, nv);
                 mfmas(fa, nv);
-                if (ls < nk) issue_b(cur, ls);
+                if (ls < nkl) issue_b(cur, ls);
                 read_frags(slot, 2, fa, nv);
                 mfmas(fb, nv);
                 read_frags(slot, 3, fb, nv);
                 mfmas(fa, nv);
                 mfmas(fb, nv);
-                wait_stages(min(NS - 2, nk - 2 - kt));  // stage kt+1 landed
-                if (kt == nk - 1) {  // this wave's loads (and the claim) have landed
-                    if (tid == 0) next_tile = xcd * q + per + claim;
+                wait_stages(min(NS - 2, nkl - 2 - kt));  // stage kt+1 landed
+                if (kt == nkl - 1) {  // this wave's loads (and the claim) have landed
+                    if (tid == 0) next_tile = per + claim;
                     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the write is visible at the barrier
                 }
                 __builtin_amdgcn_s_barrier();
-                if (kt + 1 < nk) read_frags((kt + 1) % NS, 0, fa, nv);
+                if (kt + 1 < nkl) read_frags((kt + 1) % NS, 0, fa, nv);
             }
         };
         // a ragged last row tile of a group leaves some waves' row blocks empty
@@ -803,39 +895,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             setup(s_next, nxt);
             prologue(nxt);
         }
-        if constexpr (MODE == MODE_SWIGLU) {
-#pragma clang loop unroll(full)
-            for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-                for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
-        } else if constexpr (MODE == MODE_GELU) {
-#pragma clang loop unroll(full)
-            for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-                for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
-        }
-        uint8_t* Cp = (uint8_t*)a.C;
-        const bool hi = lane >= 32;
-#pragma clang loop unroll(full)
-        for (int tm = 0; tm < C::TM; ++tm) {
-            const int row = cur.row0 + wm * C::WM + tm * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-            for (int tn = 0; tn < C::TN; ++tn) {
-                const floatx16& v = acc[tm * C::TN + tn];
-#pragma clang loop unroll(full)
-                for (int pp = 0; pp < 2; ++pp) {
-                    // groups 2pp (columns 16pp + 0..7) and 2pp+1 (16pp + 8..15)
-                    uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
-                    uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-                    const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
-                    const int col = cur.n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
-                    if (row < cur.row_end && col < Nout)
-                        *(u32x4*)(Cp + ((size_t)row * Nout + col) * 2) = o;
-                }
-            }
-        }
+        if (cur.slot >= 0)
+            k64_store_partial<BM, MODE>(acc, a.partial, cur.slot, tid);
+        else
+            k64_epilogue<BM, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -843,6 +906,46 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     wait_vmcnt<0>();
 #endif
 }
+
+// Sums the pieces of each split tail tile (in piece order) and runs the
+// epilogue.  One block per (XCD, tail tile); `per` = blocks per XCD of the GEMM
+// launch, so the split is recomputed exactly as that launch made it.
+template <int BM, int MODE>
+__global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
+    using C = K64Cfg<BM, MODE>;
+    const int xcd = blockIdx.x / kTailSlots, jt = blockIdx.x % kTailSlots;
+    const int nk = a.K / 64;
+    const int n_m = a.tiles[a.m_tiles].group;
+    const int total = n_m * a.n_tiles;
+    const int q = (total + 7) / 8;
+    const int tx0 = xcd * q;
+    const int Tx = max(0, min(q, total - tx0));
+    int r_tail, S;
+    tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
+    if (S < 2 || jt >= r_tail) return;
+    int mt, nt;
+    sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, mt, nt);
+    const GemmTile tl = a.tiles[mt];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    floatx16 acc[C::NACC];
+#pragma unroll
+    for (int i = 0; i < C::NACC; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+    for (int p = 0; p < S; ++p) {
+        const floatx4* P = (const floatx4*)a.partial + (size_t)(xcd * kTailSlots + jt * S + p) * (C::NACC * 4 * 512);
+#pragma unroll
+        for (int ai = 0; ai < C::NACC; ++ai)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const floatx4 v = P[(ai * 4 + q4) * 512 + tid];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[ai][4 * q4 + i] += v[i];
+            }
+    }
+    k64_epilogue<BM, MODE>(acc, tl.row0, tl.row_end, nt * C::BNM, a.Nout, (uint8_t*)a.C, wave >> 2, wave & 3, lane);
+}
+
 
 // ------------------------------------------------------------- fp32 VALU
 // 64 x 64 output tile per matrix, BK = 16, 256 threads each computing 4x4.
@@ -910,9 +1013,22 @@ static int pick_bm(int dtype, int G, int max_rows) {
 }
 static int max_m_tiles(int BM, int G, int max_rows) { return (max_rows + BM - 1) / BM + G; }
 
+// FFN workspace: the tile table, its header and the claim counters, then (bf16)
+// the fp32 partial tiles of split tail tiles: 8 XCDs x kTailSlots slots of one
+// BM x 256 fp32 tile (256 KB for BM = 256)
+static size_t table_bytes(int BM, int G, int max_rows) {
+    const size_t b = (size_t)(max_m_tiles(BM, G, max_rows) + 1 + kClaimSets) * sizeof(GemmTile);
+    return (b + 255) & ~(size_t)255;
+}
+static size_t partial_bytes(int BM, int dtype) {
+    return dtype == MOE_BF16 ? (size_t)8 * kTailSlots * BM * 256 * sizeof(float) : 0;
+}
+static float* partial_of(GemmTile* tiles, int BM, int G, int max_rows, int dtype) {
+    return dtype == MOE_BF16 ? (float*)((char*)tiles + table_bytes(BM, G, max_rows)) : nullptr;
+}
 size_t ffn_workspace_bytes(int G, int max_rows, int dtype) {
     const int BM = pick_bm(dtype, G, max_rows);
-    return (size_t)(max_m_tiles(BM, G, max_rows) + 1 + kClaimSets) * sizeof(GemmTile);  // + header, counters
+    return table_bytes(BM, G, max_rows) + partial_bytes(BM, dtype);
 }
 
 // one block per compute unit of the current device (a multiple of the 8 XCDs)
@@ -946,7 +1062,11 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     if (!ring_first && offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
         using R = K64Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
-        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+        const int pb = persistent_blocks();
+        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(pb), dim3(512), 0, st, g);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess || !g.partial) return err;
+        hipLaunchKernelGGL((gemm_k64_tail_kernel<BM, MODE>), dim3(8 * kTailSlots), dim3(512), 0, st, g, pb / 8);
         return hipGetLastError();
     }
     if (g.K % 32 == 0 && offsets_fit) {
@@ -1003,6 +1123,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.C = f.h_tmp;
         g.tiles = f.tiles;
         g.claim = (int32_t*)(f.tiles + mtiles + 1);
+        g.partial = partial_of(f.tiles, BM, f.G, f.max_rows, f.dtype);
         g.m_tiles = mtiles;
         g.K = f.d;
         g.Nout = f.f;
@@ -1018,6 +1139,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.C = f.y_perm;
         g.tiles = f.tiles;
         g.claim = (int32_t*)(f.tiles + mtiles + 1) + 8;
+        g.partial = partial_of(f.tiles, BM, f.G, f.max_rows, f.dtype);
         g.m_tiles = mtiles;
         g.K = f.f;
         g.Nout = f.d;
@@ -1048,6 +1170,7 @@ hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const 
     g.C = y;
     g.tiles = tiles;
     g.claim = (int32_t*)(tiles + mtiles + 1);
+    g.partial = partial_of(tiles, BM, 1, rows, dtype);
     g.m_tiles = mtiles;
     g.K = k;
     g.Nout = n;

@@ -156,12 +156,34 @@ def _synthetic_groups(G_, n_rows_target, rng, empty_every=5, big_group=True):
 def test_grouped_ffn(name):
     cfg = inputs.variant(name, **SMALL[name])
     H, E = cfg.get("H", 1), cfg["E"]
-    Gn, dd, f = H * E, cfg["h"] // H, cfg["f"]
     rng = np.random.default_rng(1)
-    counts = _synthetic_groups(Gn, 900, rng)
+    counts = _synthetic_groups(H * E, 900, rng)
+    _check_grouped_ffn(cfg, counts, name)
+
+
+# Shapes whose last round of tiles is split along K into pieces (fp32 partial
+# tiles summed by a second kernel): only tail tiles (2 groups), and whole tiles
+# followed by a split tail (4 groups of ~1280 rows); gated and GELU FFNs.
+SPLIT_CASES = {
+    "tail_only_swiglu": ("top2_e8_h4096", dict(E=2, K=1, h=1024, f=1024), [310, 290]),
+    "tail_only_gelu": ("switch_top1_e64_zipf", dict(E=2, K=1, h=1024, f=1024), [301, 299]),
+    "whole_and_tail_swiglu": ("top2_e8_h4096", dict(E=4, K=1, h=1024, f=2048), [1300, 1250, 1290, 1280]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLIT_CASES))
+def test_grouped_ffn_split_tail(case):
+    name, over, counts = SPLIT_CASES[case]
+    cfg = inputs.variant(name, T=sum(counts), capacity_factor=0.0, **over)
+    _check_grouped_ffn(cfg, np.array(counts, dtype=np.int32), case)
+
+
+def _check_grouped_ffn(cfg, counts, label):
+    H, E = cfg.get("H", 1), cfg["E"]
+    Gn, dd, f = H * E, cfg["h"] // H, cfg["f"]
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     N = int(offsets[-1])
-    G.log(f"[grouped ffn] {name} groups={Gn} rows={N} d={dd} f={f}")
+    G.log(f"[grouped ffn] {label} groups={Gn} rows={N} d={dd} f={f}")
     inp = inputs.make_inputs(cfg, "cpu")
     dt = inputs.torch_dtype(cfg)
     xp = torch.randn((N, dd), generator=torch.Generator().manual_seed(5)).to(dt)
@@ -187,7 +209,7 @@ def test_grouped_ffn(name):
             continue
         ref[a:b], mag[a:b] = orc.expert_ffn(cfg, dd, wg[e], None if wu is None else wu[e], wd[e], xin[a:b],
                                             with_mag=True)
-    st = G.assert_close(got[:N], ref, cfg["dtype"], f"y_perm {name}", mag=mag, mag_unit=2.0 ** -9)
+    st = G.assert_close(got[:N], ref, cfg["dtype"], f"y_perm {label}", mag=mag, mag_unit=2.0 ** -9)
     G.log(f"   {st}")
     # rows past the last group are untouched
     assert np.all(got[N:] == 7.0)
