@@ -397,6 +397,52 @@ struct LdsRun<0> {
     static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t, lds_void_ptr, const uint32_t*, int) {}
 };
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Epilogue of the persistent kernels (weight fragment as the MFMA's first
+// operand): activation in fp32, one rounding to bf16, then (lane l holding row
+// l%32 and, per group q of four, columns 8q + 4*(l/32) + 0..3) one
+// v_permlane32_swap per register pair so that every lane stores 8 consecutive
+// outputs (16 bytes).  C gives the wave tile (TM x TN 32x32 tiles, WM rows,
+// WNM columns per matrix).
+template <typename C, int MODE>
+__device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
+                                                  int wm, int wn, int lane) {
+    if constexpr (MODE == MODE_SWIGLU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
+    } else if constexpr (MODE == MODE_GELU) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t)
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
+    }
+    const bool hi = lane >= 32;
+#pragma clang loop unroll(full)
+    for (int tm = 0; tm < C::TM; ++tm) {
+        const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const floatx16& v = acc[tm * C::TN + tn];
+#pragma clang loop unroll(full)
+            for (int pp = 0; pp < 2; ++pp) {
+                // groups 2pp (columns 16pp + 0..7) and 2pp+1 (16pp + 8..15)
+                uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+                uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
+                const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+                if (row < row_end && col < Nout) *(u32x4*)(Cp + ((size_t)row * Nout + col) * 2) = o;
+            }
+        }
+    }
+}
+
 // Persistent form: one block per CU.  XCD x (blocks b with b % 8 == x) takes a
 // contiguous slice of the tile schedule: its blocks start on the slice's first
 // tiles and then claim the next unclaimed one from the XCD's counter (claimed at
@@ -404,9 +450,9 @@ struct LdsRun<0> {
 // running at once on an XCD stay neighbours in the schedule (groups of NGROUP
 // weight-column tiles sweeping one expert's row tiles) and share their rows in
 // that XCD's L2, and a block that drew short tiles (the ragged last row tile
-// of an expert) simply takes more of them.  When a tile's k loop ends, every LDS slot is free:
-// the first stages of the block's next tile are loaded before the current
-// tile's epilogue, which hides their latency.
+// of an expert) simply takes more of them.  When a tile's k loop ends, every
+// LDS slot is free: the first stages of the block's next tile are loaded before
+// the current tile's epilogue, which hides their latency.
 template <int BM, int MODE>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     // device pass only: the LDS address-space casts and the buffer-to-LDS loads
@@ -529,7 +575,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
                 for (int tn = 0; tn < C::TN; ++tn) {
                     if (tm >= nv) continue;
                     const int ai = (m * C::TM + tm) * C::TN + tn;
-                    acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[m * C::TN + tn], acc[ai], 0, 0, 0);
+                    acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[m * C::TN + tn], af[tm], acc[ai], 0, 0, 0);
                 }
     };
 
@@ -581,31 +627,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
             setup(s_next, nxt);
             prologue(nxt);
         }
-        const int row0 = cur.row0, row_end = cur.row_end, n0 = cur.n0;
-        if constexpr (MODE == MODE_SWIGLU) {
-#pragma clang loop unroll(full)
-            for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-                for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
-        } else if constexpr (MODE == MODE_GELU) {
-#pragma clang loop unroll(full)
-            for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-                for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
-        }
-        uint16_t* Cp = (uint16_t*)a.C;
-#pragma clang loop unroll(full)
-        for (int tm = 0; tm < C::TM; ++tm)
-#pragma clang loop unroll(full)
-            for (int tn = 0; tn < C::TN; ++tn) {
-                const int col = n0 + wn * C::WNM + tn * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-                for (int i = 0; i < 16; ++i) {
-                    const int row = row0 + wm * C::WM + tm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                    if (row < row_end && col < Nout)
-                        Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
-                }
-            }
+        rowstore_epilogue<C, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -650,50 +672,6 @@ struct K64Cfg {
 
 __device__ __forceinline__ int swz64(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
-
-// Epilogue of a 64-wide-stage tile: activation in fp32, one rounding to bf16,
-// then (lane l holding row l%32 and, per group q of four, columns 8q + 4*(l/32)
-// + 0..3) one v_permlane32_swap per register pair so that every lane stores 8
-// consecutive outputs (16 bytes).
-template <int BM, int MODE>
-__device__ __forceinline__ void k64_epilogue(floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
-                                             int wm, int wn, int lane) {
-    using C = K64Cfg<BM, MODE>;
-    if constexpr (MODE == MODE_SWIGLU) {
-#pragma clang loop unroll(full)
-        for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
-    } else if constexpr (MODE == MODE_GELU) {
-#pragma clang loop unroll(full)
-        for (int t = 0; t < C::TM * C::TN; ++t)
-#pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) acc[t][i] = act_gelu(acc[t][i]);
-    }
-    const bool hi = lane >= 32;
-#pragma clang loop unroll(full)
-    for (int tm = 0; tm < C::TM; ++tm) {
-        const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-        for (int tn = 0; tn < C::TN; ++tn) {
-            const floatx16& v = acc[tm * C::TN + tn];
-#pragma clang loop unroll(full)
-            for (int pp = 0; pp < 2; ++pp) {
-                // groups 2pp (columns 16pp + 0..7) and 2pp+1 (16pp + 8..15)
-                uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
-                uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
-                const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-                const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-                const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
-                const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
-                if (row < row_end && col < Nout) *(u32x4*)(Cp + ((size_t)row * Nout + col) * 2) = o;
-            }
-        }
-    }
-}
 
 // fp32 partial tile of one piece: register (ai, 4q..4q+3) of thread tid at
 // float4 index (ai*4 + q)*512 + tid of the slot (coalesced 16-byte stores)
@@ -898,7 +876,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         if (cur.slot >= 0)
             k64_store_partial<BM, MODE>(acc, a.partial, cur.slot, tid);
         else
-            k64_epilogue<BM, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane);
+            rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -943,7 +921,7 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
                 for (int i = 0; i < 4; ++i) acc[ai][4 * q4 + i] += v[i];
             }
     }
-    k64_epilogue<BM, MODE>(acc, tl.row0, tl.row_end, nt * C::BNM, a.Nout, (uint8_t*)a.C, wave >> 2, wave & 3, lane);
+    rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, tl.row0, tl.row_end, nt * C::BNM, a.Nout, (uint8_t*)a.C, wave >> 2, wave & 3, lane);
 }
 
 
@@ -1069,7 +1047,7 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
         hipLaunchKernelGGL((gemm_k64_tail_kernel<BM, MODE>), dim3(8 * kTailSlots), dim3(512), 0, st, g, pb / 8);
         return hipGetLastError();
     }
-    if (g.K % 32 == 0 && offsets_fit) {
+    if (g.K % 32 == 0 && offsets_fit && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
         using R = Ring8Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
         hipLaunchKernelGGL((gemm_bf16_ring8_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
