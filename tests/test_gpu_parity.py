@@ -70,9 +70,31 @@ def route_gpu(cfg, logits=None, x=None, w_router=None, biases=None, T=None, want
 
 
 # ------------------------------------------------------------------ routing
-@pytest.mark.parametrize("name", WORKLOADS)
+# the workloads, plus routers that reach other kernel paths: sigmoid scoring
+# with few experts, expert counts that are not multiples of 16, several heads,
+# a logit bias, and more than 64 experts
+ROUTE_VARIANTS = {
+    "sigmoid_e16_k4": ("sigmoid_top8_e256_shared", dict(E=16, K=4, T=1500)),
+    "sigmoid_e20_k3": ("sigmoid_top8_e256_shared", dict(E=20, K=3, T=999)),
+    "sigmoid_e48_k6": ("sigmoid_top8_e256_shared", dict(E=48, K=6, T=2000)),
+    "sigmoid_e96_k8": ("sigmoid_top8_e256_shared", dict(E=96, K=8, T=700)),
+    "softmax_e20_k3": ("top2_e8_h4096", dict(E=20, K=3, T=1001)),
+    "heads2_e24_k5": ("multihead_h8_e32_top4", dict(H=2, E=24, K=5, T=777)),
+    "zipf_e40_k2": ("switch_top1_e64_zipf", dict(E=40, K=2, T=1234)),
+}
+ROUTE_CASES = WORKLOADS + sorted(ROUTE_VARIANTS)
+
+
+def _route_cfg(case, **extra):
+    if case in ROUTE_VARIANTS:
+        base, over = ROUTE_VARIANTS[case]
+        return inputs.variant(base, **dict(over, **extra))
+    return inputs.variant(case, **extra) if extra else inputs.CONFIGS[case]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
 def test_route_shared_logits_bit_exact(name):
-    cfg = inputs.CONFIGS[name]
+    cfg = _route_cfg(name)
     G.log(f"[route shared-logits] {name} T={cfg['T']}")
     lg = inputs.make_logits(cfg, "cpu", tie_every=5)
     b = inputs.make_biases(cfg, "cpu")
@@ -87,11 +109,11 @@ def test_route_shared_logits_bit_exact(name):
     assert np.allclose(g["P"], P_ref, rtol=1e-4, atol=1e-7)
 
 
-@pytest.mark.parametrize("name", WORKLOADS)
+@pytest.mark.parametrize("name", ROUTE_CASES)
 def test_route_logits_gemm(name):
     """Router GEMM at full width on a ragged token count: logits within fp32
     accumulation error, indices exact wherever the oracle margin is >= 1e-3."""
-    cfg = inputs.variant(name, T=500)
+    cfg = _route_cfg(name, T=500)
     G.log(f"[route gemm] {name} T=500 h={cfg['h']}")
     inp = inputs.make_inputs(dict(cfg, f=8), "cpu")  # f is irrelevant here; keep the weights small
     dv = {k: (None if v is None else v.to(G.DEV)) for k, v in inp.items()}
