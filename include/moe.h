@@ -173,6 +173,19 @@ moe_status moe_grouped_ffn(const moe_desc *desc, const void *x_perm, const int32
                            const void *w_down, void *h_tmp, void *y_perm, uint32_t flags,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* The same grouped FFN with the row gather fused into the gate/up GEMM's
+ * loads (lesson 10, item 3: the packed rows are only read by the expert
+ * GEMM, so they are fetched from x where they lie).  Row i of the first GEMM
+ * is row src_token[i] of x viewed as [T*H][d] (sub-token s = t*H + g is
+ * x[t][g*d : g*d+d]), i.e. exactly the row moe_permute would have copied to
+ * x_perm[i]; no x_perm is read or written.  src_token as produced by
+ * moe_permute; values outside [0, T*H) are clamped to that range (never read
+ * out of bounds).  Everything else as in moe_grouped_ffn; same workspace. */
+moe_status moe_grouped_ffn_rows(const moe_desc *desc, const void *x, const int32_t *src_token,
+                                const int32_t *offsets, int32_t max_rows, const void *w_gate,
+                                const void *w_up, const void *w_down, void *h_tmp, void *y_perm,
+                                uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 /* Gate-weighted unpermute and combine (lesson 10, item 1 output formula and
  * item 3 weighted sum): y[t][g*d + j] = sum over k with dest_row >= 0, in slot
  * order, of topk_w[s][k] * y_perm[dest_row[s][k]][j] (fp32), plus

@@ -17,7 +17,7 @@ from ._ffi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FFN_GEMM1, MOE_FFN_GEMM2, M
 
 __all__ = [
     "MoeError", "MoeDesc", "desc_from_cfg", "moe_capacity", "moe_workspace_size", "moe_route",
-    "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_version", "lib",
+    "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_rows", "moe_combine", "moe_layer_forward", "moe_version", "lib",
     "workspace",
 ]
 
@@ -114,6 +114,14 @@ def moe_grouped_ffn(desc, x_perm, offsets, max_rows, w_gate, w_up, w_down, h_tmp
     _check(lib().moe_grouped_ffn(C.byref(desc), _ptr(x_perm), _ptr(offsets), int(max_rows), _ptr(w_gate),
                                  _ptr(w_up), _ptr(w_down), _ptr(h_tmp), _ptr(y_perm), int(flags), wp, wn,
                                  _stream(stream)))
+
+
+def moe_grouped_ffn_rows(desc, x, src_token, offsets, max_rows, w_gate, w_up, w_down, h_tmp, y_perm, flags=0,
+                         ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().moe_grouped_ffn_rows(C.byref(desc), _ptr(x), _ptr(src_token), _ptr(offsets), int(max_rows),
+                                      _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h_tmp), _ptr(y_perm), int(flags),
+                                      wp, wn, _stream(stream)))
 
 
 def moe_combine(desc, dest_row, topk_w, y_perm, y_shared, y, stream=None):

@@ -56,6 +56,8 @@ SIGNATURES = {
                               _VP, C.c_size_t, _VP]),
     "moe_grouped_ffn": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP,
                                   C.c_uint32, _VP, C.c_size_t, _VP]),
+    "moe_grouped_ffn_rows": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                       C.c_uint32, _VP, C.c_size_t, _VP]),
     "moe_combine": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_layer_forward": (C.c_int, [C.POINTER(MoeDesc), C.POINTER(MoeWeights), _VP, _VP,
                                     C.POINTER(MoeAux), _VP, C.c_size_t, _VP]),

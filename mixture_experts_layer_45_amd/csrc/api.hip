@@ -119,7 +119,7 @@ struct LayerWs {
     int32_t *topk_idx, *counts, *kept, *offsets, *dest_row, *src_token, *hist, *off_sh, *off_wo;
     float *topk_w, *prob_part, *prob_mean;
     GemmTile *tiles, *tiles_sh, *tiles_wo;
-    void *x_perm, *h_tmp, *y_perm, *h_sh, *y_sh, *y_cat;
+    void *h_tmp, *y_perm, *h_sh, *y_sh, *y_cat;
 };
 
 LayerWs carve_layer(Carver& c, const Plan& p, const moe_desc* d) {
@@ -135,7 +135,6 @@ LayerWs carve_layer(Carver& c, const Plan& p, const moe_desc* d) {
     w.dest_row = c.take<int32_t>((size_t)p.A + 1);
     w.src_token = c.take<int32_t>((size_t)p.A + 1);
     w.tiles = carve_ffn(c, p, d->dtype);
-    w.x_perm = c.take<char>((size_t)p.max_rows * p.d * p.esz + 16);
     w.h_tmp = c.take<char>((size_t)p.max_rows * p.f * p.esz + 16);
     w.y_perm = c.take<char>((size_t)p.max_rows * p.d * p.esz + 16);
     if (d->n_shared) {
@@ -268,9 +267,10 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, const void* x
     return MOE_OK;
 }
 
-moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets, int32_t max_rows,
-                           const void* w_gate, const void* w_up, const void* w_down, void* h_tmp,
-                           void* y_perm, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+static moe_status grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* src_rows,
+                              const int32_t* offsets, int32_t max_rows, const void* w_gate, const void* w_up,
+                              const void* w_down, void* h_tmp, void* y_perm, uint32_t flags, void* ws,
+                              size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     moe_status s = check_desc(d);
     if (s != MOE_OK) return s;
@@ -294,9 +294,29 @@ moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t*
     a.G = p.Et; a.d = p.d; a.f = p.f; a.dtype = d->dtype; a.act = d->act; a.max_rows = max_rows;
     a.x_perm = x_perm; a.offsets = offsets; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
     a.h_tmp = h_tmp; a.y_perm = y_perm; a.flags = fl; a.tiles = carve_ffn(c, q, d->dtype);
+    a.src_rows = src_rows; a.a_nrows = p.T * p.H;
     hipError_t e = launch_ffn(a, (hipStream_t)stream);
     if (e != hipSuccess) return dev_fail(e, "grouped ffn kernels");
     return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* offsets, int32_t max_rows,
+                           const void* w_gate, const void* w_up, const void* w_down, void* h_tmp,
+                           void* y_perm, uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+    return grouped_ffn(d, x_perm, nullptr, offsets, max_rows, w_gate, w_up, w_down, h_tmp, y_perm, flags, ws,
+                       ws_bytes, stream);
+}
+
+moe_status moe_grouped_ffn_rows(const moe_desc* d, const void* x, const int32_t* src_token,
+                                const int32_t* offsets, int32_t max_rows, const void* w_gate, const void* w_up,
+                                const void* w_down, void* h_tmp, void* y_perm, uint32_t flags, void* ws,
+                                size_t ws_bytes, void* stream) {
+    if (!src_token && max_rows > 0 && (!flags || (flags & MOE_FFN_GEMM1))) {
+        g_err[0] = 0;
+        return fail(MOE_ERR_INVALID_ARG, "src_token is NULL");
+    }
+    return grouped_ffn(d, x, src_token, offsets, max_rows, w_gate, w_up, w_down, h_tmp, y_perm, flags, ws,
+                       ws_bytes, stream);
 }
 
 moe_status moe_combine(const moe_desc* d, const int32_t* dest_row, const float* topk_w, const void* y_perm,
@@ -355,13 +375,15 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
     PermuteArgs pa{};
     pa.A = p.A; pa.K = p.K; pa.H = p.H; pa.Et = p.Et; pa.d = p.d; pa.h = p.h; pa.dtype = d->dtype;
     pa.capacity = (int)p.cap; pa.topk_idx = topk_idx; pa.x = x; pa.counts = counts; pa.kept = L.kept;
-    pa.offsets = L.offsets; pa.dest_row = dest_row; pa.src_token = L.src_token; pa.x_perm = L.x_perm;
-    pa.n_kept = nullptr; pa.hist = L.hist; pa.max_rows = p.max_rows;
+    // no row gather: the gate/up GEMM reads its rows of x through src_token
+    pa.offsets = L.offsets; pa.dest_row = dest_row; pa.src_token = L.src_token; pa.x = nullptr;
+    pa.x_perm = nullptr; pa.n_kept = nullptr; pa.hist = L.hist; pa.max_rows = p.max_rows;
     if ((e = launch_permute(pa, st)) != hipSuccess) return dev_fail(e, "permute kernels");
 
     FfnArgs fa{};
     fa.G = p.Et; fa.d = p.d; fa.f = p.f; fa.dtype = d->dtype; fa.act = d->act; fa.max_rows = p.max_rows;
-    fa.x_perm = L.x_perm; fa.offsets = L.offsets; fa.w_gate = w->w_gate; fa.w_up = w->w_up;
+    fa.x_perm = x; fa.src_rows = L.src_token; fa.a_nrows = p.T * p.H;
+    fa.offsets = L.offsets; fa.w_gate = w->w_gate; fa.w_up = w->w_up;
     fa.w_down = w->w_down; fa.h_tmp = L.h_tmp; fa.y_perm = L.y_perm; fa.flags = 0; fa.tiles = L.tiles;
     if ((e = launch_ffn(fa, st)) != hipSuccess) return dev_fail(e, "grouped ffn kernels");
 

@@ -85,7 +85,9 @@ struct FfnArgs {
     int d, f;       // in/out width of the layer and hidden width
     int dtype, act;
     int max_rows;
-    const void* x_perm;
+    const void* x_perm;         // GEMM1 activations: rows [max_rows][d], or x [a_nrows][d] with src_rows
+    const int32_t* src_rows;    // null, or row i of GEMM1 reads row src_rows[i] of x_perm
+    int a_nrows;                // rows behind x_perm when src_rows is given
     const int32_t* offsets;
     const void* w_gate;
     const void* w_up;

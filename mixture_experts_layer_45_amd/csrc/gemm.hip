@@ -106,7 +106,14 @@ struct GArgs {
     long long a_bytes;  // bytes of A the tiles may address (buffer bound of the 8-wave kernel)
     int32_t* claim;     // 8 zeroed tile-claim counters for this launch (persistent kernels)
     float* partial;     // fp32 partial tiles of the split last round (64-wide kernel), or null
+    const int32_t* a_rows;  // row map: tile row i reads row a_rows[i] of A (null: row i)
 };
+
+// the A row behind tile row r, clamped to the nrows rows of A
+__device__ __forceinline__ int a_row(const GArgs& a, int r, int nrows) {
+    if (!a.a_rows) return r;
+    return min(max(a.a_rows[r], 0), nrows - 1);
+}
 
 // The last round of an XCD's slice is usually short (r < B tiles for B blocks):
 // the 64-wide kernel then splits each of those r tiles into S pieces along K,
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GArgs a) {
     const uint16_t* pa[BM / 32];
 #pragma unroll
     for (int p = 0; p < BM / 32; ++p) {
-        const int r = min(row0 + lrow + 32 * p, row_end - 1);
+        const int r = a_row(a, min(row0 + lrow + 32 * p, row_end - 1), (int)(a.a_bytes / ((long long)K * 2)));
         pa[p] = Ab + (size_t)r * K + lch * 8;
     }
     const uint16_t* pb[8];
@@ -486,6 +493,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     const int b_dst = C::A_BYTES + w4 * 64 * 64;
     const uint8_t* Ab = (const uint8_t*)a.A;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
+    const int a_nrows = (int)(a.a_bytes / rowbytes);
 
     // schedule index -> (row tile, column tile): groups of NGROUP column tiles,
     // each sweeping every real row tile
@@ -519,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
         for (int i = 0; i < C::A_LOADS; ++i) {
             const int r = w4 * (BM / 4) + 16 * i + lr;
             const int c = pc ^ ((r >> 1) & 3);
-            const int gr = min(t.row0 + r, t.row_end - 1);
+            const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
             t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
 #pragma unroll
@@ -720,6 +728,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     const int b_dst = C::A_BYTES + wu * 32 * 128;
     const uint8_t* Ab = (const uint8_t*)a.A;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
+    const int a_nrows = (int)(a.a_bytes / rowbytes);
 
     struct Tile {
         int row0, row_end, n0;
@@ -756,7 +765,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         for (int i = 0; i < C::A_PW; ++i) {
             const int r = wu * (BM / 8) + 8 * i + lr;
             const int c = pc ^ ((r >> 1) & 7);
-            const int gr = min(t.row0 + r, t.row_end - 1);
+            const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
             t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
 #pragma unroll
@@ -948,7 +957,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GArgs a) {
     for (int k0 = 0; k0 < K; k0 += FBK) {
         for (int i = tid; i < FBM * FBK; i += 256) {
             const int r = i / FBK, k = i % FBK;
-            const int gr = min(tl.row0 + r, tl.row_end - 1);
+            const int gr = a_row(a, min(tl.row0 + r, tl.row_end - 1), (int)(a.a_bytes / ((long long)K * 4)));
             As[k][r] = k0 + k < K ? A[(size_t)gr * K + k0 + k] : 0.0f;
         }
         for (int m = 0; m < NMAT; ++m)
@@ -1105,7 +1114,9 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.m_tiles = mtiles;
         g.K = f.d;
         g.Nout = f.f;
-        g.a_bytes = (long long)f.max_rows * f.d * 2;
+        const int esz = f.dtype == MOE_BF16 ? 2 : 4;
+        g.a_bytes = f.src_rows ? (long long)f.a_nrows * f.d * esz : (long long)f.max_rows * f.d * esz;
+        g.a_rows = f.src_rows;
         err = run_gemm(f.dtype, BM, f.act == MOE_SWIGLU ? MODE_SWIGLU : MODE_GELU, g, st);
         if (err != hipSuccess) return err;
     }
@@ -1121,7 +1132,7 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.m_tiles = mtiles;
         g.K = f.f;
         g.Nout = f.d;
-        g.a_bytes = (long long)f.max_rows * f.f * 2;
+        g.a_bytes = (long long)f.max_rows * f.f * (f.dtype == MOE_BF16 ? 2 : 4);
         err = run_gemm(f.dtype, BM, MODE_PLAIN, g, st);
         if (err != hipSuccess) return err;
     }
@@ -1152,7 +1163,7 @@ hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const 
     g.m_tiles = mtiles;
     g.K = k;
     g.Nout = n;
-    g.a_bytes = (long long)rows * k * 2;
+    g.a_bytes = (long long)rows * k * (dtype == MOE_BF16 ? 2 : 4);
     return run_gemm(dtype, BM, MODE_PLAIN, g, st);
 }
 

@@ -91,6 +91,8 @@ def test_stage_calls_validate_before_launch():
     assert L.moe_route(C.byref(d), None, None, None, None, None, 3, None, None, None, None, None, 0, None) == 1
     assert L.moe_permute(C.byref(d), None, None, -1, None, None, None, None, None, None, None, None, 0, None) == 1
     assert L.moe_grouped_ffn(C.byref(d), None, None, 10**9, None, None, None, None, None, 0, None, 0, None) == 1
+    assert L.moe_grouped_ffn_rows(C.byref(d), None, None, None, 10**9, None, None, None, None, None, 0, None, 0,
+                                  None) == 1
     assert L.moe_combine(C.byref(d), None, None, None, None, None, None) == 1
     W = _ffi.MoeWeights()
     assert L.moe_layer_forward(C.byref(d), C.byref(W), None, None, None, None, 0, None) == 1
@@ -115,7 +117,8 @@ def test_workspace_sizes_cover_stages():
         lay = moe.moe_workspace_size(d, _ffi.MOE_WS_LAYER)
         for k in (_ffi.MOE_WS_ROUTE, _ffi.MOE_WS_PERMUTE, _ffi.MOE_WS_FFN):
             assert 0 < moe.moe_workspace_size(d, k) <= lay, (name, k)
-    # the whole-layer workspace of the 8-expert top-2 workload holds x_perm, h and y_perm
+    # the whole-layer workspace of the 8-expert top-2 workload holds h and y_perm
+    # (the layer reads its packed rows straight from x, so it keeps no x_perm)
     d = moe.desc_from_cfg(inputs.CONFIGS["top2_e8_h4096"])
     rows = 16384
-    assert moe.moe_workspace_size(d) >= rows * (4096 + 14336 + 4096) * 2
+    assert moe.moe_workspace_size(d) >= rows * (14336 + 4096) * 2

@@ -237,6 +237,77 @@ def _check_grouped_ffn(cfg, counts, label):
     assert np.all(got[N:] == 7.0)
 
 
+# ------------------------------------------- grouped FFN reading rows of x
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_grouped_ffn_rows_matches_packed(name):
+    """The gather fused into the first GEMM's loads gives bit-for-bit the output
+    of the same FFN run on the packed x_perm (real routing of the workload)."""
+    cfg = inputs.variant(name, **SMALL[name])
+    T, H, K, E = cfg["T"], cfg.get("H", 1), cfg["K"], cfg["E"]
+    dd, f = cfg["h"] // H, cfg["f"]
+    G.log(f"[grouped ffn rows] {name}")
+    inp = inputs.make_inputs(cfg, "cpu")
+    dv = {k: (None if v is None else v.to(G.DEV)) for k, v in inp.items()}
+    d = moe.desc_from_cfg(cfg)
+    A, Et = T * H * K, H * E
+    idx = inputs.make_routing(cfg, "cpu", skew=0.7).to(G.DEV)
+    C = orc.capacity(cfg)
+    counts, kept, offsets, dest, src, nk = i32(Et), i32(Et), i32(Et + 1), i32(A), i32(A), i32(1)
+    dt = inputs.torch_dtype(cfg)
+    x_perm = torch.empty((A, dd), dtype=dt, device=G.DEV)
+    moe.moe_permute(d, idx, dv["x"], moe.INT32_MAX if C is None else C, counts, kept, offsets, dest, src, x_perm,
+                    nk, moe.workspace(d, moe.MOE_WS_PERMUTE))
+    ws = moe.workspace(d, moe.MOE_WS_FFN)
+    outs = []
+    for fused in (False, True):
+        h_tmp = torch.zeros((A, f), dtype=dt, device=G.DEV)
+        y_perm = torch.zeros((A, dd), dtype=dt, device=G.DEV)
+        if fused:
+            moe.moe_grouped_ffn_rows(d, dv["x"], src, offsets, A, dv["w_gate"], dv["w_up"], dv["w_down"], h_tmp,
+                                     y_perm, 0, ws)
+        else:
+            moe.moe_grouped_ffn(d, x_perm, offsets, A, dv["w_gate"], dv["w_up"], dv["w_down"], h_tmp, y_perm, 0, ws)
+        torch.cuda.synchronize()
+        outs.append((h_tmp, y_perm))
+    n = int(nk.item())
+    iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(outs[0][0][:n].view(iv), outs[1][0][:n].view(iv))
+    assert torch.equal(outs[0][1][:n].view(iv), outs[1][1][:n].view(iv))
+
+
+def test_grouped_ffn_rows_clamps_row_indices():
+    """Row indices outside [0, T*H) read the nearest valid row, never out of bounds."""
+    cfg = inputs.variant("top2_e8_h4096", **SMALL["top2_e8_h4096"])
+    T, K, E, dd, f = cfg["T"], cfg["K"], cfg["E"], cfg["h"], cfg["f"]
+    inp = inputs.make_inputs(cfg, "cpu")
+    dv = {k: (None if v is None else v.to(G.DEV)) for k, v in inp.items()}
+    d = moe.desc_from_cfg(cfg)
+    A = T * K
+    counts = np.full(E, A // E, dtype=np.int32)
+    counts[-1] += A - counts.sum()
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(G.DEV)
+    rng = np.random.default_rng(3)
+    src = rng.integers(0, T, size=A).astype(np.int32)
+    src[::7] = -5
+    src[3::11] = 10 ** 9
+    srcd = torch.from_numpy(src).to(G.DEV)
+    x_perm = dv["x"][torch.from_numpy(np.clip(src, 0, T - 1)).long().to(G.DEV)].contiguous()
+    ws = moe.workspace(d, moe.MOE_WS_FFN)
+    dt = inputs.torch_dtype(cfg)
+    outs = []
+    for fused in (False, True):
+        h_tmp = torch.zeros((A, f), dtype=dt, device=G.DEV)
+        y_perm = torch.zeros((A, dd), dtype=dt, device=G.DEV)
+        if fused:
+            moe.moe_grouped_ffn_rows(d, dv["x"], srcd, offsets, A, dv["w_gate"], dv["w_up"], dv["w_down"], h_tmp,
+                                     y_perm, 0, ws)
+        else:
+            moe.moe_grouped_ffn(d, x_perm, offsets, A, dv["w_gate"], dv["w_up"], dv["w_down"], h_tmp, y_perm, 0, ws)
+        torch.cuda.synchronize()
+        outs.append(y_perm)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
 # ------------------------------------------------------------------ combine
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_combine(name):
