@@ -160,7 +160,14 @@ def main():
     def permute():
         moe.moe_permute(desc, topk_idx, inp["x"], cap, counts, keptb, offsets, dest_row, src, x_perm, None, ws_p)
 
-    def gemm1():
+    def permute_tables():  # what the layer runs: routing tables only, no row gather
+        moe.moe_permute(desc, topk_idx, None, cap, counts, keptb, offsets, dest_row, src, None, None, ws_p)
+
+    def gemm1():  # the layer's gate/up GEMM: rows read from x through src_token
+        moe.moe_grouped_ffn_rows(desc, inp["x"], src, offsets, max_rows, inp["w_gate"], inp["w_up"],
+                                 inp["w_down"], h_tmp, y_perm, moe.MOE_FFN_GEMM1, ws_f)
+
+    def gemm1_packed():  # the stage-wise path: the same GEMM on the gathered x_perm
         moe.moe_grouped_ffn(desc, x_perm, offsets, max_rows, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
                             y_perm, moe.MOE_FFN_GEMM1, ws_f)
 
@@ -198,9 +205,9 @@ def main():
     permute()
     if args.counters:
         torch.cuda.synchronize()
-        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+        cp_src = torch.ones(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
+        cp_dst = torch.empty_like(cp_src)
+        cp_dst.copy_(cp_src)
         torch.cuda.synchronize()
         for _ in range(3):
             gemm1()
@@ -213,6 +220,9 @@ def main():
         shared_fn()
     t_route = timed(route, R, stream)
     t_perm = timed(permute, R, stream)
+    t_tables = timed(permute_tables, R, stream)
+    permute()  # leave x_perm and the tables in place for the packed GEMM
+    t_g1_packed = timed(gemm1_packed, R, stream)
     t_g1 = timed(gemm1, R, stream)
     t_g2 = timed(gemm2, R, stream)
     t_comb = timed(combine, R, stream)
@@ -237,7 +247,9 @@ def main():
     stages = {
         "route_ms": t_route, "route_hbm_frac": frac(route_bytes / (t_route * 1e-3) / 1e9, HBM_PEAK_GBS),
         "permute_ms": t_perm, "permute_hbm_frac": frac(permute_bytes / (t_perm * 1e-3) / 1e9, HBM_PEAK_GBS),
+        "permute_tables_ms": t_tables,
         "gemm1_ms": t_g1, "gemm1_tflops": g1_tfs, "gemm1_mfma_frac": g1_tfs / MFMA_BF16_PEAK_TFS,
+        "gemm1_packed_ms": t_g1_packed,
         "gemm2_ms": t_g2, "gemm2_tflops": g2_tfs, "gemm2_mfma_frac": g2_tfs / MFMA_BF16_PEAK_TFS,
         "combine_ms": t_comb,
         "combine_hbm_frac": combine_bytes / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -245,7 +257,7 @@ def main():
         "shared_ffn_tflops": None if t_sh is None else 2.0 * (n_act + 1) * T * h * f / (t_sh * 1e-3) / 1e12,
         "w_o_ms": t_wo,
         "w_o_tflops": None if t_wo is None else 2.0 * T * h * h / (t_wo * 1e-3) / 1e12,
-        "sum_of_stages_ms": t_route + t_perm + t_g1 + t_g2 + t_comb + (t_sh or 0.0) + (t_wo or 0.0),
+        "sum_of_stages_ms": t_route + t_tables + t_g1 + t_g2 + t_comb + (t_sh or 0.0) + (t_wo or 0.0),
         "ffn_mfma_frac": (gemm1_flops + gemm2_flops) / ((t_g1 + t_g2) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "ffn_weight_bytes": w_bytes,
     }
