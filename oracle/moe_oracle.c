@@ -25,7 +25,12 @@
  *         FFN, top-K per token, capacity factor and token dropping) and item 4
  *         (aux loss, DeepSeek's bias-based balancing, capacity and drop/pad).
  *  [MH]   "Multi-Head LatentMoE 与 Head 并行" (ai-stack.site), "核心方法与创新":
- *         the token vector is split into heads and each head routes on its own.
+ *         the token vector is split into heads and each head routes on its own;
+ *         "3. 理论基础": an expert may be chosen by a hash or a fixed map of the
+ *         input's index instead of a learned gate.
+ *  [HAI] also lists a HashGate (top-1 only) and a (train, val) pair of
+ *         capacity factors; [L10] item 5 (node-limited routing): the K experts
+ *         of a token may lie in at most M nodes.
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes): ties in the routing key go to the lower expert index; C is
@@ -34,7 +39,16 @@
  * the capacity queue of an expert is first-come by (sub-)token index; a dropped
  * assignment contributes zero and the remaining weights are not renormalised;
  * f_i = counts_i / (T K) counted before drops; P_i averages the full score
- * distribution over all T tokens; SwiGLU = (silu(x Wg^T) * (x Wu^T)) Wd^T and
+ * distribution over all T tokens; group-limited routing splits a head's E
+ * experts into n_groups contiguous groups (the expert-to-node map of [L10]'s
+ * worked exercise), scores a group by the largest key in it, keeps the
+ * group_limit best groups (ties to the lower group index) and takes the top-K
+ * among their experts; the hash gate sends sub-token s = t H + g to expert
+ * fmix32(key_t H + g) mod E of its head with weight 1 (fmix32 is the 32-bit
+ * finaliser of Appleby's MurmurHash3; key_t is a caller-given integer per
+ * token, by default t) and has no scores, so P and L_aux are 0; the
+ * choice-major queue ranks all first choices of an expert (by sub-token)
+ * before any second choice; SwiGLU = (silu(x Wg^T) * (x Wu^T)) Wd^T and
  * GELU uses the exact erf form; no biases; the multi-head layer routes the
  * contiguous d = h/H slice of each token with its own router and its own E
  * experts, concatenates the head outputs and applies W_o.
@@ -65,6 +79,12 @@ typedef struct {
     int32_t act;   /* 0 = SwiGLU, 1 = GELU */
     float capacity_factor; /* <= 0 : no capacity limit */
     float alpha;
+    int32_t gate;        /* 0 = top-K of router scores, 1 = hash gate (K = 1) */
+    int32_t n_groups;    /* > 1: group-limited top-K over this many groups per head */
+    int32_t group_limit; /* groups a sub-token may choose from */
+    int32_t queue;       /* 0 = capacity queue by sub-token, 1 = by choice, then sub-token */
+    float capacity_factor_eval; /* capacity factor in evaluation mode */
+    int32_t eval;        /* 1: use capacity_factor_eval */
 } orc_desc;
 
 typedef struct {
@@ -74,6 +94,7 @@ typedef struct {
     const void *w_gate, *w_up, *w_down;
     const void *sh_gate, *sh_up, *sh_down; /* shared expert or NULL */
     const void *w_o;                       /* [h][h] or NULL */
+    const int32_t *hash_keys;              /* [T] keys of the hash gate or NULL (key = t) */
 } orc_weights;
 
 /* Optional outputs of orc_layer_forward; any pointer may be NULL. */
@@ -163,8 +184,10 @@ float orc_sigmoid_key(float l, float b)
  * T sub-tokens).  Returns -1 for "no limit" (CF <= 0).                       */
 int64_t orc_capacity(const orc_desc *d)
 {
-    if (d->capacity_factor <= 0.0f) return -1;
-    double v = (double)d->capacity_factor * (double)d->K * (double)d->T / (double)d->E;
+    /* [HAI]: the capacity factor is a (train, val) pair; eval selects the second */
+    float cf = d->eval ? d->capacity_factor_eval : d->capacity_factor;
+    if (cf <= 0.0f) return -1;
+    double v = (double)cf * (double)d->K * (double)d->T / (double)d->E;
     double r = nearbyint(v);
     double tol = 1e-6 * (v > 1.0 ? v : 1.0);
     if (fabs(v - r) <= tol) return (int64_t)r;
@@ -196,7 +219,10 @@ void orc_logits(const orc_desc *d, const void *x, const void *w_router, float *l
  * For every sub-token: the biased logit l' = l + logit_bias (one fp32 add),
  * the routing key (l' for softmax, sigma(l') + select_bias for sigmoid), the K
  * experts with the largest keys (ties to the lower index), listed by key
- * descending; the gate weights over the selected set ([L10] item 1):
+ * descending (with n_groups > 1, only experts of the group_limit groups with
+ * the largest group scores are candidates, and the margin is the smaller of
+ * the expert margin and the gap between the last kept and the best dropped
+ * group score); the gate weights over the selected set ([L10] item 1):
  *   softmax: w_k = exp(l'_k) / sum_{j in S} exp(l'_j)
  *   sigmoid: w_k = sigma(l'_k) / sum_{j in S} sigma(l'_j)   (unbiased sigma)
  * with sigma in exact double here; the margin key_(K) - key_(K+1) (+inf when
@@ -241,6 +267,34 @@ void orc_select(const orc_desc *d, const float *logits, const float *logit_bias,
         /* selection by repeated arg-max under the (key desc, index asc) order */
         int32_t chosen[4096];
         unsigned char *used = (unsigned char *)calloc((size_t)E, 1);
+        /* group limit ([L10] item 5): score each group by its largest key,
+         * keep the group_limit best groups (larger score first, lower group
+         * index on ties) and take no expert outside them */
+        double gmargin = INFINITY;
+        if (d->n_groups > 1) {
+            const int32_t G = d->n_groups, gs = E / G;
+            float gscore[4096];
+            unsigned char gkeep[4096];
+            for (int32_t q = 0; q < G; ++q) {
+                gscore[q] = ks[q * gs];
+                for (int32_t j = 1; j < gs; ++j)
+                    if (ks[q * gs + j] > gscore[q]) gscore[q] = ks[q * gs + j];
+                gkeep[q] = 0;
+            }
+            int32_t last = -1;
+            for (int32_t m = 0; m < d->group_limit; ++m) {
+                int32_t bq = -1;
+                for (int32_t q = 0; q < G; ++q)
+                    if (!gkeep[q] && (bq < 0 || gscore[q] > gscore[bq])) bq = q;
+                gkeep[bq] = 1;
+                last = bq;
+            }
+            int32_t nq = -1;
+            for (int32_t q = 0; q < G; ++q)
+                if (!gkeep[q] && (nq < 0 || gscore[q] > gscore[nq])) nq = q;
+            if (nq >= 0) gmargin = (double)gscore[last] - (double)gscore[nq];
+            for (int32_t e = 0; e < E; ++e) used[e] = !gkeep[e / gs];
+        }
         for (int32_t k = 0; k < K; ++k) {
             int32_t best = -1;
             for (int32_t e = 0; e < E; ++e) {
@@ -256,8 +310,10 @@ void orc_select(const orc_desc *d, const float *logits, const float *logit_bias,
             if (next < 0 || key_before(ks[e], e, ks[next], next)) next = e;
         }
         free(used);
-        if (margin)
-            margin[s] = next < 0 ? INFINITY : (double)ks[chosen[K - 1]] - (double)ks[next];
+        if (margin) {
+            double em = next < 0 ? INFINITY : (double)ks[chosen[K - 1]] - (double)ks[next];
+            margin[s] = em < gmargin ? em : gmargin;
+        }
         /* gate weights over the selected set */
         double wsum = 0.0, wv[4096];
         if (d->score == 1) {
@@ -297,11 +353,49 @@ void orc_select(const orc_desc *d, const float *logits, const float *logit_bias,
     free(lb);
 }
 
+/* ------------------------------------------------------------- hash gate
+ * [HAI] HashGate (top-1) and [MH] "3. 理论基础" (the expert follows from a hash
+ * of the input's index, not from its values).  fmix32 is the finalisation
+ * step of MurmurHash3 (Austin Appleby, SMHasher, public domain): xor-shift by
+ * 16, multiply by 0x85ebca6b, xor-shift by 13, multiply by 0xc2b2ae35,
+ * xor-shift by 16, all mod 2^32.  Sub-token s = t H + g of token t goes to
+ * expert g E + fmix32(key_t H + g) mod E with weight 1, key_t = hash_keys[t]
+ * (or t when hash_keys is NULL), the product and sum taken mod 2^32.        */
+uint32_t orc_fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+void orc_hash_select(const orc_desc *d, const int32_t *hash_keys, int32_t *topk_idx, double *topk_w,
+                     int32_t *counts)
+{
+    const int32_t T = d->T, H = d->H, E = d->E;
+    for (int64_t t = 0; t < T; ++t) {
+        uint32_t key = hash_keys ? (uint32_t)hash_keys[t] : (uint32_t)t;
+        for (int32_t g = 0; g < H; ++g) {
+            uint32_t u = key * (uint32_t)H + (uint32_t)g;
+            int32_t e = (int32_t)(orc_fmix32(u) % (uint32_t)E);
+            int64_t s = t * H + g;
+            topk_idx[s] = g * E + e;
+            topk_w[s] = 1.0;
+            if (counts) counts[g * E + e] += 1;
+        }
+    }
+}
+
 /* ------------------------------------------------------ capacity and permute
  * [L10] items 3-4: rows are grouped by expert; an expert keeps at most C of the
  * assignments sent to it and drops the rest.  The queue of expert e is ordered
  * by sub-token index (an expert appears at most once in a sub-token's top-K),
  * so pos(s, k) is the number of earlier sub-tokens that chose the same expert.
+ * With the choice-major queue (GShard-style priority to first choices), it is
+ * ordered by slot k first, then sub-token: pos(s, k) counts the assignments
+ * (s', k') to the same expert with k' < k, or k' = k and s' < s.
  *   counts[e]  assignments to e before drops
  *   kept[e]    min(counts[e], C)
  *   offsets    exclusive prefix sum of kept (length H*E+1)
@@ -322,17 +416,18 @@ void orc_permute(const orc_desc *d, const int32_t *topk_idx, int64_t capacity,
         kept[e] = (int32_t)((capacity >= 0 && c > capacity) ? capacity : c);
         offsets[e + 1] = offsets[e] + kept[e];
     }
-    for (int64_t s = 0; s < S; ++s) {
-        for (int32_t k = 0; k < K; ++k) {
-            int32_t e = topk_idx[s * K + k];
-            int64_t pos = seen[e]++;
-            if (capacity >= 0 && pos >= capacity) {
-                dest_row[s * K + k] = -1;
-            } else {
-                int32_t row = offsets[e] + (int32_t)pos;
-                dest_row[s * K + k] = row;
-                src_sub[row] = (int32_t)s;
-            }
+    /* walk the assignments in queue order */
+    for (int64_t i = 0; i < S * K; ++i) {
+        int64_t s = d->queue == 1 ? i % S : i / K;
+        int32_t k = (int32_t)(d->queue == 1 ? i / S : i % K);
+        int32_t e = topk_idx[s * K + k];
+        int64_t pos = seen[e]++;
+        if (capacity >= 0 && pos >= capacity) {
+            dest_row[s * K + k] = -1;
+        } else {
+            int32_t row = offsets[e] + (int32_t)pos;
+            dest_row[s * K + k] = row;
+            src_sub[row] = (int32_t)s;
         }
     }
     *n_kept = offsets[Et];
@@ -424,6 +519,10 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
     const int32_t dd = h / H, Et = H * E;
     const int64_t S = (int64_t)T * H, A = S * K;
     if (H <= 0 || h % H != 0 || K <= 0 || K > E || E > 4096) return 1;
+    if (d->gate == 1 && K != 1) return 1;
+    if (d->n_groups > 1 && (E % d->n_groups != 0 || d->group_limit < 1 || d->group_limit > d->n_groups ||
+                            (int64_t)d->group_limit * (E / d->n_groups) < K))
+        return 1;
 
     float *logits = (float *)malloc(sizeof(float) * (size_t)(S * E + 1));
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
@@ -437,8 +536,15 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
     double *psum = (double *)calloc((size_t)Et, sizeof(double));
     int32_t nk = 0;
 
-    orc_logits(d, x, w->w_router, logits);
-    orc_select(d, logits, w->logit_bias, w->select_bias, idx, wts, mrg, NULL, psum);
+    if (d->gate == 1) {
+        /* the hash gate has no router: no logits, no scores (P = 0), no margin */
+        memset(logits, 0, sizeof(float) * (size_t)(S * E + 1));
+        orc_hash_select(d, w->hash_keys, idx, wts, NULL);
+        for (int64_t s = 0; s < S; ++s) mrg[s] = INFINITY;
+    } else {
+        orc_logits(d, x, w->w_router, logits);
+        orc_select(d, logits, w->logit_bias, w->select_bias, idx, wts, mrg, NULL, psum);
+    }
     orc_permute(d, idx, orc_capacity(d), cnt, kep, off, dst, src, &nk);
 
     int32_t nt = tokens ? n_tokens : T;

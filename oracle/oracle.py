@@ -12,7 +12,10 @@ volume).
 Arrays in bf16 are passed as numpy uint16 holding the raw bf16 bits.
 A layer configuration is a plain dict with keys
   T, h, H, E, K, f, n_shared, has_wo, dtype ('f32'|'bf16'),
-  score ('softmax'|'sigmoid'), act ('swiglu'|'gelu'), capacity_factor, alpha.
+  score ('softmax'|'sigmoid'), act ('swiglu'|'gelu'), capacity_factor, alpha,
+and optionally the routing variants
+  gate ('topk'|'hash'), n_groups, group_limit, queue ('token'|'choice'),
+  capacity_factor_eval, eval (0|1).
 """
 import ctypes as C
 import os
@@ -29,6 +32,8 @@ class OrcDesc(C.Structure):
         ("K", C.c_int32), ("f", C.c_int32), ("n_shared", C.c_int32),
         ("has_wo", C.c_int32), ("dtype", C.c_int32), ("score", C.c_int32),
         ("act", C.c_int32), ("capacity_factor", C.c_float), ("alpha", C.c_float),
+        ("gate", C.c_int32), ("n_groups", C.c_int32), ("group_limit", C.c_int32),
+        ("queue", C.c_int32), ("capacity_factor_eval", C.c_float), ("eval", C.c_int32),
     ]
 
 
@@ -37,7 +42,7 @@ class OrcWeights(C.Structure):
         ("w_router", C.c_void_p), ("logit_bias", C.c_void_p), ("select_bias", C.c_void_p),
         ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
-        ("w_o", C.c_void_p),
+        ("w_o", C.c_void_p), ("hash_keys", C.c_void_p),
     ]
 
 
@@ -75,6 +80,10 @@ def lib():
         _lib.orc_logits.argtypes = [C.POINTER(OrcDesc), C.c_void_p, C.c_void_p, C.c_void_p]
         _lib.orc_select.restype = None
         _lib.orc_select.argtypes = [C.POINTER(OrcDesc)] + [C.c_void_p] * 8
+        _lib.orc_fmix32.restype = C.c_uint32
+        _lib.orc_fmix32.argtypes = [C.c_uint32]
+        _lib.orc_hash_select.restype = None
+        _lib.orc_hash_select.argtypes = [C.POINTER(OrcDesc)] + [C.c_void_p] * 4
         _lib.orc_permute.restype = None
         _lib.orc_permute.argtypes = [C.POINTER(OrcDesc), C.c_void_p, C.c_int64] + [C.c_void_p] * 6
         _lib.orc_expert_ffn.restype = None
@@ -104,6 +113,10 @@ def desc(cfg, T=None):
         act=1 if cfg.get("act", "swiglu") == "gelu" else 0,
         capacity_factor=float(cfg.get("capacity_factor", 0.0)),
         alpha=float(cfg.get("alpha", 0.01)),
+        gate=1 if cfg.get("gate", "topk") == "hash" else 0,
+        n_groups=int(cfg.get("n_groups", 0)), group_limit=int(cfg.get("group_limit", 0)),
+        queue=1 if cfg.get("queue", "token") == "choice" else 0,
+        capacity_factor_eval=float(cfg.get("capacity_factor_eval", 0.0)), eval=int(cfg.get("eval", 0)),
     )
 
 
@@ -167,6 +180,24 @@ def select(cfg, logits_, logit_bias=None, select_bias=None, T=None):
     lib().orc_select(C.byref(d), _p(lg), _p(lb), _p(sb), _p(idx), _p(w), _p(margin),
                      _p(counts), _p(psum))
     return dict(topk_idx=idx, topk_w=w, margin=margin, counts=counts, psum=psum)
+
+
+def fmix32(v):
+    """MurmurHash3's 32-bit finaliser, as the hash gate uses it."""
+    return int(lib().orc_fmix32(int(v) & 0xFFFFFFFF))
+
+
+def hash_select(cfg, hash_keys=None, T=None):
+    """Hash gate (K = 1): expert ids [T*H, 1], weights (all 1) and counts."""
+    d = desc(cfg, T)
+    S = d.T * d.H
+    keys = None if hash_keys is None else _chk(np.asarray(hash_keys, dtype=np.int32), np.int32)
+    assert keys is None or keys.size == d.T
+    idx = np.empty((S, 1), dtype=np.int32)
+    w = np.empty((S, 1), dtype=np.float64)
+    counts = np.zeros(d.H * d.E, dtype=np.int32)
+    lib().orc_hash_select(C.byref(d), _p(keys), _p(idx), _p(w), _p(counts))
+    return dict(topk_idx=idx, topk_w=w, counts=counts)
 
 
 def permute(cfg, topk_idx, cap, T=None):
@@ -243,6 +274,7 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
         select_bias=ptr("select_bias", np.float32), w_gate=ptr("w_gate", el),
         w_up=ptr("w_up", el), w_down=ptr("w_down", el), sh_gate=ptr("sh_gate", el),
         sh_up=ptr("sh_up", el), sh_down=ptr("sh_down", el), w_o=ptr("w_o", el),
+        hash_keys=ptr("hash_keys", np.int32),
     )
     x = _chk(x, el)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
