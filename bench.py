@@ -6,7 +6,9 @@ A step is one call of moe_layer_forward (route -> permute -> grouped FFN ->
 combine -> aux statistics) over one batch of synthetic inputs already resident
 in HBM.  W untimed steps, then exactly K steps bracketed by device
 synchronisation and timed with HIP events on the stream the library launches
-on; value = tokens per second.  Per-stage times come from the stage entry
+on; value = tokens per second.  The same step is then timed call by call, warm
+and cache-cold (a 512 MB buffer, twice the last-level cache, written before
+each call outside the event window), for the median, p10 and p90.  Per-stage times come from the stage entry
 points timed the same way.  The dominant kernel (the grouped gate/up GEMM with
 the fused activation) is timed on its own for the roofline figure.  The CPU
 oracle is timed on a bounded sample of the same workload for the CPU baseline.
@@ -25,6 +27,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+# a one-group dense FFN descriptor carries none of the layer's routing options
+DENSE = dict(capacity_factor=0.0, gate="topk", n_groups=0, group_limit=0, queue="token", eval=0)
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_45_amd", "csrc", "gemm.hip")
 
 
@@ -34,6 +38,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=None)
+    p.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
+                   help="override a workload field, e.g. the routing variants n_groups=8, group_limit=4, "
+                        "gate=hash, queue=choice, capacity_factor_eval=1.5, eval=1")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the baseline sample")
     p.add_argument("--stage-reps", type=int, default=10)
@@ -45,6 +52,31 @@ def parse():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def per_step(fn, reps, stream, flush=None):
+    """Per-call times (ms) from an event pair around each call; with `flush`,
+    that buffer is rewritten before every call, outside the event window, so
+    each call starts with the last-level cache (256 MB MALL) holding none of
+    its inputs."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if flush is not None:
+            flush.fill_(1)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def spread(ms, T):
+    import numpy as np
+    p10, p50, p90 = (float(v) for v in np.percentile(ms, [10, 50, 90]))
+    return {"median_ms": p50, "p10_ms": p10, "p90_ms": p90, "tokens_per_s_median": T / (p50 * 1e-3),
+            "calls": len(ms)}
 
 
 def timed(fn, reps, stream):
@@ -94,7 +126,18 @@ def main():
     from mixture_experts_layer_45_amd import inputs
 
     name = args.workload or inputs.BENCH_WORKLOAD
-    cfg = inputs.variant(name)
+    over = {}
+    for kv in args.set:
+        k, v = kv.split("=", 1)
+        for conv in (int, float):
+            try:
+                v = conv(v)
+                break
+            except ValueError:
+                pass
+        over[k] = v
+    cfg = inputs.variant(name, **over)
+    name = cfg["name"]
     T, h, H, E, K, f = cfg["T"], cfg["h"], cfg["H"], cfg["E"], cfg["K"], cfg["f"]
     d = h // H
     Et, A = H * E, T * H * K
@@ -132,6 +175,12 @@ def main():
     ms_step = start.elapsed_time(end) / args.steps
     tok_s = T / (ms_step * 1e-3)
 
+    # ---- per-step spread, warm and cache-cold (512 MB written before each step)
+    warm = spread(per_step(step, args.steps, stream), T)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = dict(spread(per_step(step, args.steps, stream, flush), T), flush_bytes=512 << 20)
+    del flush
+
     # ---- routing facts of this batch (N, non-empty experts)
     n_kept = int(aux["n_kept"].item())
     kept = aux["kept"].cpu().numpy()
@@ -154,6 +203,9 @@ def main():
     R = args.stage_reps
 
     def route():
+        if cfg.get("gate") == "hash":
+            moe.moe_route_hash(desc, None, topk_idx, topk_w)
+            return
         moe.moe_route(desc, inp["x"], inp["w_router"], inp["logit_bias"], inp["select_bias"], None, 0,
                       topk_idx, topk_w, None, pm, ws_r)
 
@@ -179,7 +231,7 @@ def main():
     shared_fn = wo_fn = None
     if cfg.get("n_shared"):
         # the shared expert is one group of all T rows of x: a dense descriptor
-        dsh = moe.desc_from_cfg(dict(cfg, H=1, E=1, K=1, n_shared=0, has_wo=0, capacity_factor=0.0))
+        dsh = moe.desc_from_cfg(dict(cfg, H=1, E=1, K=1, n_shared=0, has_wo=0, **DENSE))
         off_sh = torch.tensor([0, T], **i32)
         h_sh = torch.empty((T, f), dtype=inputs.torch_dtype(cfg), device=dev)
         y_sh = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev)
@@ -191,7 +243,7 @@ def main():
     y_cat = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev) if cfg.get("has_wo") else None
     if cfg.get("has_wo"):
         # W_o is the second GEMM of a one-group descriptor with f = h
-        dwo = moe.desc_from_cfg(dict(cfg, H=1, E=1, K=1, f=h, n_shared=0, has_wo=0, capacity_factor=0.0))
+        dwo = moe.desc_from_cfg(dict(cfg, H=1, E=1, K=1, f=h, n_shared=0, has_wo=0, **DENSE))
         off_wo = torch.tensor([0, T], **i32)
         ws_wo = moe.workspace(dwo, moe.MOE_WS_FFN)
 
@@ -233,7 +285,7 @@ def main():
     n_act = 2 if cfg["act"] == "swiglu" else 1
     gemm1_flops = 2.0 * n_act * n_kept * d * f
     gemm2_flops = 2.0 * n_kept * f * d
-    route_bytes = T * h * esz + Et * d * esz + A * 8
+    route_bytes = A * 8 if cfg.get("gate") == "hash" else T * h * esz + Et * d * esz + A * 8
     distinct_rows = n_kept  # every kept row is a distinct (token, expert) pair; x rows read once per row
     permute_bytes = distinct_rows * d * esz + n_kept * d * esz + A * 4 * 2
     combine_bytes = n_kept * d * esz + A * 8 + T * h * esz + (T * h * esz if cfg.get("n_shared") else 0)
@@ -261,6 +313,23 @@ def main():
         "ffn_mfma_frac": (gemm1_flops + gemm2_flops) / ((t_g1 + t_g2) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
         "ffn_weight_bytes": w_bytes,
     }
+    # the FFN against its attainable roofline min(MFMA peak, AI x HBM BW): AI counts
+    # the weights of non-empty experts, the x rows read and the y rows written
+    # (plus the shared expert's weights and its x/y when there is one)
+    ffn_flops = gemm1_flops + gemm2_flops
+    ffn_bytes = w_bytes + 2.0 * n_kept * d * esz
+    ffn_ms = t_g1 + t_g2
+    if cfg.get("n_shared"):
+        ffn_flops += 2.0 * (n_act + 1) * T * h * f
+        ffn_bytes += (n_act + 1) * h * f * esz + 2.0 * T * h * esz
+        ffn_ms += t_sh
+    ai = ffn_flops / ffn_bytes
+    attain = min(MFMA_BF16_PEAK_TFS, ai * HBM_PEAK_GBS / 1e3)
+    ffn_tfs = ffn_flops / (ffn_ms * 1e-3) / 1e12
+    stages.update({
+        "ffn_flop_per_byte": ai, "ffn_bound": "mfma" if attain >= MFMA_BF16_PEAK_TFS else "hbm",
+        "ffn_attainable_tflops": attain, "ffn_tflops": ffn_tfs, "ffn_attainable_frac": ffn_tfs / attain,
+    })
     total_flops = gemm1_flops + gemm2_flops + 2.0 * T * H * d * E
     if cfg.get("has_wo"):
         total_flops += 2.0 * T * h * h
@@ -310,9 +379,10 @@ def main():
         "dtype": cfg["dtype"], "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": name, "tokens": T, "hidden": h, "heads": H, "experts": E, "top_k": K,
                    "ffn": f, "act": cfg["act"], "score": cfg["score"], "capacity_factor": cfg["capacity_factor"],
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **({"variant": over} if over else {})},
         "tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "n_kept": n_kept, "n_dropped": A - n_kept, "nonempty_experts": nonempty, "l_aux": l_aux,
+        "warm_per_step": warm, "cold_per_step": cold,
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -67,12 +67,30 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 typedef enum { MOE_SWIGLU = 0, MOE_GELU = 1 } moe_act;
+/* Gate kinds ("HAI-LLM MoE", "HAI-LLM 上的使用": GShard/Switch gates score the
+ * tokens, the HashGate sends each token to one expert by a hash). */
+typedef enum { MOE_GATE_TOPK = 0, MOE_GATE_HASH = 1 } moe_gate;
+/* Order of an expert's capacity queue: by sub-token, or all first choices
+ * (by sub-token) before any second choice (GShard-style priority). */
+typedef enum { MOE_QUEUE_TOKEN = 0, MOE_QUEUE_CHOICE = 1 } moe_queue;
 
 /* Layer description.  T tokens of width h; H router heads (1 = ordinary MoE);
  * E experts per head; top-K; expert hidden width f; n_shared 0 or 1 shared
  * experts (weight 1, never dropped, H = 1 only); has_wo applies W_o after the
  * head concat.  capacity_factor <= 0 means no capacity limit.  aux_alpha is
  * the alpha of L_aux.
+ * Routing variants (all zero = plain top-K, token-order queue, training CF):
+ *   gate         MOE_GATE_HASH: top-1 by hash, no router (K must be 1)
+ *   n_groups     > 1: group-limited top-K (lesson 10, item 5: a token's experts
+ *                lie in at most group_limit nodes).  A head's E experts form
+ *                n_groups contiguous groups of E/n_groups; a group's score is
+ *                its largest routing key; the group_limit best groups (ties to
+ *                the lower group) are eligible and the top-K is taken among
+ *                their experts.  Needs E % n_groups == 0, 1 <= group_limit <=
+ *                n_groups and K <= group_limit * E / n_groups.
+ *   queue        moe_queue order of each expert's capacity queue
+ *   capacity_factor_eval, eval   "HAI-LLM MoE" (train, val) capacity factors:
+ *                with eval = 1 the capacity uses capacity_factor_eval.
  * Limits: 1 <= K <= E <= 256; h % H == 0; for MOE_BF16, d = h/H and f are
  * multiples of 8 (16-byte rows). */
 typedef struct moe_desc {
@@ -83,6 +101,12 @@ typedef struct moe_desc {
     int32_t act;   /* moe_act   */
     float capacity_factor;
     float aux_alpha;
+    int32_t gate;        /* moe_gate  */
+    int32_t n_groups;    /* 0 or 1: no group limit */
+    int32_t group_limit;
+    int32_t queue;       /* moe_queue */
+    float capacity_factor_eval;
+    int32_t eval;        /* 0: capacity_factor, 1: capacity_factor_eval */
 } moe_desc;
 
 /* Flags of moe_route. */
@@ -101,7 +125,8 @@ typedef enum {
     MOE_WS_FFN = 3
 } moe_ws_kind;
 
-/* Expert capacity C = CF * K * T / E rounded up, where a value within 1e-6
+/* Expert capacity C = CF * K * T / E rounded up (CF = capacity_factor, or
+ * capacity_factor_eval when eval = 1), where a value within 1e-6
  * (relative) of an integer counts as that integer (lesson 10, item 4: each
  * expert keeps at most C of the assignments sent to it).  Returns INT32_MAX
  * when capacity_factor <= 0 (no limit) and -1 for an invalid descriptor. */
@@ -131,11 +156,26 @@ moe_status moe_workspace_size(const moe_desc *desc, int32_t kind, size_t *bytes)
  *   prob_mean  [H*E] fp32|NULL   P_e = mean over the T tokens of the full score
  *                              distribution of the expert's head (softmax over
  *                              all E, or sigma_e / sum of all sigma)
+ * With n_groups > 1 the selection is group-limited (see moe_desc).  The hash
+ * gate does not use this call (MOE_ERR_INVALID_ARG): see moe_route_hash.
  * Needs moe_workspace_size(MOE_WS_ROUTE) bytes of workspace. */
 moe_status moe_route(const moe_desc *desc, const void *x, const void *w_router,
                      const float *logit_bias, const float *select_bias, float *logits,
                      uint32_t flags, int32_t *topk_idx, float *topk_w, int32_t *counts,
                      float *prob_mean, void *ws, size_t ws_bytes, void *stream);
+
+/* Hash gate ("HAI-LLM MoE", HashGate, top-1; "Multi-Head LatentMoE 与 Head
+ * 并行", "3. 理论基础": the expert follows from a hash of the input's index).
+ * Sub-token s = t*H + g goes to expert g*E + fmix32(key_t*H + g) mod E with
+ * weight 1, where key_t = hash_keys[t] (e.g. the token's vocabulary id) or t
+ * when hash_keys is NULL, the arithmetic mod 2^32, and fmix32 the 32-bit
+ * finaliser of MurmurHash3 (xor-shift 16, * 0x85ebca6b, xor-shift 13,
+ * * 0xc2b2ae35, xor-shift 16).  Needs desc->gate == MOE_GATE_HASH, K = 1.
+ *   hash_keys [T] int32|NULL;  topk_idx [T*H][1] int32;  topk_w [T*H][1] fp32
+ *   counts    [H*E] int32|NULL  assignments per expert
+ * No workspace. */
+moe_status moe_route_hash(const moe_desc *desc, const int32_t *hash_keys, int32_t *topk_idx,
+                          float *topk_w, int32_t *counts, void *stream);
 
 /* Histogram, prefix scan, capacity and permutation (lesson 10, items 3-4).
  *   topk_idx   [T*H][K] int32  from moe_route
@@ -147,7 +187,9 @@ moe_status moe_route(const moe_desc *desc, const void *x, const void *w_router,
  *                              are [offsets[e], offsets[e+1])
  *   dest_row   [T*H*K] int32   row of each assignment in x_perm, -1 if dropped.
  *                              The queue of an expert is ordered by sub-token
- *                              index; the first C assignments are kept.
+ *                              index (MOE_QUEUE_TOKEN) or by slot, then
+ *                              sub-token (MOE_QUEUE_CHOICE); the first C
+ *                              assignments are kept, in queue order.
  *   src_token  [T*H*K] int32   sub-token that fills each row (first n_kept used)
  *   x_perm     [T*H*K][d]      x_perm[row] = slice g of x[t] for s = t*H + g
  *   n_kept     [1] int32       total kept rows = offsets[H*E]
@@ -203,6 +245,7 @@ typedef struct moe_weights {
     const void *w_gate, *w_up, *w_down;
     const void *sh_gate, *sh_up, *sh_down;
     const void *w_o;
+    const int32_t *hash_keys; /* [T] keys of the hash gate, or NULL (key = token index) */
 } moe_weights;
 
 /* Optional outputs of moe_layer_forward; device pointers, any may be NULL.
@@ -224,6 +267,7 @@ typedef struct moe_aux {
 
 /* The whole layer: route -> permute -> grouped FFN (+ shared expert) ->
  * combine (-> W_o) -> aux statistics, all on `stream` with no host sync.
+ * With the hash gate, w_router is unused and P and l_aux are 0 (no scores).
  *   x [T][h], y [T][h]; capacity = moe_capacity(desc).
  * Needs moe_workspace_size(MOE_WS_LAYER) bytes of workspace. */
 moe_status moe_layer_forward(const moe_desc *desc, const moe_weights *w, const void *x, void *y,

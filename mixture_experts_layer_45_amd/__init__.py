@@ -11,13 +11,13 @@ import ctypes as C
 
 from . import _ffi
 from ._ffi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FFN_GEMM1, MOE_FFN_GEMM2, MOE_GELU,  # noqa: F401
-                   MOE_LOGITS_IN, MOE_LOGITS_OUT, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU,
+                   MOE_GATE_HASH, MOE_GATE_TOPK, MOE_QUEUE_CHOICE, MOE_QUEUE_TOKEN, MOE_LOGITS_IN, MOE_LOGITS_OUT, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU,
                    MOE_WS_FFN, MOE_WS_LAYER, MOE_WS_PERMUTE, MOE_WS_ROUTE, MoeAux, MoeDesc,
                    MoeWeights)
 
 __all__ = [
     "MoeError", "MoeDesc", "desc_from_cfg", "moe_capacity", "moe_workspace_size", "moe_route",
-    "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_rows", "moe_combine", "moe_layer_forward", "moe_version", "lib",
+    "moe_route_hash", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_rows", "moe_combine", "moe_layer_forward", "moe_version", "lib",
     "workspace",
 ]
 
@@ -47,6 +47,10 @@ def desc_from_cfg(cfg, T=None):
         score=MOE_SIGMOID if cfg.get("score", "softmax") == "sigmoid" else MOE_SOFTMAX,
         act=MOE_GELU if cfg.get("act", "swiglu") == "gelu" else MOE_SWIGLU,
         capacity_factor=float(cfg.get("capacity_factor", 0.0)), aux_alpha=float(cfg.get("alpha", 0.01)),
+        gate=MOE_GATE_HASH if cfg.get("gate", "topk") == "hash" else MOE_GATE_TOPK,
+        n_groups=int(cfg.get("n_groups", 0)), group_limit=int(cfg.get("group_limit", 0)),
+        queue=MOE_QUEUE_CHOICE if cfg.get("queue", "token") == "choice" else MOE_QUEUE_TOKEN,
+        capacity_factor_eval=float(cfg.get("capacity_factor_eval", 0.0)), eval=int(cfg.get("eval", 0)),
     )
 
 
@@ -100,6 +104,11 @@ def moe_route(desc, x, w_router, logit_bias, select_bias, logits, flags, topk_id
                            _ptr(prob_mean), wp, wn, _stream(stream)))
 
 
+def moe_route_hash(desc, hash_keys, topk_idx, topk_w, counts=None, stream=None):
+    _check(lib().moe_route_hash(C.byref(desc), _ptr(hash_keys), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                                _stream(stream)))
+
+
 def moe_permute(desc, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm,
                 n_kept=None, ws=None, stream=None):
     wp, wn = _ws(ws)
@@ -130,7 +139,7 @@ def moe_combine(desc, dest_row, topk_w, y_perm, y_shared, y, stream=None):
 
 
 _WEIGHT_KEYS = ("w_router", "logit_bias", "select_bias", "w_gate", "w_up", "w_down", "sh_gate",
-                "sh_up", "sh_down", "w_o")
+                "sh_up", "sh_down", "w_o", "hash_keys")
 _AUX_KEYS = ("topk_idx", "topk_w", "dest_row", "counts", "kept", "n_kept", "n_dropped", "f", "P", "l_aux")
 
 

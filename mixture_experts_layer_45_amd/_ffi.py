@@ -13,6 +13,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_SWIGLU, MOE_GELU = 0, 1
+MOE_GATE_TOPK, MOE_GATE_HASH = 0, 1
+MOE_QUEUE_TOKEN, MOE_QUEUE_CHOICE = 0, 1
 MOE_LOGITS_IN, MOE_LOGITS_OUT = 1, 2
 MOE_FFN_GEMM1, MOE_FFN_GEMM2 = 1, 2
 MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FFN = range(4)
@@ -25,6 +27,8 @@ class MoeDesc(C.Structure):
         ("K", C.c_int32), ("f", C.c_int32), ("n_shared", C.c_int32), ("has_wo", C.c_int32),
         ("dtype", C.c_int32), ("score", C.c_int32), ("act", C.c_int32),
         ("capacity_factor", C.c_float), ("aux_alpha", C.c_float),
+        ("gate", C.c_int32), ("n_groups", C.c_int32), ("group_limit", C.c_int32), ("queue", C.c_int32),
+        ("capacity_factor_eval", C.c_float), ("eval", C.c_int32),
     ]
 
 
@@ -33,7 +37,7 @@ class MoeWeights(C.Structure):
         ("w_router", C.c_void_p), ("logit_bias", C.c_void_p), ("select_bias", C.c_void_p),
         ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
         ("sh_gate", C.c_void_p), ("sh_up", C.c_void_p), ("sh_down", C.c_void_p),
-        ("w_o", C.c_void_p),
+        ("w_o", C.c_void_p), ("hash_keys", C.c_void_p),
     ]
 
 
@@ -52,6 +56,7 @@ SIGNATURES = {
     "moe_workspace_size": (C.c_int, [C.POINTER(MoeDesc), C.c_int32, C.POINTER(C.c_size_t)]),
     "moe_route": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, _VP, _VP, C.c_uint32, _VP, _VP, _VP, _VP,
                             _VP, C.c_size_t, _VP]),
+    "moe_route_hash": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, _VP, _VP]),
     "moe_permute": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                               _VP, C.c_size_t, _VP]),
     "moe_grouped_ffn": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP,

@@ -64,6 +64,23 @@ moe_status check_desc(const moe_desc* d) {
     if ((long long)d->T * d->H * d->K > 0x3fffffffLL)
         return fail(MOE_ERR_UNSUPPORTED, "T*H*K = %lld assignments is too many", (long long)d->T * d->H * d->K);
     if (!(d->capacity_factor == d->capacity_factor)) return fail(MOE_ERR_INVALID_ARG, "capacity_factor is NaN");
+    if (!(d->capacity_factor_eval == d->capacity_factor_eval))
+        return fail(MOE_ERR_INVALID_ARG, "capacity_factor_eval is NaN");
+    if (d->eval != 0 && d->eval != 1) return fail(MOE_ERR_INVALID_ARG, "eval must be 0 or 1");
+    if (d->gate != MOE_GATE_TOPK && d->gate != MOE_GATE_HASH) return fail(MOE_ERR_INVALID_ARG, "unknown gate %d", d->gate);
+    if (d->gate == MOE_GATE_HASH && d->K != 1) return fail(MOE_ERR_INVALID_ARG, "the hash gate needs K = 1");
+    if (d->queue != MOE_QUEUE_TOKEN && d->queue != MOE_QUEUE_CHOICE)
+        return fail(MOE_ERR_INVALID_ARG, "unknown queue order %d", d->queue);
+    if (d->n_groups < 0) return fail(MOE_ERR_INVALID_ARG, "n_groups = %d < 0", d->n_groups);
+    if (d->n_groups > 1) {
+        if (d->gate != MOE_GATE_TOPK) return fail(MOE_ERR_INVALID_ARG, "a group limit needs the top-K gate");
+        if (d->E % d->n_groups != 0)
+            return fail(MOE_ERR_INVALID_ARG, "E = %d is not a multiple of n_groups = %d", d->E, d->n_groups);
+        if (d->group_limit < 1 || d->group_limit > d->n_groups)
+            return fail(MOE_ERR_INVALID_ARG, "group_limit = %d outside [1, n_groups = %d]", d->group_limit, d->n_groups);
+        if ((long)d->group_limit * (d->E / d->n_groups) < d->K)
+            return fail(MOE_ERR_INVALID_ARG, "K = %d > group_limit * E / n_groups", d->K);
+    }
     return MOE_OK;
 }
 
@@ -72,8 +89,9 @@ int esize(const moe_desc* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
 // C = CF * K * T / E rounded up; a value within 1e-6 (relative) of an integer
 // is that integer.
 int64_t capacity_of(const moe_desc* d) {
-    if (d->capacity_factor <= 0.0f) return INT32_MAX;
-    const double v = (double)d->capacity_factor * d->K * (double)d->T / d->E;
+    const float cf = d->eval ? d->capacity_factor_eval : d->capacity_factor;
+    if (cf <= 0.0f) return INT32_MAX;
+    const double v = (double)cf * d->K * (double)d->T / d->E;
     const double nearest = floor(v + 0.5);
     const double slack = 1e-6 * (v > 1.0 ? v : 1.0);
     double c = (fabs(v - nearest) <= slack) ? nearest : ceil(v);
@@ -215,6 +233,7 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
     if (flags & ~(MOE_LOGITS_IN | MOE_LOGITS_OUT)) return fail(MOE_ERR_INVALID_ARG, "unknown route flags 0x%x", flags);
     if ((flags & MOE_LOGITS_IN) && (flags & MOE_LOGITS_OUT))
         return fail(MOE_ERR_INVALID_ARG, "MOE_LOGITS_IN and MOE_LOGITS_OUT are exclusive");
+    if (d->gate == MOE_GATE_HASH) return fail(MOE_ERR_INVALID_ARG, "the hash gate routes with moe_route_hash");
     if (d->T == 0) return MOE_OK;
     if ((flags & (MOE_LOGITS_IN | MOE_LOGITS_OUT)) && !logits)
         return fail(MOE_ERR_INVALID_ARG, "logits is NULL but a logits flag is set");
@@ -230,12 +249,29 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
     if (counts && (e = launch_fill_i32(counts, p.Et, 0, st)) != hipSuccess) return dev_fail(e, "fill");
     RouteArgs a{};
     a.T = d->T; a.h = d->h; a.H = d->H; a.E = d->E; a.K = d->K; a.dtype = d->dtype; a.score = d->score;
+    a.n_groups = d->n_groups > 1 ? d->n_groups : 1; a.group_limit = d->group_limit;
     a.flags = flags; a.x = x; a.w_router = w_router; a.logit_bias = logit_bias;
     a.select_bias = d->score == MOE_SIGMOID ? select_bias : nullptr;
     a.logits = logits; a.topk_idx = topk_idx; a.topk_w = topk_w; a.counts = counts; a.prob_part = w.prob_part;
     if ((e = launch_route(a, st)) != hipSuccess) return dev_fail(e, "route kernel");
     if (prob_mean && (e = launch_prob_mean(w.prob_part, p.route_nbx, p.H, p.E, p.T, prob_mean, st)) != hipSuccess)
         return dev_fail(e, "prob_mean kernel");
+    return MOE_OK;
+}
+
+moe_status moe_route_hash(const moe_desc* d, const int32_t* hash_keys, int32_t* topk_idx, float* topk_w,
+                          int32_t* counts, void* stream) {
+    g_err[0] = 0;
+    moe_status s = check_desc(d);
+    if (s != MOE_OK) return s;
+    if (d->gate != MOE_GATE_HASH) return fail(MOE_ERR_INVALID_ARG, "desc->gate is not MOE_GATE_HASH");
+    if (d->T == 0) return MOE_OK;
+    if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx or topk_w is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (counts && (e = launch_fill_i32(counts, d->H * d->E, 0, st)) != hipSuccess) return dev_fail(e, "fill");
+    if ((e = launch_route_hash(hash_keys, d->T, d->H, d->E, topk_idx, topk_w, counts, st)) != hipSuccess)
+        return dev_fail(e, "hash route kernel");
     return MOE_OK;
 }
 
@@ -257,7 +293,7 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, const void* x
     Carver c(ws);
     PermuteArgs a{};
     a.A = p.A; a.K = p.K; a.H = p.H; a.Et = p.Et; a.d = p.d; a.h = p.h; a.dtype = d->dtype;
-    a.capacity = capacity; a.topk_idx = topk_idx; a.x = x; a.counts = counts; a.kept = kept;
+    a.capacity = capacity; a.queue = d->queue; a.topk_idx = topk_idx; a.x = x; a.counts = counts; a.kept = kept;
     a.offsets = offsets; a.dest_row = dest_row; a.src_token = src_token; a.x_perm = x_perm;
     a.n_kept = n_kept; a.hist = carve_permute(c, p);
     const int64_t byc = capacity >= INT32_MAX ? (int64_t)p.A : (int64_t)p.Et * capacity;
@@ -343,7 +379,7 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
     if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
     if (d->T == 0) return MOE_OK;
     if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
-    if (!w->w_router || !w->w_gate || !w->w_down || (d->act == MOE_SWIGLU && !w->w_up))
+    if ((d->gate == MOE_GATE_TOPK && !w->w_router) || !w->w_gate || !w->w_down || (d->act == MOE_SWIGLU && !w->w_up))
         return fail(MOE_ERR_INVALID_ARG, "a routed-expert or router weight is NULL");
     if (d->n_shared && (!w->sh_gate || !w->sh_down || (d->act == MOE_SWIGLU && !w->sh_up)))
         return fail(MOE_ERR_INVALID_ARG, "a shared-expert weight is NULL");
@@ -362,19 +398,28 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
     const bool want_stats = aux && (aux->f || aux->P || aux->l_aux || aux->kept || aux->n_kept || aux->n_dropped);
     hipError_t e;
 
-    RouteArgs ra{};
-    ra.T = p.T; ra.h = p.h; ra.H = p.H; ra.E = p.E; ra.K = p.K; ra.dtype = d->dtype; ra.score = d->score;
-    ra.flags = 0; ra.x = x; ra.w_router = w->w_router; ra.logit_bias = w->logit_bias;
-    ra.select_bias = d->score == MOE_SIGMOID ? w->select_bias : nullptr;
-    ra.logits = nullptr; ra.topk_idx = topk_idx; ra.topk_w = topk_w; ra.counts = nullptr;
-    ra.prob_part = want_stats ? L.prob_part : nullptr;
-    if ((e = launch_route(ra, st)) != hipSuccess) return dev_fail(e, "route kernel");
-    if (want_stats && (e = launch_prob_mean(L.prob_part, p.route_nbx, p.H, p.E, p.T, L.prob_mean, st)) != hipSuccess)
-        return dev_fail(e, "prob_mean kernel");
+    if (d->gate == MOE_GATE_HASH) {
+        // no router and no scores: P (and so L_aux) is zero
+        if ((e = launch_route_hash(w->hash_keys, p.T, p.H, p.E, topk_idx, topk_w, nullptr, st)) != hipSuccess)
+            return dev_fail(e, "hash route kernel");
+        if (want_stats && (e = launch_fill_i32((int32_t*)L.prob_mean, p.Et, 0, st)) != hipSuccess)
+            return dev_fail(e, "fill");
+    } else {
+        RouteArgs ra{};
+        ra.T = p.T; ra.h = p.h; ra.H = p.H; ra.E = p.E; ra.K = p.K; ra.dtype = d->dtype; ra.score = d->score;
+        ra.n_groups = d->n_groups > 1 ? d->n_groups : 1; ra.group_limit = d->group_limit;
+        ra.flags = 0; ra.x = x; ra.w_router = w->w_router; ra.logit_bias = w->logit_bias;
+        ra.select_bias = d->score == MOE_SIGMOID ? w->select_bias : nullptr;
+        ra.logits = nullptr; ra.topk_idx = topk_idx; ra.topk_w = topk_w; ra.counts = nullptr;
+        ra.prob_part = want_stats ? L.prob_part : nullptr;
+        if ((e = launch_route(ra, st)) != hipSuccess) return dev_fail(e, "route kernel");
+        if (want_stats && (e = launch_prob_mean(L.prob_part, p.route_nbx, p.H, p.E, p.T, L.prob_mean, st)) != hipSuccess)
+            return dev_fail(e, "prob_mean kernel");
+    }
 
     PermuteArgs pa{};
     pa.A = p.A; pa.K = p.K; pa.H = p.H; pa.Et = p.Et; pa.d = p.d; pa.h = p.h; pa.dtype = d->dtype;
-    pa.capacity = (int)p.cap; pa.topk_idx = topk_idx; pa.x = x; pa.counts = counts; pa.kept = L.kept;
+    pa.capacity = (int)p.cap; pa.queue = d->queue; pa.topk_idx = topk_idx; pa.x = x; pa.counts = counts; pa.kept = L.kept;
     // no row gather: the gate/up GEMM reads its rows of x through src_token
     pa.offsets = L.offsets; pa.dest_row = dest_row; pa.src_token = L.src_token; pa.x = nullptr;
     pa.x_perm = nullptr; pa.n_kept = nullptr; pa.hist = L.hist; pa.max_rows = p.max_rows;

@@ -40,6 +40,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // Every launcher enqueues on `st` and returns hipGetLastError() of the launch.
 struct RouteArgs {
     int T, h, H, E, K, dtype, score;
+    int n_groups, group_limit;  // group-limited top-K when n_groups > 1
     uint32_t flags;
     const void* x;
     const void* w_router;
@@ -53,6 +54,9 @@ struct RouteArgs {
 };
 int route_blocks(int T, int E, int dtype);  // route blocks per head (= rows of prob_part per head)
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+// hash gate: topk_idx/topk_w [T*H] (K = 1); counts (may be null) accumulated
+hipError_t launch_route_hash(const int32_t* keys, int T, int H, int E, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, hipStream_t st);
 hipError_t launch_prob_mean(const float* prob_part, int n_blocks_per_head, int H, int E, int T,
                             float* prob_mean, hipStream_t st);
 
@@ -60,6 +64,7 @@ struct PermuteArgs {
     int A;        // assignments = T*H*K
     int K, H, Et, d, h, dtype;
     int capacity;
+    int queue;            // MOE_QUEUE_TOKEN or MOE_QUEUE_CHOICE
     const int32_t* topk_idx;
     const void* x;        // may be null (no gather)
     int32_t* counts;

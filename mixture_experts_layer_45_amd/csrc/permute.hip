@@ -7,8 +7,11 @@
 // ("Chương 10: Song song MoE", items 1 and 4: capacity factor, drop/pad).  On
 // one GPU the pack is a permutation of the token rows into expert-major order.
 //
-// The assignment list (T*H*K expert ids, sub-token-major) is cut into chunks of
-// CHUNK ids, one wave per chunk:
+// The assignment list (T*H*K expert ids) is walked in queue order -- the
+// stored sub-token-major order, or, for the choice-major queue (all first
+// choices, then all second choices, ...), position i = k*S + s holding
+// assignment s*K + k -- and cut into chunks of CHUNK positions, one wave per
+// chunk:
 //   1. hist:    per-chunk expert counts (LDS integer atomics; exact):
 //               hist[chunk][e].
 //   2. scan:    per expert, the exclusive prefix over chunks (chunk order), the
@@ -35,14 +38,23 @@ constexpr int MAX_ET = 4096;      // experts the LDS tables hold
 
 int permute_chunks(int A) { return (A + CHUNK - 1) / CHUNK; }
 
-__global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int Et, int nch, int32_t* hist) {
+// assignment at queue position i (S sub-tokens, K slots)
+__device__ __forceinline__ int queue_at(int i, int S, int K, bool choice) {
+    if (!choice) return i;
+    const int k = i / S;
+    return (i - k * S) * K + k;
+}
+
+__global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nch,
+                                                  int32_t* hist) {
     __shared__ int cnt[MAX_ET];
     for (int e = threadIdx.x; e < Et; e += 64) cnt[e] = 0;
     __syncthreads();
     const int a0 = blockIdx.x * CHUNK;
     const int a1 = min(a0 + CHUNK, A);
-    for (int a = a0 + threadIdx.x; a < a1; a += 64) {
-        const int e = idx[a];
+    const int S = A / K;
+    for (int i = a0 + threadIdx.x; i < a1; i += 64) {
+        const int e = idx[queue_at(i, S, K, choice)];
         if ((unsigned)e < (unsigned)Et) atomicAdd(&cnt[e], 1);  // out-of-range ids are dropped
     }
     __syncthreads();
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int 
     }
 }
 
-__global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int K, int Et, int nbits,
+__global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nbits,
                                                   int capacity, const int32_t* base,
                                                   const int32_t* offsets, int32_t* dest_row,
                                                   int32_t* src_token) {
@@ -144,10 +156,12 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int
     __syncthreads();
     const uint64_t lt = lanemask_lt();
     const int a0 = blockIdx.x * CHUNK;
+    const int S = A / K;
     for (int step = 0; step < CHUNK / 64; ++step) {
-        const int a = a0 + step * 64 + lane;
+        const int i = a0 + step * 64 + lane;
         if (a0 + step * 64 >= A) break;  // uniform
-        const int ev = a < A ? idx[a] : -1;
+        const int a = i < A ? queue_at(i, S, K, choice) : A;
+        const int ev = i < A ? idx[a] : -1;
         const bool valid = (unsigned)ev < (unsigned)Et;
         const int e = valid ? ev : 0;
         // lanes with the same (valid, e)
@@ -206,7 +220,8 @@ hipError_t launch_permute(const PermuteArgs& p, hipStream_t st) {
     const int nch = permute_chunks(p.A);
     hipError_t err;
     if (nch > 0) {
-        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.Et, nch, p.hist);
+        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE,
+                           p.Et, nch, p.hist);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, p.hist, nch, p.Et, p.capacity, p.counts,
@@ -215,7 +230,7 @@ hipError_t launch_permute(const PermuteArgs& p, hipStream_t st) {
     if (nch == 0) return hipSuccess;
     int nbits = 1;
     while ((1 << nbits) < p.Et) ++nbits;
-    hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.Et, nbits,
+    hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE, p.Et, nbits,
                        p.capacity, p.hist, p.offsets, p.dest_row, p.src_token);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (p.x && p.x_perm && p.max_rows > 0) {

@@ -18,6 +18,18 @@
 // the lanes hold the keys of experts lane, lane+64, ...; K rounds of a wave
 // arg-max (key descending, index ascending) pick the experts.  Gate weights,
 // the per-block score sums for P and the per-block expert histogram follow.
+//
+// Group-limited selection (lesson 10, item 5: a token's experts lie in at
+// most M nodes): a head's experts form n_groups contiguous groups scored by
+// their largest key, and only the group_limit best groups are eligible.  Both
+// kernels find those groups with group_limit arg-max rounds over the experts of
+// groups not yet kept: the best remaining key lies in the best remaining
+// group, and on equal scores the lower expert, hence the lower group, wins.
+//
+// The hash gate ("HAI-LLM MoE" HashGate; "Multi-Head LatentMoE 与 Head 并行",
+// "3. 理论基础") has no router: route_hash_kernel maps sub-token t*H + g to
+// expert fmix32(key_t*H + g) mod E of head g, fmix32 being MurmurHash3's
+// 32-bit finaliser.
 #include "common.hpp"
 
 namespace moe {
@@ -202,6 +214,32 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
                 key[j] = l;
             }
             used[j] = !valid;
+        }
+        if (a.n_groups > 1) {
+            const int gsz = E / a.n_groups;
+            bool gk[EJ];
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) gk[j] = false;
+            for (int m = 0; m < a.group_limit; ++m) {
+                float bk = NEG;
+                int be = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) {
+                    const int e = lane + 64 * j;
+                    if (!used[j] && !gk[j] && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
+                }
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) {
+                    const float ok = __shfl_xor(bk, off);
+                    const int oe = __shfl_xor(be, off);
+                    if (better(ok, oe, bk, be)) { bk = ok; be = oe; }
+                }
+                const int gb = be / gsz;
+#pragma unroll
+                for (int j = 0; j < EJ; ++j) gk[j] = gk[j] || (lane + 64 * j) / gsz == gb;
+            }
+#pragma unroll
+            for (int j = 0; j < EJ; ++j) used[j] = used[j] || !gk[j];
         }
         // K rounds of wave arg-max; slot k is kept by lane k % 64
         int my_e[4] = {0, 0, 0, 0};
@@ -416,11 +454,32 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
                 key[e] = l;
             }
         }
+        // group limit: experts outside the group_limit best groups are excluded
+        uint64_t excl = 0;
+        if (a.n_groups > 1) {
+            const int gsz = E / a.n_groups;  // <= 32 here (E <= 64, n_groups >= 2)
+            const uint64_t gbits = (1ull << gsz) - 1ull;
+            uint64_t kept = 0;
+            for (int m = 0; m < a.group_limit; ++m) {
+                float bk = NEG;
+                int be = 0;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) {
+                    const bool free_e = e < E && !((kept >> e) & 1ull);
+                    if (free_e && better(key[e], e, bk, be)) {
+                        bk = key[e];
+                        be = e;
+                    }
+                }
+                kept |= gbits << ((be / gsz) * gsz);
+            }
+            excl = ~kept;
+        }
         // two passes of K sequential arg-max rounds: the first sums the kept
         // scores, the second writes the normalised weights
         float den = 0.0f, vmax = 0.0f;
         for (int pass = 0; pass < 2; ++pass) {
-            uint64_t used = 0;
+            uint64_t used = excl;
             for (int k = 0; k < K; ++k) {
                 float bk = NEG, bv = 0.0f;
                 int be = EP;
@@ -496,6 +555,38 @@ __global__ __launch_bounds__(256) void prob_mean_kernel(const float* part, int n
         __syncthreads();
     }
     if (threadIdx.x == 0) out[i] = T > 0 ? red[0] / (float)T : 0.0f;
+}
+
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+// one thread per sub-token; integer atomics only, so counts are exact
+__global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* keys, int T, int H, int E,
+                                                         int32_t* topk_idx, float* topk_w, int32_t* counts) {
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= T * H) return;
+    const int t = s / H, g = s - t * H;
+    const uint32_t key = keys ? (uint32_t)keys[t] : (uint32_t)t;
+    const uint32_t u = key * (uint32_t)H + (uint32_t)g;
+    const int e = (int)(fmix32(u) % (uint32_t)E);
+    topk_idx[s] = g * E + e;
+    topk_w[s] = 1.0f;
+    if (counts) atomicAdd(&counts[g * E + e], 1);
+}
+
+hipError_t launch_route_hash(const int32_t* keys, int T, int H, int E, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, hipStream_t st) {
+    const int S = T * H;
+    if (S == 0) return hipSuccess;
+    hipLaunchKernelGGL(route_hash_kernel, dim3((S + 255) / 256), dim3(256), 0, st, keys, T, H, E, topk_idx,
+                       topk_w, counts);
+    return hipGetLastError();
 }
 
 template <int NB>

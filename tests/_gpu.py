@@ -119,7 +119,8 @@ def excluded_tokens(cfg, ref, gpu_idx, gpu_dest):
     gpu_kept = (np.asarray(gpu_dest) >= 0).reshape(T, H * K)
     ridx = ref["topk_idx"].reshape(T, H * K)
     gidx = np.asarray(gpu_idx).reshape(T, H * K)
-    if cfg.get("capacity_factor", 0) > 0:
+    cf = cfg.get("capacity_factor_eval", 0.0) if cfg.get("eval") else cfg.get("capacity_factor", 0.0)
+    if cf > 0:
         touched = set()
         for t in np.nonzero(close)[0]:
             touched.update(ridx[t].tolist())

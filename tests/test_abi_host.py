@@ -4,6 +4,7 @@ include/moe.h declares, and rejects bad arguments before touching the GPU
 import ctypes as C
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -31,11 +32,27 @@ def test_library_exports_every_declared_symbol():
     assert moe.moe_version().startswith("libmoe")
 
 
-def test_struct_layouts_match_header():
-    # 11 int32 + 2 float; 10 and 10 pointers
-    assert C.sizeof(_ffi.MoeDesc) == 13 * 4
-    assert C.sizeof(_ffi.MoeWeights) == 10 * 8
-    assert C.sizeof(_ffi.MoeAux) == 10 * 8
+def test_struct_layouts_match_header(tmp_path):
+    # compile the header and compare every field offset with the ctypes structs
+    structs = {"moe_desc": _ffi.MoeDesc, "moe_weights": _ffi.MoeWeights, "moe_aux": _ffi.MoeAux}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, fname, v = line.split()
+        got[(cname, fname)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == C.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
 
 
 @pytest.mark.parametrize("name", list(inputs.CONFIGS))
@@ -71,6 +88,14 @@ def _desc(**over):
     (dict(f=100), _ffi.MOE_ERR_UNSUPPORTED),      # f % 8
     (dict(T=-1), _ffi.MOE_ERR_INVALID_ARG),
     (dict(n_shared=1, H=2, h=64), _ffi.MOE_ERR_UNSUPPORTED),
+    (dict(gate="hash", K=2), _ffi.MOE_ERR_INVALID_ARG),          # hash gate is top-1
+    (dict(n_groups=3, group_limit=1), _ffi.MOE_ERR_INVALID_ARG),  # 8 % 3
+    (dict(n_groups=4, group_limit=5), _ffi.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=4, group_limit=0), _ffi.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=8, group_limit=1, K=2), _ffi.MOE_ERR_INVALID_ARG),  # 1 group of 1 < K
+    (dict(gate="hash", K=1, n_groups=2, group_limit=1), _ffi.MOE_ERR_INVALID_ARG),
+    (dict(eval=2), _ffi.MOE_ERR_INVALID_ARG),
+    (dict(capacity_factor_eval=float("nan")), _ffi.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_descriptors_are_rejected(over, status):
     d = _desc(**over)
@@ -101,6 +126,29 @@ def test_stage_calls_validate_before_launch():
     one = C.c_void_p(4096)
     assert L.moe_permute(C.byref(d), one, None, 4, one, one, one, one, one, None, None, fake, 8, None) == 3
     assert L.moe_permute(C.byref(d), one, None, 4, one, one, one, one, one, None, None, None, 0, None) == 3
+
+
+def test_routing_variant_entry_points_validate():
+    L = _ffi.lib()
+    one = C.c_void_p(4096)
+    hd = _desc(K=1, gate="hash")
+    # the hash gate has its own entry point; the top-K router refuses it
+    assert L.moe_route(C.byref(hd), one, one, None, None, None, 0, one, one, None, None, None, 0, None) == 1
+    assert "moe_route_hash" in L.moe_last_error().decode()
+    assert L.moe_route_hash(C.byref(_desc()), None, one, one, None, None) == 1
+    assert L.moe_route_hash(C.byref(hd), None, None, one, None, None) == 1
+    assert L.moe_route_hash(C.byref(_desc(K=1, gate="hash", T=0)), None, None, None, None, None) == 0
+    # the hash-gated layer needs no router weights
+    W = _ffi.MoeWeights()
+    assert L.moe_layer_forward(C.byref(hd), C.byref(W), one, one, None, None, 0, None) == 1
+    assert "routed-expert" in L.moe_last_error().decode()
+
+
+def test_eval_capacity_factor_agrees_with_oracle():
+    for cf, cfe, ev in [(1.25, 1.5, 0), (1.25, 1.5, 1), (1.0, 0.0, 1), (2.0, 1.0, 1)]:
+        cfg = dict(inputs.CONFIGS["top2_e8_h4096"], capacity_factor=cf, capacity_factor_eval=cfe, eval=ev)
+        ref = orc.capacity(cfg)
+        assert moe.moe_capacity(moe.desc_from_cfg(cfg)) == (moe.INT32_MAX if ref is None else ref)
 
 
 def test_empty_batch_is_a_no_op():
