@@ -644,3 +644,415 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* ============================================================ backward pass
+ * Gradients of the loss L = sum_{t,j} dy[t][j] * y[t][j] + c_aux * L_aux with
+ * respect to x and every weight, by the chain rule through the forward pass
+ * above ([L10] item 1: y = sum over the kept top-K of w_k FFN_k(x), plus the
+ * shared expert, then W_o; item 4: L_aux = alpha E sum_i f_i P_i).  Every
+ * quantity is recomputed here in double from the inputs.
+ *   - Selection (top-K, group limit, capacity) is piecewise constant, so only
+ *     the gate weights carry a gradient to the logits: for the softmax gate
+ *     w_k = exp(l_k) / sum_{j in S} exp(l_j), dl_j = w_j (dw_j - sum_k w_k dw_k)
+ *     for j in the selected set S (dropped slots included: their dw is 0 but
+ *     their logit still normalises the kept weights); for the sigmoid gate
+ *     w_k = s_k / sum_S s, ds_j = (dw_j - sum_k w_k dw_k) / sum_S s and
+ *     dl_j = ds_j s_j (1 - s_j).  Experts outside S get 0.  K = 1 gives 0.
+ *   - f_i is a count (no gradient); P_i = mean_t p_t,i, so with c = alpha E / (H T)
+ *     softmax:  dL_aux/dl_j = c p_j (f_j - sum_i f_i p_i)
+ *     sigmoid:  dL_aux/dl_j = c s_j (1 - s_j) / sum_all s * (f_j - sum_i f_i p_i).
+ *   - The hash gate has no router and no scores: no router gradient.
+ *   - silu'(a) = sigma(a) (1 + a (1 - sigma(a))); gelu'(a) = Phi(a) + a phi(a).
+ * With absm = 1 every factor is replaced by its absolute value (and every
+ * difference by a sum), which yields, per gradient element, the magnitude
+ * sum |terms| that scales the rounding error of a narrower evaluation.       */
+typedef struct {
+    double *dx;        /* [T][h] */
+    double *dw_router; /* [H][E][d] */
+    double *dw_gate;   /* [H*E][f][d] */
+    double *dw_up;     /* [H*E][f][d] (SwiGLU) */
+    double *dw_down;   /* [H*E][d][f] */
+    double *dsh_gate;  /* [f][h] */
+    double *dsh_up;    /* [f][h] */
+    double *dsh_down;  /* [h][f] */
+    double *dw_o;      /* [h][h] */
+    double *dlogits;   /* [T*H][E] */
+    double *dtopk_w;   /* [T*H*K] */
+} orc_grads;
+
+static double mabs(double v, int absm) { return absm ? fabs(v) : v; }
+
+static double sig_d(double a) { return 1.0 / (1.0 + exp(-a)); }
+
+/* activation value and derivative for one pre-activation pair */
+static void act_fwd_bwd(int act, double a, double u, double *hval, double *dh_da, double *dh_du)
+{
+    if (act == 0) {
+        double sg = sig_d(a), silu = a * sg;
+        *hval = silu * u;
+        *dh_da = u * sg * (1.0 + a * (1.0 - sg));
+        *dh_du = silu;
+    } else {
+        double phi = exp(-0.5 * a * a) / sqrt(8.0 * atan(1.0));
+        double Phi = 0.5 * (1.0 + erf(a / sqrt(2.0)));
+        *hval = a * Phi;
+        *dh_da = Phi + a * phi;
+        *dh_du = 0.0;
+    }
+}
+
+int orc_layer_backward(const orc_desc *d, const orc_weights *w, const void *x, const double *dy,
+                       double c_aux, int absm, orc_grads *gr)
+{
+    const int32_t T = d->T, h = d->h, H = d->H, E = d->E, K = d->K, f = d->f;
+    const int32_t dd = h / H, Et = H * E, dt = d->dtype;
+    const int64_t S = (int64_t)T * H, A = S * K;
+    if (H <= 0 || h % H != 0 || K <= 0 || K > E || E > 4096) return 1;
+    if (d->gate == 1 && K != 1) return 1;
+    const size_t wsz = dt == 1 ? 2 : 4;
+
+    /* ---- routing, as in the forward pass */
+    float *logits = (float *)calloc((size_t)(S * E + 1), sizeof(float));
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    double *wts = (double *)malloc(sizeof(double) * (size_t)(A + 1));
+    int32_t *cnt = (int32_t *)calloc((size_t)Et, sizeof(int32_t));
+    int32_t *kep = (int32_t *)calloc((size_t)Et, sizeof(int32_t));
+    int32_t *off = (int32_t *)calloc((size_t)Et + 1, sizeof(int32_t));
+    int32_t *dst = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    int32_t *src = (int32_t *)malloc(sizeof(int32_t) * (size_t)(A + 1));
+    double *psum = (double *)calloc((size_t)Et, sizeof(double));
+    int32_t nk = 0;
+    if (d->gate == 1) {
+        orc_hash_select(d, w->hash_keys, idx, wts, NULL);
+    } else {
+        orc_logits(d, x, w->w_router, logits);
+        orc_select(d, logits, w->logit_bias, w->select_bias, idx, wts, NULL, NULL, psum);
+    }
+    orc_permute(d, idx, orc_capacity(d), cnt, kep, off, dst, src, &nk);
+    int64_t *row_asg = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nk + 1));
+    for (int64_t a = 0; a < A; ++a)
+        if (dst[a] >= 0) row_asg[dst[a]] = a;
+
+    /* ---- per-row forward quantities of the routed experts */
+    const int nact = d->act == 0 ? 2 : 1;
+    double *ra = (double *)malloc(sizeof(double) * ((size_t)nk * f + 1));
+    double *ru = (double *)malloc(sizeof(double) * ((size_t)nk * f + 1));
+    double *rh = (double *)malloc(sizeof(double) * ((size_t)nk * f + 1));
+    double *ro = (double *)malloc(sizeof(double) * ((size_t)nk * dd + 1));
+    int64_t r;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (r = 0; r < nk; ++r) {
+        int64_t a = row_asg[r], s = a / K, t = s / H, g = s % H;
+        int64_t e = idx[a];
+        const char *w1 = (const char *)w->w_gate + (size_t)e * f * dd * wsz;
+        const char *w3 = nact == 2 ? (const char *)w->w_up + (size_t)e * f * dd * wsz : NULL;
+        const char *w2 = (const char *)w->w_down + (size_t)e * dd * f * wsz;
+        for (int32_t j = 0; j < f; ++j) {
+            double av = 0.0, uv = 0.0;
+            for (int32_t i = 0; i < dd; ++i) {
+                double xv = ld(x, dt, t * h + g * dd + i);
+                av += xv * ld(w1, dt, (int64_t)j * dd + i);
+                if (w3) uv += xv * ld(w3, dt, (int64_t)j * dd + i);
+            }
+            double hv, t1, t2;
+            act_fwd_bwd(d->act, av, uv, &hv, &t1, &t2);
+            ra[r * f + j] = av;
+            ru[r * f + j] = uv;
+            rh[r * f + j] = hv;
+        }
+        for (int32_t o = 0; o < dd; ++o) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < f; ++j) acc += rh[r * f + j] * ld(w2, dt, (int64_t)o * f + j);
+            ro[r * dd + o] = acc;
+        }
+    }
+
+    /* ---- shared expert forward (per token) */
+    double *sa = NULL, *su = NULL, *sh = NULL, *so = NULL;
+    if (d->n_shared > 0) {
+        sa = (double *)malloc(sizeof(double) * (size_t)T * f);
+        su = (double *)malloc(sizeof(double) * (size_t)T * f);
+        sh = (double *)malloc(sizeof(double) * (size_t)T * f);
+        so = (double *)malloc(sizeof(double) * (size_t)T * h);
+        int64_t t;
+#pragma omp parallel for schedule(dynamic, 4)
+        for (t = 0; t < T; ++t) {
+            for (int32_t j = 0; j < f; ++j) {
+                double av = 0.0, uv = 0.0;
+                for (int32_t i = 0; i < h; ++i) {
+                    double xv = ld(x, dt, t * h + i);
+                    av += xv * ld(w->sh_gate, dt, (int64_t)j * h + i);
+                    if (nact == 2) uv += xv * ld(w->sh_up, dt, (int64_t)j * h + i);
+                }
+                double hv, t1, t2;
+                act_fwd_bwd(d->act, av, uv, &hv, &t1, &t2);
+                sa[t * f + j] = av;
+                su[t * f + j] = uv;
+                sh[t * f + j] = hv;
+            }
+            for (int32_t o = 0; o < h; ++o) {
+                double acc = 0.0;
+                for (int32_t j = 0; j < f; ++j) acc += sh[t * f + j] * ld(w->sh_down, dt, (int64_t)o * f + j);
+                so[t * h + o] = acc;
+            }
+        }
+    }
+
+    /* ---- W_o: dcat = dy W_o, dW_o = dy^T cat (cat = the concatenated head outputs) */
+    double *dcat = (double *)malloc(sizeof(double) * (size_t)T * h);
+    if (d->has_wo) {
+        double *cat = (double *)calloc((size_t)T * h, sizeof(double));
+        for (int64_t a = 0; a < A; ++a) {
+            if (dst[a] < 0) continue;
+            int64_t s = a / K, t = s / H, g = s % H;
+            for (int32_t j = 0; j < dd; ++j) cat[t * h + g * dd + j] += wts[a] * ro[(int64_t)dst[a] * dd + j];
+        }
+        if (so)
+            for (int64_t i = 0; i < (int64_t)T * h; ++i) cat[i] += so[i];
+        int64_t t;
+#pragma omp parallel for schedule(static)
+        for (t = 0; t < T; ++t)
+            for (int32_t i = 0; i < h; ++i) {
+                double acc = 0.0;
+                for (int32_t q = 0; q < h; ++q)
+                    acc += mabs(dy[t * h + q], absm) * mabs(ld(w->w_o, dt, (int64_t)q * h + i), absm);
+                dcat[t * h + i] = acc;
+            }
+        if (gr->dw_o) {
+            int64_t q;
+#pragma omp parallel for schedule(static)
+            for (q = 0; q < h; ++q)
+                for (int32_t i = 0; i < h; ++i) {
+                    double acc = 0.0;
+                    for (int64_t t2 = 0; t2 < T; ++t2)
+                        acc += mabs(dy[t2 * h + q], absm) * mabs(cat[t2 * h + i], absm);
+                    gr->dw_o[q * h + i] = acc;
+                }
+        }
+        free(cat);
+    } else {
+        for (int64_t i = 0; i < (int64_t)T * h; ++i) dcat[i] = mabs(dy[i], absm);
+    }
+
+    /* ---- gate-weight gradients dw[a] = <dcat slice, o[row]> */
+    double *dw = (double *)calloc((size_t)(A + 1), sizeof(double));
+    for (int64_t a = 0; a < A; ++a) {
+        if (dst[a] < 0) continue;
+        int64_t s = a / K, t = s / H, g = s % H;
+        double acc = 0.0;
+        for (int32_t j = 0; j < dd; ++j)
+            acc += dcat[t * h + g * dd + j] * mabs(ro[(int64_t)dst[a] * dd + j], absm);
+        dw[a] = acc;
+    }
+    if (gr->dtopk_w) memcpy(gr->dtopk_w, dw, sizeof(double) * (size_t)A);
+
+    /* ---- routed experts backward, per row: dO = w dcat, dH = W2^T dO, da, du */
+    double *rda = (double *)malloc(sizeof(double) * ((size_t)nk * f + 1));
+    double *rdu = (double *)malloc(sizeof(double) * ((size_t)nk * f + 1));
+    double *rdo = (double *)malloc(sizeof(double) * ((size_t)nk * dd + 1));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (r = 0; r < nk; ++r) {
+        int64_t a = row_asg[r], s = a / K, t = s / H, g = s % H;
+        int64_t e = idx[a];
+        const char *w2 = (const char *)w->w_down + (size_t)e * dd * f * wsz;
+        for (int32_t o = 0; o < dd; ++o) rdo[r * dd + o] = mabs(wts[a], absm) * dcat[t * h + g * dd + o];
+        for (int32_t j = 0; j < f; ++j) {
+            double dh = 0.0;
+            for (int32_t o = 0; o < dd; ++o) dh += rdo[r * dd + o] * mabs(ld(w2, dt, (int64_t)o * f + j), absm);
+            double hv, t1, t2;
+            act_fwd_bwd(d->act, ra[r * f + j], ru[r * f + j], &hv, &t1, &t2);
+            rda[r * f + j] = dh * mabs(t1, absm);
+            rdu[r * f + j] = dh * mabs(t2, absm);
+        }
+    }
+    /* weight gradients, one expert per iteration (rows of an expert are contiguous) */
+    int64_t e;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (e = 0; e < Et; ++e) {
+        int64_t g = e / E;
+        for (int32_t o = 0; o < dd; ++o)
+            for (int32_t j = 0; j < f; ++j) {
+                double acc = 0.0;
+                for (int64_t rr = off[e]; rr < off[e + 1]; ++rr)
+                    acc += rdo[rr * dd + o] * mabs(rh[rr * f + j], absm);
+                if (gr->dw_down) gr->dw_down[(e * dd + o) * (int64_t)f + j] = acc;
+            }
+        for (int32_t j = 0; j < f; ++j)
+            for (int32_t i = 0; i < dd; ++i) {
+                double ag = 0.0, au = 0.0;
+                for (int64_t rr = off[e]; rr < off[e + 1]; ++rr) {
+                    int64_t t = (row_asg[rr] / K) / H;
+                    double xv = mabs(ld(x, dt, t * h + g * dd + i), absm);
+                    ag += rda[rr * f + j] * xv;
+                    au += rdu[rr * f + j] * xv;
+                }
+                if (gr->dw_gate) gr->dw_gate[(e * f + j) * (int64_t)dd + i] = ag;
+                if (gr->dw_up && nact == 2) gr->dw_up[(e * f + j) * (int64_t)dd + i] = au;
+            }
+    }
+
+    /* ---- router: dlogits from dw (+ the aux-loss term), per sub-token */
+    double *dl = (double *)calloc((size_t)(S * E + 1), sizeof(double));
+    if (d->gate == 0) {
+        double *fq = (double *)calloc((size_t)Et, sizeof(double));
+        double *pm = (double *)calloc((size_t)Et, sizeof(double));
+        for (int32_t q = 0; q < Et; ++q) {
+            fq[q] = (double)cnt[q] / ((double)T * K);
+            pm[q] = T > 0 ? psum[q] / (double)T : 0.0;
+        }
+        const double caux = c_aux * (double)d->alpha * (double)E / ((double)H * (double)T);
+        int64_t s;
+#pragma omp parallel for schedule(static)
+        for (s = 0; s < S; ++s) {
+            int64_t g = s % H;
+            double lp[4096], p[4096], sgv[4096];
+            for (int32_t q = 0; q < E; ++q)
+                lp[q] = (double)logits[s * E + q] + (w->logit_bias ? (double)w->logit_bias[g * E + q] : 0.0);
+            /* gate-weight part over the selected set */
+            double wdw = 0.0;
+            for (int32_t k = 0; k < K; ++k) wdw += mabs(wts[s * K + k], absm) * dw[s * K + k];
+            double ssel = 0.0;
+            if (d->score == 1)
+                for (int32_t k = 0; k < K; ++k) ssel += sig_d(lp[idx[s * K + k] - g * E]);
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t q = idx[s * K + k] - (int32_t)(g * E);
+                double diff = absm ? dw[s * K + k] + wdw : dw[s * K + k] - wdw;
+                if (d->score == 1) {
+                    double sq = sig_d(lp[q]);
+                    dl[s * E + q] += diff / ssel * sq * (1.0 - sq);
+                } else {
+                    dl[s * E + q] += mabs(wts[s * K + k], absm) * diff;
+                }
+            }
+            /* aux part: every expert of the head */
+            if (c_aux != 0.0) {
+                double tot = 0.0;
+                if (d->score == 1) {
+                    for (int32_t q = 0; q < E; ++q) { sgv[q] = sig_d(lp[q]); tot += sgv[q]; }
+                    for (int32_t q = 0; q < E; ++q) p[q] = sgv[q] / tot;
+                } else {
+                    double m = -INFINITY;
+                    for (int32_t q = 0; q < E; ++q) m = fmax(m, lp[q]);
+                    for (int32_t q = 0; q < E; ++q) { p[q] = exp(lp[q] - m); tot += p[q]; }
+                    for (int32_t q = 0; q < E; ++q) p[q] /= tot;
+                }
+                double fp = 0.0;
+                for (int32_t q = 0; q < E; ++q) fp += fq[g * E + q] * p[q];
+                for (int32_t q = 0; q < E; ++q) {
+                    double diff = absm ? fq[g * E + q] + fp : fq[g * E + q] - fp;
+                    double jac = d->score == 1 ? sgv[q] * (1.0 - sgv[q]) / tot : p[q];
+                    dl[s * E + q] += caux * jac * diff;
+                }
+            }
+        }
+        free(fq);
+        free(pm);
+        if (gr->dw_router) {
+            int64_t q;
+#pragma omp parallel for schedule(static)
+            for (q = 0; q < Et; ++q) {
+                int64_t g = q / E, ee = q % E;
+                for (int32_t i = 0; i < dd; ++i) {
+                    double acc = 0.0;
+                    for (int64_t t = 0; t < T; ++t)
+                        acc += dl[(t * H + g) * E + ee] * mabs(ld(x, dt, t * h + g * dd + i), absm);
+                    gr->dw_router[q * dd + i] = acc;
+                }
+            }
+        }
+    }
+    if (gr->dlogits) memcpy(gr->dlogits, dl, sizeof(double) * (size_t)(S * E));
+
+    /* ---- shared expert backward */
+    if (d->n_shared > 0) {
+        double *sda = (double *)malloc(sizeof(double) * (size_t)T * f);
+        double *sdu = (double *)malloc(sizeof(double) * (size_t)T * f);
+        int64_t t;
+#pragma omp parallel for schedule(static)
+        for (t = 0; t < T; ++t)
+            for (int32_t j = 0; j < f; ++j) {
+                double dh = 0.0;
+                for (int32_t o = 0; o < h; ++o) dh += dcat[t * h + o] * mabs(ld(w->sh_down, dt, (int64_t)o * f + j), absm);
+                double hv, t1, t2;
+                act_fwd_bwd(d->act, sa[t * f + j], su[t * f + j], &hv, &t1, &t2);
+                sda[t * f + j] = dh * mabs(t1, absm);
+                sdu[t * f + j] = dh * mabs(t2, absm);
+            }
+        int64_t q;
+#pragma omp parallel for schedule(static)
+        for (q = 0; q < h; ++q)
+            for (int32_t j = 0; j < f; ++j) {
+                double acc = 0.0;
+                for (int64_t t2 = 0; t2 < T; ++t2) acc += dcat[t2 * h + q] * mabs(sh[t2 * f + j], absm);
+                if (gr->dsh_down) gr->dsh_down[q * f + j] = acc;
+            }
+#pragma omp parallel for schedule(static)
+        for (q = 0; q < f; ++q)
+            for (int32_t i = 0; i < h; ++i) {
+                double ag = 0.0, au = 0.0;
+                for (int64_t t2 = 0; t2 < T; ++t2) {
+                    double xv = mabs(ld(x, dt, t2 * h + i), absm);
+                    ag += sda[t2 * f + q] * xv;
+                    au += sdu[t2 * f + q] * xv;
+                }
+                if (gr->dsh_gate) gr->dsh_gate[q * h + i] = ag;
+                if (gr->dsh_up && nact == 2) gr->dsh_up[q * h + i] = au;
+            }
+        /* shared part of dx */
+        if (gr->dx) {
+#pragma omp parallel for schedule(static)
+            for (t = 0; t < T; ++t)
+                for (int32_t i = 0; i < h; ++i) {
+                    double acc = 0.0;
+                    for (int32_t j = 0; j < f; ++j) {
+                        acc += sda[t * f + j] * mabs(ld(w->sh_gate, dt, (int64_t)j * h + i), absm);
+                        if (nact == 2) acc += sdu[t * f + j] * mabs(ld(w->sh_up, dt, (int64_t)j * h + i), absm);
+                    }
+                    gr->dx[t * h + i] = acc;
+                }
+        }
+        free(sda);
+        free(sdu);
+    } else if (gr->dx) {
+        for (int64_t i = 0; i < (int64_t)T * h; ++i) gr->dx[i] = 0.0;
+    }
+
+    /* ---- dx: routed experts (dX rows summed per sub-token) + router */
+    if (gr->dx) {
+        int64_t t;
+#pragma omp parallel for schedule(dynamic, 4)
+        for (t = 0; t < T; ++t) {
+            for (int32_t g = 0; g < H; ++g) {
+                int64_t s = t * H + g;
+                for (int32_t k = 0; k < K; ++k) {
+                    int64_t a = s * K + k;
+                    if (dst[a] < 0) continue;
+                    int64_t rr = dst[a], ee = idx[a];
+                    const char *w1 = (const char *)w->w_gate + (size_t)ee * f * dd * wsz;
+                    const char *w3 = nact == 2 ? (const char *)w->w_up + (size_t)ee * f * dd * wsz : NULL;
+                    for (int32_t i = 0; i < dd; ++i) {
+                        double acc = 0.0;
+                        for (int32_t j = 0; j < f; ++j) {
+                            acc += rda[rr * f + j] * mabs(ld(w1, dt, (int64_t)j * dd + i), absm);
+                            if (w3) acc += rdu[rr * f + j] * mabs(ld(w3, dt, (int64_t)j * dd + i), absm);
+                        }
+                        gr->dx[t * h + g * dd + i] += acc;
+                    }
+                }
+                if (d->gate == 0)
+                    for (int32_t i = 0; i < dd; ++i) {
+                        double acc = 0.0;
+                        for (int32_t q = 0; q < E; ++q)
+                            acc += dl[s * E + q] * mabs(ld(w->w_router, dt, ((int64_t)g * E + q) * dd + i), absm);
+                        gr->dx[t * h + g * dd + i] += acc;
+                    }
+            }
+        }
+    }
+
+    free(logits); free(idx); free(wts); free(cnt); free(kep); free(off); free(dst); free(src);
+    free(psum); free(row_asg); free(ra); free(ru); free(rh); free(ro); free(dcat); free(dw);
+    free(rda); free(rdu); free(rdo); free(dl);
+    free(sa); free(su); free(sh); free(so);
+    return 0;
+}

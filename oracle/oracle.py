@@ -46,6 +46,11 @@ class OrcWeights(C.Structure):
     ]
 
 
+class OrcGrads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dsh_gate", "dsh_up",
+                                          "dsh_down", "dw_o", "dlogits", "dtopk_w")]
+
+
 class OrcAux(C.Structure):
     _fields_ = [
         ("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("margin", C.c_void_p),
@@ -94,6 +99,9 @@ def lib():
         _lib.orc_layer_forward.argtypes = [C.POINTER(OrcDesc), C.POINTER(OrcWeights), C.c_void_p,
                                            C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                            C.POINTER(OrcAux)]
+        _lib.orc_layer_backward.restype = C.c_int
+        _lib.orc_layer_backward.argtypes = [C.POINTER(OrcDesc), C.POINTER(OrcWeights), C.c_void_p, C.c_void_p,
+                                            C.c_double, C.c_int, C.POINTER(OrcGrads)]
         _lib.orc_num_threads.restype = C.c_int
         _lib.orc_num_threads.argtypes = []
     return _lib
@@ -298,6 +306,59 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
     out["l_aux"] = float(out["l_aux"][0])
     out["y"] = y
     out["ymag"] = ymag
+    return out
+
+
+def _weights_struct(cfg, weights, keep):
+    el = _elem(cfg)
+
+    def ptr(name, dtype):
+        a = weights.get(name)
+        if a is None:
+            return None
+        a = _chk(a, dtype)
+        keep.append(a)
+        return a.ctypes.data
+
+    return OrcWeights(
+        w_router=ptr("w_router", el), logit_bias=ptr("logit_bias", np.float32),
+        select_bias=ptr("select_bias", np.float32), w_gate=ptr("w_gate", el),
+        w_up=ptr("w_up", el), w_down=ptr("w_down", el), sh_gate=ptr("sh_gate", el),
+        sh_up=ptr("sh_up", el), sh_down=ptr("sh_down", el), w_o=ptr("w_o", el),
+        hash_keys=ptr("hash_keys", np.int32),
+    )
+
+
+def layer_backward(cfg, weights, x, dy, c_aux=1.0, magnitude=False):
+    """Gradients of L = sum(dy * y) + c_aux * L_aux with respect to x and every
+    weight, in float64 (moe_oracle.c, orc_layer_backward).  With magnitude, the
+    same sums taken over absolute values (the scale of rounding errors).
+    Returns a dict with dx, dw_router, dw_gate, dw_up, dw_down, dsh_gate,
+    dsh_up, dsh_down, dw_o (None where the layer has no such weight), dlogits
+    [T*H, E] and dtopk_w [T*H, K]."""
+    d = desc(cfg)
+    S, Et, dd, f, h = d.T * d.H, d.H * d.E, d.h // d.H, d.f, d.h
+    keep = []
+    W = _weights_struct(cfg, weights, keep)
+    x = _chk(x, _elem(cfg))
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dy.shape == (d.T, h)
+    gated = cfg.get("act", "swiglu") != "gelu"
+    out = dict(
+        dx=np.zeros((d.T, h)), dw_router=np.zeros((d.H, d.E, dd)) if cfg.get("gate", "topk") != "hash" else None,
+        dw_gate=np.zeros((Et, f, dd)), dw_up=np.zeros((Et, f, dd)) if gated else None,
+        dw_down=np.zeros((Et, dd, f)),
+        dsh_gate=np.zeros((f, h)) if d.n_shared else None,
+        dsh_up=np.zeros((f, h)) if d.n_shared and gated else None,
+        dsh_down=np.zeros((h, f)) if d.n_shared else None,
+        dw_o=np.zeros((h, h)) if d.has_wo else None,
+        dlogits=np.zeros((S, d.E)), dtopk_w=np.zeros((S, d.K)),
+    )
+    G = OrcGrads(**{k: _p(v) for k, v in out.items()})
+    rc = lib().orc_layer_backward(C.byref(d), C.byref(W), _p(x), _p(dy), float(c_aux), int(bool(magnitude)),
+                                  C.byref(G))
+    if rc != 0:
+        raise ValueError("oracle rejected the layer description")
     return out
 
 
