@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the baseline sample")
     p.add_argument("--stage-reps", type=int, default=10)
+    p.add_argument("--train", action="store_true",
+                   help="time a training step instead: the training forward (it keeps what the backward "
+                        "reads) and moe_layer_backward of sum(dy * y) + L_aux")
     p.add_argument("--counters", action="store_true",
                    help="for rocprofv3 --pmc runs: a 1 GiB device copy (counter calibration), then the "
                         "dominant kernel three times; prints nothing else")
@@ -113,6 +116,98 @@ def traffic_from_profile(kernel_tag, workload):
         return None
 
 
+def train_bench(args, cfg, name, inp, desc, ws, y, stream):
+    """One training step = moe_layer_forward_train + moe_layer_backward on the
+    same batch; prints one JSON line (tokens per second of whole steps)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_45_amd as moe
+    T, h, H, E, K, f = cfg["T"], cfg["h"], cfg["H"], cfg["E"], cfg["K"], cfg["f"]
+    d = h // H
+    sv = moe.alloc_saved(desc)
+    gr = moe.alloc_grads(desc, inp, inp["x"])
+    wsb = moe.workspace(desc, moe.MOE_WS_BACKWARD)
+    dy = torch.randn((T, h), generator=torch.Generator(device="cuda").manual_seed(1), device="cuda").to(torch.bfloat16)
+    aux = dict(n_kept=torch.empty(1, dtype=torch.int32, device="cuda"))
+
+    def fwd():
+        moe.moe_layer_forward_train(desc, inp, inp["x"], y, sv, aux=aux, ws=ws)
+
+    def bwd():
+        moe.moe_layer_backward(desc, inp, inp["x"], dy, sv, gr, aux_weight=1.0, ws=wsb)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} training steps")
+    ms_step = timed(step, args.steps, stream)
+    fwd()
+    t_fwd = timed(fwd, args.stage_reps, stream)
+    t_bwd = timed(bwd, args.stage_reps, stream)
+    n_kept = int(aux["n_kept"].item())
+    n_act = 2 if cfg["act"] == "swiglu" else 1
+    ffn = 2.0 * (n_act + 1) * n_kept * d * f
+    router = 2.0 * T * H * E * d if cfg.get("gate", "topk") != "hash" else 0.0
+    fwd_flops = ffn + router
+    if cfg.get("n_shared"):
+        fwd_flops += 2.0 * (n_act + 1) * T * h * f
+    if cfg.get("has_wo"):
+        fwd_flops += 2.0 * T * h * h
+    # backward: an input-gradient and a weight-gradient product per forward product
+    bwd_flops = 2.0 * fwd_flops
+    bwd_tfs = bwd_flops / (t_bwd * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu:
+        from oracle import oracle as orc
+
+        def to_np(t):
+            if t is None:
+                return None
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+        host = {k: to_np(v) for k, v in inp.items()}
+        dyh = dy.float().cpu().numpy().astype(np.float64)
+        threads = orc.num_threads()
+        Ts, elapsed = 2, 0.0
+        while True:
+            t0 = time.perf_counter()
+            c = dict(cfg, T=Ts)
+            orc.layer_forward(c, host, host["x"][:Ts])
+            orc.layer_backward(c, host, host["x"][:Ts], dyh[:Ts], c_aux=1.0)
+            elapsed = time.perf_counter() - t0
+            if elapsed >= args.cpu_seconds * 0.6 or Ts >= T:
+                break
+            Ts = min(T, Ts * 4, max(Ts + 1, int(Ts * args.cpu_seconds / max(elapsed, 1e-3))))
+        log(f"[bench] oracle forward + backward: {Ts} tokens in {elapsed:.2f} s on {threads} threads")
+        cpu = {"value": Ts / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {Ts} tokens of the {name} batch as their own batch, full weights; fp64 C "
+                         f"oracle forward + backward, {elapsed:.1f} s"}
+    out = {
+        "metric": "MoE-layer fwd+bwd (training step) tokens/sec on 1 GPU",
+        "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg["dtype"], "data": "synthetic (seeded inputs, N(0,1) dy)",
+        "config": {"workload": name, "tokens": T, "hidden": h, "heads": H, "experts": E, "top_k": K, "ffn": f,
+                   "act": cfg["act"], "score": cfg["score"], "capacity_factor": cfg["capacity_factor"],
+                   "parallelism": "single GPU"},
+        "n_kept": n_kept,
+        "stages": {"forward_train_ms": t_fwd, "backward_ms": t_bwd,
+                   "forward_tflops": fwd_flops / (t_fwd * 1e-3) / 1e12, "backward_tflops": bwd_tfs},
+        "roofline": {"kernel": "whole backward pass (dgrad + wgrad grouped GEMMs, transposes, router)",
+                     "bound": "mfma", "achieved": bwd_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": bwd_tfs / MFMA_BF16_PEAK_TFS, "traffic": None, "flops_per_launch": bwd_flops,
+                     "launch_ms": t_bwd},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -150,6 +245,8 @@ def main():
     desc = moe.desc_from_cfg(cfg)
     ws = moe.workspace(desc)
     y = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev)
+    if args.train:
+        return train_bench(args, cfg, name, inp, desc, ws, y, stream)
     i32 = dict(dtype=torch.int32, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     aux = dict(topk_idx=torch.empty((T * H, K), **i32), topk_w=torch.empty((T * H, K), **f32),

@@ -122,7 +122,8 @@ typedef enum {
     MOE_WS_LAYER = 0, /* moe_layer_forward (also enough for every stage call) */
     MOE_WS_ROUTE = 1,
     MOE_WS_PERMUTE = 2,
-    MOE_WS_FFN = 3
+    MOE_WS_FFN = 3,
+    MOE_WS_BACKWARD = 4 /* moe_layer_backward */
 } moe_ws_kind;
 
 /* Expert capacity C = CF * K * T / E rounded up (CF = capacity_factor, or
@@ -272,6 +273,70 @@ typedef struct moe_aux {
  * Needs moe_workspace_size(MOE_WS_LAYER) bytes of workspace. */
 moe_status moe_layer_forward(const moe_desc *desc, const moe_weights *w, const void *x, void *y,
                              moe_aux *aux, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------ training
+ * Every page is about training these layers (lesson 10; "HAI-LLM MoE"): the
+ * backward pass of L = sum(dy * y) + aux_weight * L_aux, by the chain rule
+ * through the forward pass above.  Selection (top-K, group limit, capacity)
+ * is piecewise constant, so the router receives gradient only through the
+ * gate weights (softmax or sigmoid over the selected experts, dropped slots
+ * included) and through P_i of the aux loss (f_i is a count):
+ *   softmax: dl_j = w_j (dw_j - sum_k w_k dw_k) + c p_j (f_j - sum_i f_i p_i)
+ *   sigmoid: dl_j = (dw_j - sum_k w_k dw_k) / sum_S s * s_j (1 - s_j)
+ *                   + c s_j (1 - s_j) / sum_all s * (f_j - sum_i f_i p_i)
+ * with dw_k = <dy_t, expert output of slot k> (0 if dropped) and
+ * c = aux_weight * alpha * E / (H * T).  The hash gate has no router.
+ * Supported for MOE_BF16 with d = h/H, f and h multiples of 64.  Gradients
+ * are bf16 (fp32 accumulation, one rounding); the intermediate row gradients
+ * are bf16 as in the forward pass. */
+
+/* State a training forward leaves for the backward pass: device buffers the
+ * caller owns.  R = moe_max_rows(desc), n_act = 2 (SwiGLU) or 1 (GELU). */
+typedef struct moe_saved {
+    int32_t *topk_idx; /* [T*H][K] */
+    float *topk_w;     /* [T*H][K] */
+    int32_t *dest_row; /* [T*H*K] */
+    int32_t *src_token;/* [T*H*K] (first n_kept used) */
+    int32_t *offsets;  /* [H*E+1] */
+    int32_t *counts;   /* [H*E] assignments before drops */
+    float *logits;     /* [T*H][E] pre-bias router logits (unused by the hash gate) */
+    void *act_grad;    /* [R][n_act*f] local derivatives of the expert activation h at the
+                        * pre-activations a = x W_gate^T, u = x W_up^T: dh/da | dh/du
+                        * (SwiGLU: u silu'(a) | silu(a); GELU: gelu'(a)), from fp32 */
+    void *h;           /* [R][f] expert hidden activations */
+    void *y_perm;      /* [R][d] expert outputs */
+    void *sh_act_grad; /* [T][n_act*f] the same for the shared expert (n_shared) */
+    void *sh_h;        /* [T][f] shared expert hidden activations (n_shared) */
+    void *y_cat;       /* [T][h] combined output before W_o (has_wo) */
+} moe_saved;
+
+/* Gradients (device buffers, same shapes and dtype as the weights); every
+ * one the layer has must be given. */
+typedef struct moe_grads {
+    void *dx;          /* [T][h] */
+    void *w_router;    /* [H][E][d] (top-K gate) */
+    void *w_gate, *w_up, *w_down;
+    void *sh_gate, *sh_up, *sh_down;
+    void *w_o;
+} moe_grads;
+
+/* R: rows of the packed expert buffers, min(T*H*K, H*E*C); -1 if invalid. */
+int32_t moe_max_rows(const moe_desc *desc);
+
+/* moe_layer_forward that also fills `saved` (every field the layer uses must
+ * be non-NULL); the expert GEMMs then run on the 64-wide kernel.  Same
+ * workspace as moe_layer_forward. */
+moe_status moe_layer_forward_train(const moe_desc *desc, const moe_weights *w, const void *x, void *y,
+                                   moe_aux *aux, const moe_saved *saved, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/* Gradients of L = sum(dy * y) + aux_weight * L_aux for the batch that the
+ * training forward saved.  x [T][h] and the weights as in that call, dy
+ * [T][h].  Needs moe_workspace_size(MOE_WS_BACKWARD) bytes (it holds the
+ * transposed weights and the row gradients).  Deterministic. */
+moe_status moe_layer_backward(const moe_desc *desc, const moe_weights *w, const void *x, const void *dy,
+                              const moe_saved *saved, float aux_weight, moe_grads *grads, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *moe_status_string(moe_status s);

@@ -12,12 +12,14 @@ import ctypes as C
 from . import _ffi
 from ._ffi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FFN_GEMM1, MOE_FFN_GEMM2, MOE_GELU,  # noqa: F401
                    MOE_GATE_HASH, MOE_GATE_TOPK, MOE_QUEUE_CHOICE, MOE_QUEUE_TOKEN, MOE_LOGITS_IN, MOE_LOGITS_OUT, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU,
-                   MOE_WS_FFN, MOE_WS_LAYER, MOE_WS_PERMUTE, MOE_WS_ROUTE, MoeAux, MoeDesc,
-                   MoeWeights)
+                   MOE_WS_BACKWARD, MOE_WS_FFN, MOE_WS_LAYER, MOE_WS_PERMUTE, MOE_WS_ROUTE, MoeAux, MoeDesc,
+                   MoeGrads, MoeSaved, MoeWeights)
 
 __all__ = [
     "MoeError", "MoeDesc", "desc_from_cfg", "moe_capacity", "moe_workspace_size", "moe_route",
     "moe_route_hash", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_rows", "moe_combine", "moe_layer_forward", "moe_version", "lib",
+    "moe_max_rows", "moe_layer_forward_train", "moe_layer_backward", "SAVED_KEYS", "GRAD_KEYS",
+    "alloc_saved", "alloc_grads",
     "workspace",
 ]
 
@@ -151,3 +153,67 @@ def moe_layer_forward(desc, weights, x, y, aux=None, ws=None, stream=None):
     wp, wn = _ws(ws)
     _check(lib().moe_layer_forward(C.byref(desc), C.byref(W), _ptr(x), _ptr(y),
                                    C.byref(A) if A is not None else None, wp, wn, _stream(stream)))
+
+
+SAVED_KEYS = tuple(n for n, _ in MoeSaved._fields_)
+GRAD_KEYS = tuple(n for n, _ in MoeGrads._fields_)
+
+
+def moe_max_rows(desc):
+    return int(lib().moe_max_rows(C.byref(desc)))
+
+
+def moe_layer_forward_train(desc, weights, x, y, saved, aux=None, ws=None, stream=None):
+    """moe_layer_forward that also fills `saved` (dict with the keys of MoeSaved,
+    device tensors; see include/moe.h for their shapes)."""
+    W = MoeWeights(**{k: _ptr(weights.get(k)) for k in _WEIGHT_KEYS})
+    A = MoeAux(**{k: _ptr(aux.get(k)) for k in _AUX_KEYS}) if aux else None
+    Sv = MoeSaved(**{k: _ptr(saved.get(k)) for k in SAVED_KEYS})
+    wp, wn = _ws(ws)
+    _check(lib().moe_layer_forward_train(C.byref(desc), C.byref(W), _ptr(x), _ptr(y),
+                                         C.byref(A) if A is not None else None, C.byref(Sv), wp, wn,
+                                         _stream(stream)))
+
+
+def moe_layer_backward(desc, weights, x, dy, saved, grads, aux_weight=1.0, ws=None, stream=None):
+    """Gradients of sum(dy * y) + aux_weight * L_aux into `grads` (dict with the
+    keys of MoeGrads: dx and one buffer per weight the layer has)."""
+    W = MoeWeights(**{k: _ptr(weights.get(k)) for k in _WEIGHT_KEYS})
+    Sv = MoeSaved(**{k: _ptr(saved.get(k)) for k in SAVED_KEYS})
+    Gr = MoeGrads(**{k: _ptr(grads.get(k)) for k in GRAD_KEYS})
+    wp, wn = _ws(ws)
+    _check(lib().moe_layer_backward(C.byref(desc), C.byref(W), _ptr(x), _ptr(dy), C.byref(Sv), float(aux_weight),
+                                    C.byref(Gr), wp, wn, _stream(stream)))
+
+
+def alloc_saved(desc, device="cuda"):
+    """Device buffers for the state of a training forward (the fields of
+    MoeSaved that this layer uses), shaped as include/moe.h states."""
+    import torch
+    T, H, E, K, f, h = desc.T, desc.H, desc.E, desc.K, desc.f, desc.h
+    d, S, Et, R = h // H, T * H, H * E, max(moe_max_rows(desc), 1)
+    na = 1 if desc.act == MOE_GELU else 2
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    bf = dict(dtype=torch.bfloat16, device=device)
+    sv = dict(topk_idx=torch.empty((S, K), **i32), topk_w=torch.empty((S, K), **f32),
+              dest_row=torch.empty(S * K, **i32), src_token=torch.empty(S * K, **i32),
+              offsets=torch.empty(Et + 1, **i32), counts=torch.empty(Et, **i32),
+              logits=torch.empty((S, E), **f32), act_grad=torch.empty((R, na * f), **bf),
+              h=torch.empty((R, f), **bf), y_perm=torch.empty((R, d), **bf))
+    if desc.n_shared:
+        sv.update(sh_act_grad=torch.empty((T, na * f), **bf), sh_h=torch.empty((T, f), **bf))
+    if desc.has_wo:
+        sv["y_cat"] = torch.empty((T, h), **bf)
+    return sv
+
+
+def alloc_grads(desc, weights, x):
+    """Gradient buffers for moe_layer_backward: dx like x, and one like each
+    weight the layer has (the router's only with the top-K gate)."""
+    import torch
+    gr = {"dx": torch.empty_like(x)}
+    for k in ("w_router", "w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down", "w_o"):
+        if weights.get(k) is not None and not (k == "w_router" and desc.gate == MOE_GATE_HASH):
+            gr[k] = torch.empty_like(weights[k])
+    return gr

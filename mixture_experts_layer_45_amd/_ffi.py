@@ -17,7 +17,7 @@ MOE_GATE_TOPK, MOE_GATE_HASH = 0, 1
 MOE_QUEUE_TOKEN, MOE_QUEUE_CHOICE = 0, 1
 MOE_LOGITS_IN, MOE_LOGITS_OUT = 1, 2
 MOE_FFN_GEMM1, MOE_FFN_GEMM2 = 1, 2
-MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FFN = range(4)
+MOE_WS_LAYER, MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FFN, MOE_WS_BACKWARD = range(5)
 INT32_MAX = 2**31 - 1
 
 
@@ -49,6 +49,16 @@ class MoeAux(C.Structure):
     ]
 
 
+class MoeSaved(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_w", "dest_row", "src_token", "offsets", "counts",
+                                          "logits", "act_grad", "h", "y_perm", "sh_act_grad", "sh_h", "y_cat")]
+
+
+class MoeGrads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dx", "w_router", "w_gate", "w_up", "w_down", "sh_gate", "sh_up",
+                                          "sh_down", "w_o")]
+
+
 # exported symbol -> (restype, argtypes)
 _VP = C.c_void_p
 SIGNATURES = {
@@ -66,6 +76,11 @@ SIGNATURES = {
     "moe_combine": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, _VP, _VP, _VP]),
     "moe_layer_forward": (C.c_int, [C.POINTER(MoeDesc), C.POINTER(MoeWeights), _VP, _VP,
                                     C.POINTER(MoeAux), _VP, C.c_size_t, _VP]),
+    "moe_max_rows": (C.c_int32, [C.POINTER(MoeDesc)]),
+    "moe_layer_forward_train": (C.c_int, [C.POINTER(MoeDesc), C.POINTER(MoeWeights), _VP, _VP, C.POINTER(MoeAux),
+                                          C.POINTER(MoeSaved), _VP, C.c_size_t, _VP]),
+    "moe_layer_backward": (C.c_int, [C.POINTER(MoeDesc), C.POINTER(MoeWeights), _VP, _VP, C.POINTER(MoeSaved),
+                                     C.c_float, C.POINTER(MoeGrads), _VP, C.c_size_t, _VP]),
     "moe_status_string": (C.c_char_p, [C.c_int]),
     "moe_last_error": (C.c_char_p, []),
     "moe_version": (C.c_char_p, []),

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "backward.hip"]
 
 COMMON = [
     "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

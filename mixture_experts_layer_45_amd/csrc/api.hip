@@ -5,6 +5,8 @@
 // 256-byte aligned regions in a fixed order that moe_workspace_size() mirrors.
 #include <math.h>
 #include <stdarg.h>
+
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -169,6 +171,113 @@ LayerWs carve_layer(Carver& c, const Plan& p, const moe_desc* d) {
     return w;
 }
 
+// ---- backward pass: sizes and workspace
+struct BwdPlan {
+    int NA, Ep, ms_r, ms_d, ms_h;
+    long long Np_r, Np_d, Np_h;
+    bool router, shared, wo;
+};
+BwdPlan bwd_plan_of(const moe_desc* d, const Plan& p) {
+    BwdPlan b;
+    b.NA = d->act == MOE_SWIGLU ? 2 : 1;
+    b.Ep = (p.E + 63) / 64 * 64;
+    const int tst = (p.T + 63) / 64;
+    b.ms_r = (p.max_rows + 63) / 64 + p.Et;
+    b.ms_d = tst + 1;
+    b.ms_h = p.H * (tst + 1);
+    b.Np_r = 64ll * b.ms_r;
+    b.Np_d = 64ll * b.ms_d;
+    b.Np_h = 64ll * b.ms_h;
+    b.router = d->gate == MOE_GATE_TOPK;
+    b.shared = d->n_shared != 0;
+    b.wo = d->has_wo != 0;
+    return b;
+}
+
+struct BwdWs {
+    int2 *kspan_r, *kspan_d, *kspan_h;
+    int32_t *stage_r, *stage_d, *stage_h, *off_T, *off_h, *off_w, *off_f, *off_E, *off_hr, *off_fr;
+    void *w_downT, *w_guT, *wgT, *sh_downT, *sh_guT, *w_oT;
+    void *dcat, *dYp, *dAU, *dXp, *dl, *dxr, *dAUs, *dxs;
+    float* dw;
+    void *dYpT, *hT, *dAT, *dUT, *xpT, *dlT, *xhT, *dcatT, *shT, *dAsT, *dUsT, *xT, *dyT, *ycT;
+    GemmTile* tiles;
+};
+
+size_t bwd_tiles_bytes(const Plan& p, const BwdPlan& b) {
+    size_t m = 0;
+    auto upd = [&](int G, long long rows) { m = std::max(m, grouped_gemm_ws_bytes(G, (int)std::min(rows, (long long)INT32_MAX))); };
+    upd(p.Et, p.max_rows);
+    upd(p.Et, (long long)p.Et * p.d);
+    upd(p.Et, (long long)p.Et * p.f);
+    if (b.router) {
+        upd(p.H, (long long)p.H * p.T);
+        upd(p.H, (long long)p.H * p.E);
+    }
+    if (b.shared || b.wo) {
+        upd(1, p.T);
+        upd(1, p.h);
+        upd(1, p.f);
+    }
+    return m + 256;
+}
+
+BwdWs carve_bwd(Carver& c, const Plan& p, const BwdPlan& b) {
+    BwdWs w{};
+    const size_t e2 = 2;  // bf16
+    const size_t N = p.max_rows, T = p.T, S = (size_t)p.T * p.H, nf = (size_t)b.NA * p.f;
+    w.kspan_r = c.take<int2>(p.Et);
+    w.stage_r = c.take<int32_t>(b.ms_r);
+    w.kspan_d = c.take<int2>(1);
+    w.stage_d = c.take<int32_t>(b.ms_d);
+    w.kspan_h = c.take<int2>(p.H);
+    w.stage_h = c.take<int32_t>(b.ms_h);
+    w.off_T = c.take<int32_t>(2);
+    w.off_h = c.take<int32_t>(p.H + 1);
+    w.off_w = c.take<int32_t>(p.Et + 1);
+    w.off_f = c.take<int32_t>(p.Et + 1);
+    w.off_E = c.take<int32_t>(p.H + 1);
+    w.off_hr = c.take<int32_t>(2);
+    w.off_fr = c.take<int32_t>(2);
+    w.w_downT = c.take<char>((size_t)p.Et * p.f * p.d * e2);
+    w.w_guT = c.take<char>((size_t)p.Et * p.d * nf * e2);
+    w.dYp = c.take<char>(N * p.d * e2 + 16);
+    w.dw = c.take<float>((size_t)p.A + 1);
+    w.dAU = c.take<char>(N * nf * e2 + 16);
+    w.dXp = c.take<char>(N * p.d * e2 + 16);
+    w.dYpT = c.take<char>((size_t)p.d * b.Np_r * e2);
+    w.hT = c.take<char>((size_t)p.f * b.Np_r * e2);
+    w.dAT = c.take<char>((size_t)p.f * b.Np_r * e2);
+    if (b.NA == 2) w.dUT = c.take<char>((size_t)p.f * b.Np_r * e2);
+    w.xpT = c.take<char>((size_t)p.d * b.Np_r * e2);
+    if (b.router) {
+        w.wgT = c.take<char>((size_t)p.H * p.d * b.Ep * e2);
+        w.dl = c.take<char>(S * b.Ep * e2);
+        w.dxr = c.take<char>(S * p.d * e2 + 16);
+        w.dlT = c.take<char>((size_t)b.Ep * b.Np_h * e2);
+        w.xhT = c.take<char>((size_t)p.d * b.Np_h * e2);
+    }
+    if (b.wo) {
+        w.w_oT = c.take<char>((size_t)p.h * p.h * e2);
+        w.dcat = c.take<char>(T * p.h * e2 + 16);
+        w.dyT = c.take<char>((size_t)p.h * b.Np_d * e2);
+        w.ycT = c.take<char>((size_t)p.h * b.Np_d * e2);
+    }
+    if (b.shared) {
+        w.sh_downT = c.take<char>((size_t)p.f * p.h * e2);
+        w.sh_guT = c.take<char>((size_t)p.h * nf * e2);
+        w.dAUs = c.take<char>(T * nf * e2 + 16);
+        w.dxs = c.take<char>(T * p.h * e2 + 16);
+        w.dcatT = c.take<char>((size_t)p.h * b.Np_d * e2);
+        w.shT = c.take<char>((size_t)p.f * b.Np_d * e2);
+        w.dAsT = c.take<char>((size_t)p.f * b.Np_d * e2);
+        if (b.NA == 2) w.dUsT = c.take<char>((size_t)p.f * b.Np_d * e2);
+        w.xT = c.take<char>((size_t)p.h * b.Np_d * e2);
+    }
+    w.tiles = c.take<GemmTile>(bwd_tiles_bytes(p, b) / sizeof(GemmTile) + 1);
+    return w;
+}
+
 moe_status check_ws(void* ws, size_t have, size_t need) {
     if (need == 0) return MOE_OK;
     if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -184,6 +293,7 @@ size_t ws_bytes_of(const moe_desc* d, int kind) {
         case MOE_WS_ROUTE: carve_route(c, p); break;
         case MOE_WS_PERMUTE: carve_permute(c, p); break;
         case MOE_WS_FFN: carve_ffn(c, p, d->dtype); break;
+        case MOE_WS_BACKWARD: carve_bwd(c, p, bwd_plan_of(d, p)); break;
         default: carve_layer(c, p, d); break;
     }
     return c.off + 256;
@@ -218,7 +328,7 @@ moe_status moe_workspace_size(const moe_desc* d, int32_t kind, size_t* bytes) {
     moe_status s = check_desc(d);
     if (s != MOE_OK) return s;
     if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-    if (kind < MOE_WS_LAYER || kind > MOE_WS_FFN) return fail(MOE_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
+    if (kind < MOE_WS_LAYER || kind > MOE_WS_BACKWARD) return fail(MOE_ERR_INVALID_ARG, "unknown workspace kind %d", kind);
     *bytes = ws_bytes_of(d, kind);
     return MOE_OK;
 }
@@ -371,9 +481,8 @@ moe_status moe_combine(const moe_desc* d, const int32_t* dest_row, const float* 
     return MOE_OK;
 }
 
-moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void* x, void* y, moe_aux* aux,
-                             void* ws, size_t ws_bytes, void* stream) {
-    g_err[0] = 0;
+static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const void* x, void* y, moe_aux* aux,
+                                const moe_saved* sv, void* ws, size_t ws_bytes, void* stream) {
     moe_status s = check_desc(d);
     if (s != MOE_OK) return s;
     if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
@@ -391,10 +500,22 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
     hipStream_t st = (hipStream_t)stream;
     Carver c(ws);
     LayerWs L = carve_layer(c, p, d);
-    int32_t* topk_idx = aux && aux->topk_idx ? aux->topk_idx : L.topk_idx;
-    float* topk_w = aux && aux->topk_w ? aux->topk_w : L.topk_w;
-    int32_t* dest_row = aux && aux->dest_row ? aux->dest_row : L.dest_row;
-    int32_t* counts = aux && aux->counts ? aux->counts : L.counts;
+    if (sv) {  // training: the state the backward pass reads lands in the caller's buffers
+        L.topk_idx = sv->topk_idx;
+        L.topk_w = sv->topk_w;
+        L.dest_row = sv->dest_row;
+        L.src_token = sv->src_token;
+        L.offsets = sv->offsets;
+        L.counts = sv->counts;
+        L.h_tmp = sv->h;
+        L.y_perm = sv->y_perm;
+        if (d->n_shared) L.h_sh = sv->sh_h;
+        if (d->has_wo) L.y_cat = sv->y_cat;
+    }
+    int32_t* topk_idx = aux && aux->topk_idx && !sv ? aux->topk_idx : L.topk_idx;
+    float* topk_w = aux && aux->topk_w && !sv ? aux->topk_w : L.topk_w;
+    int32_t* dest_row = aux && aux->dest_row && !sv ? aux->dest_row : L.dest_row;
+    int32_t* counts = aux && aux->counts && !sv ? aux->counts : L.counts;
     const bool want_stats = aux && (aux->f || aux->P || aux->l_aux || aux->kept || aux->n_kept || aux->n_dropped);
     hipError_t e;
 
@@ -408,9 +529,9 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
         RouteArgs ra{};
         ra.T = p.T; ra.h = p.h; ra.H = p.H; ra.E = p.E; ra.K = p.K; ra.dtype = d->dtype; ra.score = d->score;
         ra.n_groups = d->n_groups > 1 ? d->n_groups : 1; ra.group_limit = d->group_limit;
-        ra.flags = 0; ra.x = x; ra.w_router = w->w_router; ra.logit_bias = w->logit_bias;
+        ra.flags = sv ? MOE_LOGITS_OUT : 0; ra.x = x; ra.w_router = w->w_router; ra.logit_bias = w->logit_bias;
         ra.select_bias = d->score == MOE_SIGMOID ? w->select_bias : nullptr;
-        ra.logits = nullptr; ra.topk_idx = topk_idx; ra.topk_w = topk_w; ra.counts = nullptr;
+        ra.logits = sv ? sv->logits : nullptr; ra.topk_idx = topk_idx; ra.topk_w = topk_w; ra.counts = nullptr;
         ra.prob_part = want_stats ? L.prob_part : nullptr;
         if ((e = launch_route(ra, st)) != hipSuccess) return dev_fail(e, "route kernel");
         if (want_stats && (e = launch_prob_mean(L.prob_part, p.route_nbx, p.H, p.E, p.T, L.prob_mean, st)) != hipSuccess)
@@ -430,6 +551,7 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
     fa.x_perm = x; fa.src_rows = L.src_token; fa.a_nrows = p.T * p.H;
     fa.offsets = L.offsets; fa.w_gate = w->w_gate; fa.w_up = w->w_up;
     fa.w_down = w->w_down; fa.h_tmp = L.h_tmp; fa.y_perm = L.y_perm; fa.flags = 0; fa.tiles = L.tiles;
+    fa.act_save = sv ? sv->act_grad : nullptr;
     if ((e = launch_ffn(fa, st)) != hipSuccess) return dev_fail(e, "grouped ffn kernels");
 
     if (d->n_shared) {
@@ -438,6 +560,7 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
         sa.G = 1; sa.d = p.h; sa.f = p.f; sa.dtype = d->dtype; sa.act = d->act; sa.max_rows = p.T;
         sa.x_perm = x; sa.offsets = L.off_sh; sa.w_gate = w->sh_gate; sa.w_up = w->sh_up;
         sa.w_down = w->sh_down; sa.h_tmp = L.h_sh; sa.y_perm = L.y_sh; sa.flags = 0; sa.tiles = L.tiles_sh;
+        sa.act_save = sv ? sv->sh_act_grad : nullptr;
         if ((e = launch_ffn(sa, st)) != hipSuccess) return dev_fail(e, "shared expert kernels");
     }
 
@@ -459,6 +582,202 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
         sa.n_dropped = aux->n_dropped; sa.kept_out = aux->kept;
         if ((e = launch_stats(sa, st)) != hipSuccess) return dev_fail(e, "stats kernel");
     }
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void* x, void* y, moe_aux* aux,
+                             void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    return layer_forward(d, w, x, y, aux, nullptr, ws, ws_bytes, stream);
+}
+
+int32_t moe_max_rows(const moe_desc* d) {
+    if (check_desc(d) != MOE_OK) return -1;
+    return plan_of(d).max_rows;
+}
+
+// the training path runs its expert GEMMs on the 64-wide kernel: bf16 with
+// every contraction length a multiple of 64
+static moe_status check_training(const moe_desc* d) {
+    moe_status s = check_desc(d);
+    if (s != MOE_OK) return s;
+    if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "training needs MOE_BF16");
+    const int dd = d->h / d->H;
+    if (dd % 64 || d->f % 64 || d->h % 64)
+        return fail(MOE_ERR_UNSUPPORTED, "training needs d = %d, f = %d and h = %d to be multiples of 64", dd, d->f, d->h);
+    return MOE_OK;
+}
+
+static moe_status check_saved(const moe_desc* d, const moe_saved* sv) {
+    if (!sv) return fail(MOE_ERR_INVALID_ARG, "saved is NULL");
+    if (!sv->topk_idx || !sv->topk_w || !sv->dest_row || !sv->src_token || !sv->offsets || !sv->counts ||
+        !sv->act_grad || !sv->h || !sv->y_perm)
+        return fail(MOE_ERR_INVALID_ARG, "a routing or expert buffer of saved is NULL");
+    if (d->gate == MOE_GATE_TOPK && !sv->logits) return fail(MOE_ERR_INVALID_ARG, "saved->logits is NULL");
+    if (d->n_shared && (!sv->sh_act_grad || !sv->sh_h)) return fail(MOE_ERR_INVALID_ARG, "saved shared-expert buffer is NULL");
+    if (d->has_wo && !sv->y_cat) return fail(MOE_ERR_INVALID_ARG, "saved->y_cat is NULL");
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward_train(const moe_desc* d, const moe_weights* w, const void* x, void* y, moe_aux* aux,
+                                   const moe_saved* saved, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    moe_status s = check_training(d);
+    if (s != MOE_OK) return s;
+    if (d->T == 0) return MOE_OK;
+    if ((s = check_saved(d, saved)) != MOE_OK) return s;
+    return layer_forward(d, w, x, y, aux, saved, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const void* x, const void* dy,
+                              const moe_saved* sv, float aux_weight, moe_grads* gr, void* ws, size_t ws_bytes,
+                              void* stream) {
+    g_err[0] = 0;
+    moe_status s = check_training(d);
+    if (s != MOE_OK) return s;
+    if (d->T == 0) return MOE_OK;
+    if (!w || !x || !dy || !gr) return fail(MOE_ERR_INVALID_ARG, "weights, x, dy or grads is NULL");
+    if ((s = check_saved(d, sv)) != MOE_OK) return s;
+    if (!(aux_weight == aux_weight)) return fail(MOE_ERR_INVALID_ARG, "aux_weight is NaN");
+    const bool router = d->gate == MOE_GATE_TOPK;
+    if (!w->w_gate || !w->w_down || (d->act == MOE_SWIGLU && !w->w_up) || (router && !w->w_router))
+        return fail(MOE_ERR_INVALID_ARG, "a routed-expert or router weight is NULL");
+    if (d->n_shared && (!w->sh_gate || !w->sh_down || (d->act == MOE_SWIGLU && !w->sh_up)))
+        return fail(MOE_ERR_INVALID_ARG, "a shared-expert weight is NULL");
+    if (d->has_wo && !w->w_o) return fail(MOE_ERR_INVALID_ARG, "w_o is NULL");
+    if (!gr->dx || !gr->w_gate || !gr->w_down || (d->act == MOE_SWIGLU && !gr->w_up) || (router && !gr->w_router) ||
+        (d->n_shared && (!gr->sh_gate || !gr->sh_down || (d->act == MOE_SWIGLU && !gr->sh_up))) ||
+        (d->has_wo && !gr->w_o))
+        return fail(MOE_ERR_INVALID_ARG, "a gradient buffer of the layer is NULL");
+    const Plan p = plan_of(d);
+    const BwdPlan b = bwd_plan_of(d, p);
+    // the 64-wide kernel addresses each operand through a 32-bit buffer range
+    const long long lim = 1ll << 31;
+    const long long nf = (long long)b.NA * p.f;
+    if ((long long)p.f * b.Np_r * 2 >= lim || (long long)p.d * b.Np_r * 2 >= lim || (long long)p.max_rows * nf * 2 >= lim ||
+        (long long)p.max_rows * p.d * 2 >= lim || (long long)p.f * p.d * 2 >= lim || (long long)p.d * nf * 2 >= lim ||
+        (long long)b.Ep * b.Np_h * 2 >= lim || (long long)p.d * b.Np_h * 2 >= lim || (long long)p.h * b.Np_d * 2 >= lim ||
+        (long long)p.f * b.Np_d * 2 >= lim || (long long)p.T * p.h * 2 >= lim)
+        return fail(MOE_ERR_UNSUPPORTED, "an operand of the backward GEMMs exceeds 2 GB");
+    const size_t need = ws_bytes_of(d, MOE_WS_BACKWARD);
+    if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Carver c(ws);
+    BwdWs W = carve_bwd(c, p, b);
+    hipError_t e;
+#define MOE_TRY(call, what) \
+    if ((e = (call)) != hipSuccess) return dev_fail(e, what)
+    const int T = p.T, H = p.H, E = p.E, K = p.K, dd = p.d, f = p.f, h = p.h, Et = p.Et, N = p.max_rows;
+    const int NA = b.NA;
+    auto gemm = [&](int mode, const void* A, long long a_bytes, const void* B0, const void* B1, void* C, void* aux,
+                    int Kc, int Nout, const int32_t* offs, int G, int rows, const int2* kspan, int a_mod,
+                    int b_shared, const int32_t* a_rows) -> hipError_t {
+        GemmSpec gs{};
+        gs.A = A; gs.B0 = B0; gs.B1 = B1; gs.C = C; gs.aux = aux; gs.K = Kc; gs.Nout = Nout; gs.a_bytes = a_bytes;
+        gs.a_rows = a_rows; gs.kspan = kspan; gs.a_mod = a_mod; gs.b_shared = b_shared;
+        return launch_grouped_gemm(mode, gs, offs, G, rows, W.tiles, st);
+    };
+    // ---- group tables
+    MOE_TRY(launch_set2(W.off_T, 0, T, st), "offsets");
+    MOE_TRY(launch_set2(W.off_hr, 0, h, st), "offsets");
+    MOE_TRY(launch_set2(W.off_fr, 0, f, st), "offsets");
+    MOE_TRY(launch_iota(W.off_h, H, T, st), "offsets");
+    MOE_TRY(launch_iota(W.off_w, Et, dd, st), "offsets");
+    MOE_TRY(launch_iota(W.off_f, Et, f, st), "offsets");
+    MOE_TRY(launch_iota(W.off_E, H, E, st), "offsets");
+    MOE_TRY(launch_kspan(sv->offsets, Et, b.ms_r, W.kspan_r, W.stage_r, st), "row-block table");
+    MOE_TRY(launch_kspan(W.off_T, 1, b.ms_d, W.kspan_d, W.stage_d, st), "row-block table");
+    MOE_TRY(launch_kspan(W.off_h, H, b.ms_h, W.kspan_h, W.stage_h, st), "row-block table");
+    // ---- weights with the other index contiguous
+    MOE_TRY(launch_transpose_batched(w->w_down, Et, dd, f, W.w_downT, dd, 0, st), "transpose");
+    MOE_TRY(launch_transpose_batched(w->w_gate, Et, f, dd, W.w_guT, NA * f, 0, st), "transpose");
+    if (NA == 2) MOE_TRY(launch_transpose_batched(w->w_up, Et, f, dd, W.w_guT, NA * f, f, st), "transpose");
+    const void* dc = dy;
+    // ---- W_o: dcat = dy W_o, dW_o = dy^T y_cat
+    if (b.wo) {
+        MOE_TRY(launch_transpose_batched(w->w_o, 1, h, h, W.w_oT, h, 0, st), "transpose");
+        MOE_TRY(gemm(GEMM_PLAIN, dy, (long long)T * h * 2, W.w_oT, nullptr, W.dcat, nullptr, h, h, W.off_T, 1, T,
+                     nullptr, 0, 0, nullptr), "W_o dgrad");
+        MOE_TRY(launch_row_blocks(dy, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.dyT, b.Np_d, st),
+                "row blocks");
+        MOE_TRY(launch_row_blocks(sv->y_cat, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.ycT,
+                                  b.Np_d, st), "row blocks");
+        MOE_TRY(gemm(GEMM_PLAIN, W.dyT, (long long)h * b.Np_d * 2, W.ycT, nullptr, gr->w_o, nullptr, (int)b.Np_d, h,
+                     W.off_hr, 1, h, W.kspan_d, 0, 1, nullptr), "W_o wgrad");
+        dc = W.dcat;
+    }
+    // ---- combine: dYp = w dcat, dw = <dcat, y_perm>
+    MOE_TRY(launch_combine_bwd(dc, H, dd, K, p.A, sv->dest_row, sv->topk_w, sv->y_perm, W.dYp, W.dw, st), "combine bwd");
+    // ---- routed experts
+    MOE_TRY(gemm(NA == 2 ? GEMM_DSWIGLU : GEMM_DGELU, W.dYp, (long long)N * dd * 2, W.w_downT, nullptr, W.dAU,
+                 sv->act_grad, dd, f, sv->offsets, Et, N, nullptr, 0, 0, nullptr), "expert down dgrad");
+    MOE_TRY(gemm(GEMM_PLAIN, W.dAU, (long long)N * nf * 2, W.w_guT, nullptr, W.dXp, nullptr, (int)nf, dd, sv->offsets,
+                 Et, N, nullptr, 0, 0, nullptr), "expert gate/up dgrad");
+    MOE_TRY(launch_row_blocks(W.dYp, dd, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, dd, W.dYpT,
+                              b.Np_r, st), "row blocks");
+    MOE_TRY(launch_row_blocks(sv->h, f, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f, W.hT, b.Np_r,
+                              st), "row blocks");
+    MOE_TRY(launch_row_blocks(W.dAU, (int)nf, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f, W.dAT,
+                              b.Np_r, st), "row blocks");
+    if (NA == 2)
+        MOE_TRY(launch_row_blocks(W.dAU, (int)nf, f, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f,
+                                  W.dUT, b.Np_r, st), "row blocks");
+    MOE_TRY(launch_row_blocks(x, dd, 0, 0, sv->src_token, T * H, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, dd,
+                              W.xpT, b.Np_r, st), "row blocks");
+    MOE_TRY(gemm(GEMM_PLAIN, W.dYpT, (long long)dd * b.Np_r * 2, W.hT, nullptr, gr->w_down, nullptr, (int)b.Np_r, f,
+                 W.off_w, Et, Et * dd, W.kspan_r, dd, 1, nullptr), "expert down wgrad");
+    MOE_TRY(gemm(GEMM_PLAIN, W.dAT, (long long)f * b.Np_r * 2, W.xpT, nullptr, gr->w_gate, nullptr, (int)b.Np_r, dd,
+                 W.off_f, Et, Et * f, W.kspan_r, f, 1, nullptr), "expert gate wgrad");
+    if (NA == 2)
+        MOE_TRY(gemm(GEMM_PLAIN, W.dUT, (long long)f * b.Np_r * 2, W.xpT, nullptr, gr->w_up, nullptr, (int)b.Np_r, dd,
+                     W.off_f, Et, Et * f, W.kspan_r, f, 1, nullptr), "expert up wgrad");
+    // ---- router: through the gate weights and the aux loss
+    if (router) {
+        const float caux = aux_weight * d->aux_alpha * (float)E / ((float)H * (float)T);
+        MOE_TRY(launch_transpose_batched(w->w_router, H, E, dd, W.wgT, b.Ep, 0, st), "transpose");
+        MOE_TRY(launch_router_bwd(T, H, E, K, b.Ep, d->score, caux, sv->logits, w->logit_bias, sv->topk_idx, sv->topk_w,
+                                  W.dw, sv->counts, W.dl, st), "router bwd");
+        MOE_TRY(gemm(GEMM_PLAIN, W.dl, (long long)H * T * b.Ep * 2, W.wgT, nullptr, W.dxr, nullptr, b.Ep, dd, W.off_h, H,
+                     H * T, nullptr, 0, 0, nullptr), "router dgrad");
+        MOE_TRY(launch_row_blocks(W.dl, b.Ep, 0, 0, nullptr, H * T, 0, W.off_h, W.kspan_h, W.stage_h, b.ms_h, b.Ep, W.dlT,
+                                  b.Np_h, st), "row blocks");
+        MOE_TRY(launch_row_blocks(x, h, 0, dd, nullptr, T, 1, W.off_h, W.kspan_h, W.stage_h, b.ms_h, dd, W.xhT, b.Np_h,
+                                  st), "row blocks");
+        MOE_TRY(gemm(GEMM_PLAIN, W.dlT, (long long)b.Ep * b.Np_h * 2, W.xhT, nullptr, gr->w_router, nullptr,
+                     (int)b.Np_h, dd, W.off_E, H, H * E, W.kspan_h, E, 1, nullptr), "router wgrad");
+    }
+    // ---- shared expert (H = 1)
+    if (b.shared) {
+        MOE_TRY(launch_transpose_batched(w->sh_down, 1, h, f, W.sh_downT, h, 0, st), "transpose");
+        MOE_TRY(launch_transpose_batched(w->sh_gate, 1, f, h, W.sh_guT, (int)nf, 0, st), "transpose");
+        if (NA == 2) MOE_TRY(launch_transpose_batched(w->sh_up, 1, f, h, W.sh_guT, (int)nf, f, st), "transpose");
+        MOE_TRY(gemm(NA == 2 ? GEMM_DSWIGLU : GEMM_DGELU, dc, (long long)T * h * 2, W.sh_downT, nullptr, W.dAUs,
+                     sv->sh_act_grad, h, f, W.off_T, 1, T, nullptr, 0, 0, nullptr), "shared down dgrad");
+        MOE_TRY(gemm(GEMM_PLAIN, W.dAUs, (long long)T * nf * 2, W.sh_guT, nullptr, W.dxs, nullptr, (int)nf, h, W.off_T,
+                     1, T, nullptr, 0, 0, nullptr), "shared gate/up dgrad");
+        MOE_TRY(launch_row_blocks(dc, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.dcatT, b.Np_d,
+                                  st), "row blocks");
+        MOE_TRY(launch_row_blocks(sv->sh_h, f, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f, W.shT,
+                                  b.Np_d, st), "row blocks");
+        MOE_TRY(launch_row_blocks(W.dAUs, (int)nf, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f, W.dAsT,
+                                  b.Np_d, st), "row blocks");
+        if (NA == 2)
+            MOE_TRY(launch_row_blocks(W.dAUs, (int)nf, f, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f,
+                                      W.dUsT, b.Np_d, st), "row blocks");
+        MOE_TRY(launch_row_blocks(x, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.xT, b.Np_d, st),
+                "row blocks");
+        MOE_TRY(gemm(GEMM_PLAIN, W.dcatT, (long long)h * b.Np_d * 2, W.shT, nullptr, gr->sh_down, nullptr, (int)b.Np_d, f,
+                     W.off_hr, 1, h, W.kspan_d, 0, 1, nullptr), "shared down wgrad");
+        MOE_TRY(gemm(GEMM_PLAIN, W.dAsT, (long long)f * b.Np_d * 2, W.xT, nullptr, gr->sh_gate, nullptr, (int)b.Np_d, h,
+                     W.off_fr, 1, f, W.kspan_d, 0, 1, nullptr), "shared gate wgrad");
+        if (NA == 2)
+            MOE_TRY(gemm(GEMM_PLAIN, W.dUsT, (long long)f * b.Np_d * 2, W.xT, nullptr, gr->sh_up, nullptr, (int)b.Np_d,
+                         h, W.off_fr, 1, f, W.kspan_d, 0, 1, nullptr), "shared up wgrad");
+    }
+    // ---- dx
+    MOE_TRY(launch_dx(W.dXp, sv->dest_row, T, H, dd, K, router ? W.dxr : nullptr, b.shared ? W.dxs : nullptr, gr->dx, st),
+            "dx");
+#undef MOE_TRY
     return MOE_OK;
 }
 

@@ -101,9 +101,31 @@ struct FfnArgs {
     void* y_perm;
     uint32_t flags;
     GemmTile* tiles;  // ws: tile table
+    void* act_save;   // training: GEMM1 also stores its pre-activations here [max_rows][n_act*f], or null
 };
 size_t ffn_workspace_bytes(int G, int max_rows, int dtype);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st);
+
+// One grouped bf16 GEMM on the 64-wide kernel: C[rows][Nout] = A[rows][K] B_g^T
+// with group g owning rows [offsets[g], offsets[g+1]).  K % 64 == 0.
+enum GemmMode { GEMM_SWIGLU = 0, GEMM_GELU = 1, GEMM_PLAIN = 2, GEMM_SWIGLU_SAVE = 3, GEMM_GELU_SAVE = 4,
+                GEMM_DSWIGLU = 5, GEMM_DGELU = 6 };
+struct GemmSpec {
+    const void* A;          // [rows][K], or [a_mod][K] shared by the groups
+    const void* B0;         // [G][Nout][K], or [Nout][K] with b_shared
+    const void* B1;         // gated modes: the up weights, like B0
+    void* C;                // [rows][Nout] ([rows][2*Nout] for GEMM_DSWIGLU)
+    void* aux;              // SAVE / D modes: pre-activations [rows][n_act*Nout]
+    int K, Nout;
+    long long a_bytes;      // bytes of A the loads may address
+    const int32_t* a_rows;  // optional row map of A
+    const int2* kspan;      // optional per-group {first k stage, k stages}
+    int a_mod;              // > 0: tile row r reads A row r % a_mod
+    int b_shared;           // 1: one B for all groups
+};
+size_t grouped_gemm_ws_bytes(int G, int max_rows);  // its tile table
+hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offsets, int G, int max_rows,
+                               GemmTile* tiles, hipStream_t st);
 // Dense GEMM y[rows][n] = x[rows][k] W^T with W [n][k] (one group; used for W_o).
 hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const void* w, void* y,
                         GemmTile* tiles, int32_t* offsets2, hipStream_t st);
@@ -133,6 +155,23 @@ struct StatsArgs {
     int32_t* kept_out;
 };
 hipError_t launch_stats(const StatsArgs& a, hipStream_t st);
+
+// backward pass (backward.hip)
+hipError_t launch_kspan(const int32_t* offsets, int G, int max_stages, int2* kspan, int32_t* stage_grp,
+                        hipStream_t st);
+hipError_t launch_row_blocks(const void* in, int ld_in, int col0, int gcol, const int32_t* rowmap, int nrows_in,
+                             int local_rows, const int32_t* offsets, const int2* kspan, const int32_t* stage_grp,
+                             int max_stages, int ncols, void* out, long long ld_out, hipStream_t st);
+hipError_t launch_transpose_batched(const void* in, int B, int R, int Cc, void* out, int ld_out, int out_col0,
+                                    hipStream_t st);
+hipError_t launch_iota(int32_t* out, int n, int step, hipStream_t st);
+hipError_t launch_combine_bwd(const void* dcat, int H, int d, int K, int A, const int32_t* dest_row,
+                              const float* topk_w, const void* y_perm, void* dYp, float* dw, hipStream_t st);
+hipError_t launch_router_bwd(int T, int H, int E, int K, int Ep, int score, float caux, const float* logits,
+                             const float* logit_bias, const int32_t* topk_idx, const float* topk_w, const float* dw,
+                             const int32_t* counts, void* dl, hipStream_t st);
+hipError_t launch_dx(const void* dXp, const int32_t* dest_row, int T, int H, int d, int K, const void* dxr,
+                     const void* dxs, void* dx, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 hipError_t launch_set2(int32_t* p, int32_t a, int32_t b, hipStream_t st);
 

@@ -25,7 +25,23 @@
 
 namespace moe {
 
-enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_PLAIN = 2 };
+// Epilogue modes.  The forward FFN uses SWIGLU/GELU (GEMM1) and PLAIN (GEMM2).
+// Training and the backward pass add, on the 64-wide kernel only:
+//   SWIGLU_SAVE / GELU_SAVE  GEMM1 that also stores the activation's local
+//                            derivatives to `aux` [rows][n_act*Nout]: for
+//                            h = silu(a) u, dh/da = u silu'(a) at column j and
+//                            dh/du = silu(a) at Nout + j; for h = gelu(a),
+//                            gelu'(a).  They are computed in fp32 from the fp32
+//                            accumulators and rounded once, so the backward
+//                            never differentiates a rounded pre-activation
+//                            (silu' changes sign near a = -1.28, where that
+//                            would lose every digit);
+//   DSWIGLU / DGELU          a plain product dH whose epilogue multiplies it by
+//                            those derivatives: da = dH dh/da, du = dH dh/du,
+//                            stored to C [rows][n_act*Nout].
+enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_PLAIN = 2, MODE_SWIGLU_SAVE = 3, MODE_GELU_SAVE = 4, MODE_DSWIGLU = 5,
+       MODE_DGELU = 6 };
+__host__ __device__ constexpr bool gated_mode(int m) { return m == MODE_SWIGLU || m == MODE_SWIGLU_SAVE; }
 
 // tile-claim counters after the tile table's header: 4 GemmTile entries = 16
 // counters, 8 (one per XCD) for each of the two GEMM launches sharing a table
@@ -107,10 +123,16 @@ struct GArgs {
     int32_t* claim;     // 8 zeroed tile-claim counters for this launch (persistent kernels)
     float* partial;     // fp32 partial tiles of the split last round (64-wide kernel), or null
     const int32_t* a_rows;  // row map: tile row i reads row a_rows[i] of A (null: row i)
+    // 64-wide kernel only:
+    void* aux;              // pre-activations: written by the SAVE modes, read by the D modes
+    const int2* kspan;      // per group {first 64-wide k stage, k stages}, or null (0, K/64)
+    int a_mod;              // > 0: tile row r reads A row r % a_mod (every group reads the same rows)
+    int b_shared;           // 1: every group reads B0 itself (no per-group weight offset)
 };
 
 // the A row behind tile row r, clamped to the nrows rows of A
 __device__ __forceinline__ int a_row(const GArgs& a, int r, int nrows) {
+    if (a.a_mod > 0) return r % a.a_mod;
     if (!a.a_rows) return r;
     return min(max(a.a_rows[r], 0), nrows - 1);
 }
@@ -414,15 +436,119 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // v_permlane32_swap per register pair so that every lane stores 8 consecutive
 // outputs (16 bytes).  C gives the wave tile (TM x TN 32x32 tiles, WM rows,
 // WNM columns per matrix).
+// Lane's 8 consecutive fp32 results of half pp of a 32x32 tile (columns
+// 16pp + 8*(lane/32) + 0..7 of the tile), gathered with the same lane swap.
+__device__ __forceinline__ void row8(const floatx16& v, int pp, float* e) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[8 * pp + j]), __float_as_uint(v[8 * pp + 4 + j]),
+                                                        false, false);
+        e[j] = __uint_as_float(s[0]);
+        e[4 + j] = __uint_as_float(s[1]);
+    }
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(u32x4 v, float* e) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        e[2 * j] = __uint_as_float(v[j] << 16);
+        e[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ u32x4 f32_to_bf16x8(const float* e) {
+    return u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+}
+
+// silu'(a) = sigma(a) (1 + a (1 - sigma(a))); gelu'(a) = Phi(a) + a phi(a)
+__device__ __forceinline__ float sigma_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ __forceinline__ float dgelu_f(float a) {
+    return 0.5f * (1.0f + erf_as(a * 0.70710678118654752f)) + a * 0.39894228040143268f * __expf(-0.5f * a * a);
+}
+
+// Stores one 32x32 tile (tm, tn) of a wave's output block as bf16 rows of ld
+// elements at column offset coff (the same lane swap as the epilogue below).
+template <typename C>
+__device__ __forceinline__ void store_tile_rows(const floatx16& v, int tm, int tn, int row0, int row_end, int n0,
+                                                int Nout, uint8_t* base, int ld, int coff, int wm, int wn, int lane) {
+    const bool hi = lane >= 32;
+    const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+    for (int pp = 0; pp < 2; ++pp) {
+        uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+        uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
+        const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+        if (row < row_end && col < Nout) *(u32x4*)(base + ((size_t)row * ld + coff + col) * 2) = o;
+    }
+}
+
 template <typename C, int MODE>
 __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
-                                                  int wm, int wn, int lane) {
-    if constexpr (MODE == MODE_SWIGLU) {
+                                                  int wm, int wn, int lane, uint8_t* aux = nullptr) {
+    if constexpr (MODE == MODE_DSWIGLU || MODE == MODE_DGELU) {
+        // acc holds dH; aux the saved pre-activations; C gets da (and du)
+        constexpr int NA = MODE == MODE_DSWIGLU ? 2 : 1;
+        const int ld = NA * Nout;
+        const bool hi = lane >= 32;
+#pragma clang loop unroll(full)
+        for (int tm = 0; tm < C::TM; ++tm) {
+            const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+            for (int tn = 0; tn < C::TN; ++tn) {
+#pragma clang loop unroll(full)
+                for (int pp = 0; pp < 2; ++pp) {
+                    float g[8];
+                    row8(acc[tm * C::TN + tn], pp, g);
+                    const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+                    if (row < row_end && col < Nout) {
+                        const size_t at = ((size_t)row * ld + col) * 2;
+#pragma unroll
+                        for (int m = 0; m < NA; ++m) {
+                            float dv[8];
+                            bf16x8_to_f32(*(const u32x4*)(aux + at + (size_t)m * Nout * 2), dv);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) dv[j] *= g[j];
+                            *(u32x4*)(Cp + at + (size_t)m * Nout * 2) = f32_to_bf16x8(dv);
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
+    if constexpr (MODE == MODE_SWIGLU_SAVE) {
+        // dh/da and dh/du of h = silu(a) u, one 32x32 tile at a time
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t) {
+            floatx16 ga, gu;
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) {
+                const float a = acc[t][i], u = acc[C::TM * C::TN + t][i];
+                const float sg = sigma_f(a);
+                ga[i] = u * (sg * (1.0f + a * (1.0f - sg)));
+                gu[i] = a * sg;
+            }
+            store_tile_rows<C>(ga, t / C::TN, t % C::TN, row0, row_end, n0, Nout, aux, 2 * Nout, 0, wm, wn, lane);
+            store_tile_rows<C>(gu, t / C::TN, t % C::TN, row0, row_end, n0, Nout, aux, 2 * Nout, Nout, wm, wn, lane);
+        }
+    } else if constexpr (MODE == MODE_GELU_SAVE) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < C::TM * C::TN; ++t) {
+            floatx16 ga;
+#pragma clang loop unroll(full)
+            for (int i = 0; i < 16; ++i) ga[i] = dgelu_f(acc[t][i]);
+            store_tile_rows<C>(ga, t / C::TN, t % C::TN, row0, row_end, n0, Nout, aux, Nout, 0, wm, wn, lane);
+        }
+    }
+    if constexpr (gated_mode(MODE)) {
 #pragma clang loop unroll(full)
         for (int t = 0; t < C::TM * C::TN; ++t)
 #pragma clang loop unroll(full)
             for (int i = 0; i < 16; ++i) acc[t][i] = act_silu(acc[t][i]) * acc[C::TM * C::TN + t][i];
-    } else if constexpr (MODE == MODE_GELU) {
+    } else if constexpr (MODE == MODE_GELU || MODE == MODE_GELU_SAVE) {
 #pragma clang loop unroll(full)
         for (int t = 0; t < C::TM * C::TN; ++t)
 #pragma clang loop unroll(full)
@@ -661,8 +787,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
 // consecutive bf16 (16 bytes) -- two stores per 32x32 tile instead of sixteen.
 template <int BM, int MODE>
 struct K64Cfg {
-    static constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
-    static constexpr int BNM = MODE == MODE_SWIGLU ? 128 : 256;  // output columns per matrix
+    static constexpr int NMAT = gated_mode(MODE) ? 2 : 1;
+    static constexpr int BNM = gated_mode(MODE) ? 128 : 256;  // output columns per matrix
     static constexpr int WM = BM / 2;
     static constexpr int WNM = BNM / 4;
     static constexpr int TM = WM / 32;
@@ -757,8 +883,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
-        const uint8_t* B0 = (const uint8_t*)a.B0 + (size_t)tl.group * Nout * rowbytes;
-        const uint8_t* B1 = MODE == MODE_SWIGLU ? (const uint8_t*)a.B1 + (size_t)tl.group * Nout * rowbytes : B0;
+        if (a.kspan) {  // the group's own k range (no split pieces are made then)
+            const int2 ks = a.kspan[tl.group];
+            t.kb = ks.x;
+            t.nkl = ks.y;
+        }
+        const size_t bgo = a.b_shared ? 0 : (size_t)tl.group * Nout * rowbytes;
+        const uint8_t* B0 = (const uint8_t*)a.B0 + bgo;
+        const uint8_t* B1 = gated_mode(MODE) ? (const uint8_t*)a.B1 + bgo : B0;
         t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
         const int lr = lane >> 3, pc = lane & 7;
 #pragma unroll
@@ -885,7 +1017,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         if (cur.slot >= 0)
             k64_store_partial<BM, MODE>(acc, a.partial, cur.slot, tid);
         else
-            rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane);
+            rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane,
+                                                      (uint8_t*)a.aux);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -930,7 +1063,8 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
                 for (int i = 0; i < 4; ++i) acc[ai][4 * q4 + i] += v[i];
             }
     }
-    rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, tl.row0, tl.row_end, nt * C::BNM, a.Nout, (uint8_t*)a.C, wave >> 2, wave & 3, lane);
+    rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, tl.row0, tl.row_end, nt * C::BNM, a.Nout, (uint8_t*)a.C, wave >> 2, wave & 3, lane,
+                                              (uint8_t*)a.aux);
 }
 
 
@@ -1089,6 +1223,41 @@ static hipError_t run_gemm(int dtype, int BM, int mode, const GArgs& g, hipStrea
     return run_f32<MODE_PLAIN>(g, st);
 }
 
+// the 64-wide kernel alone, without split tail tiles (the training and
+// backward modes, per-group k ranges)
+template <int BM, int MODE>
+static hipError_t run_k64_only(GArgs g, hipStream_t st) {
+    using R = K64Cfg<BM, MODE>;
+    g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+    g.total = g.m_tiles * g.n_tiles;
+    g.per_xcd = (g.total + 7) / 8;
+    g.partial = nullptr;
+    if (g.total == 0) return hipSuccess;
+    const long long b_bytes = (long long)g.Nout * g.K * 2;
+    if (g.a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31) || g.K % 64 != 0 || g.Nout % 8 != 0 ||
+        ((uintptr_t)g.C & 15) != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+    return hipGetLastError();
+}
+
+static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st) {
+#define MOE_K64_CASE(M)                                                         \
+    case M:                                                                     \
+        return BM == 256 ? run_k64_only<256, M>(g, st) : run_k64_only<128, M>(g, st);
+    switch (mode) {
+        MOE_K64_CASE(MODE_SWIGLU)
+        MOE_K64_CASE(MODE_GELU)
+        MOE_K64_CASE(MODE_PLAIN)
+        MOE_K64_CASE(MODE_SWIGLU_SAVE)
+        MOE_K64_CASE(MODE_GELU_SAVE)
+        MOE_K64_CASE(MODE_DSWIGLU)
+        MOE_K64_CASE(MODE_DGELU)
+    }
+#undef MOE_K64_CASE
+    return hipErrorInvalidValue;
+}
+
 static hipError_t build_tiles(const int32_t* offsets, int G, int BM, int max_rows, int max_tiles,
                               GemmTile* tiles, hipStream_t st) {
     hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, st, offsets, G, BM, max_rows, max_tiles, tiles);
@@ -1117,7 +1286,12 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         const int esz = f.dtype == MOE_BF16 ? 2 : 4;
         g.a_bytes = f.src_rows ? (long long)f.a_nrows * f.d * esz : (long long)f.max_rows * f.d * esz;
         g.a_rows = f.src_rows;
-        err = run_gemm(f.dtype, BM, f.act == MOE_SWIGLU ? MODE_SWIGLU : MODE_GELU, g, st);
+        if (f.act_save) {  // training: also keep the pre-activations for the backward pass
+            g.aux = f.act_save;
+            err = run_k64_mode(BM, f.act == MOE_SWIGLU ? MODE_SWIGLU_SAVE : MODE_GELU_SAVE, g, st);
+        } else {
+            err = run_gemm(f.dtype, BM, f.act == MOE_SWIGLU ? MODE_SWIGLU : MODE_GELU, g, st);
+        }
         if (err != hipSuccess) return err;
     }
     if (fl & MOE_FFN_GEMM2) {
@@ -1165,6 +1339,36 @@ hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const 
     g.Nout = n;
     g.a_bytes = (long long)rows * k * (dtype == MOE_BF16 ? 2 : 4);
     return run_gemm(dtype, BM, MODE_PLAIN, g, st);
+}
+
+size_t grouped_gemm_ws_bytes(int G, int max_rows) {
+    return table_bytes(pick_bm(MOE_BF16, G, max_rows), G, max_rows);
+}
+
+hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offsets, int G, int max_rows,
+                               GemmTile* tiles, hipStream_t st) {
+    if (max_rows <= 0 || G <= 0) return hipSuccess;
+    const int BM = pick_bm(MOE_BF16, G, max_rows);
+    const int mtiles = max_m_tiles(BM, G, max_rows);
+    hipError_t err = build_tiles(offsets, G, BM, max_rows, mtiles, tiles, st);
+    if (err != hipSuccess) return err;
+    GArgs g{};
+    g.A = s.A;
+    g.B0 = s.B0;
+    g.B1 = s.B1;
+    g.C = s.C;
+    g.aux = s.aux;
+    g.tiles = tiles;
+    g.claim = (int32_t*)(tiles + mtiles + 1);
+    g.m_tiles = mtiles;
+    g.K = s.K;
+    g.Nout = s.Nout;
+    g.a_bytes = s.a_bytes;
+    g.a_rows = s.a_rows;
+    g.kspan = s.kspan;
+    g.a_mod = s.a_mod;
+    g.b_shared = s.b_shared;
+    return run_k64_mode(BM, mode, g, st);
 }
 
 hipError_t launch_set2(int32_t* p, int32_t a, int32_t b, hipStream_t st) {

@@ -1,0 +1,138 @@
+"""Parity of the backward pass (training forward + moe_layer_backward, through
+the C ABI) with the oracle's backward (pinned by central differences).
+
+Gradients are bf16 with fp32 accumulation; the path rounds dcat (W_o layers),
+the rows w_k dy, the saved activation derivatives and hidden rows, da/du, the rows'
+input gradients and the router gradient to bf16 before the last products, each
+a relative error of at most 2^-9 of its value.  Each one moves a gradient
+element by at most 2^-9 times the sum of the absolute values of the terms
+behind it, which the oracle returns as the magnitude M (magnitude mode).  With
+at most six such roundings on a path the bound is
+    |g_gpu - g_ref| <= ulp_bf16(g)/2 + 3 * 2^-8 * M.
+Routing is compared first and must agree exactly (these inputs have no top-K
+margin within reach of the router GEMM's fp32 error)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_45_amd as moe
+from mixture_experts_layer_45_amd import inputs
+from oracle import oracle as orc
+from tests import _gpu as G
+from tests._np_ref import to_np
+
+pytestmark = pytest.mark.gpu
+
+BWD_MAG = 3.0 * 2.0 ** -8
+CASES = {
+    "top2_swiglu": ("top2_e8_h4096", dict(T=600, h=512, f=320)),
+    "top2_drops_choice": ("top2_e8_h4096", dict(T=600, h=512, f=320, capacity_factor=0.8, queue="choice")),
+    "sigmoid_shared": ("sigmoid_top8_e256_shared", dict(T=96, h=256, f=128)),
+    "sigmoid_shared_grouped": ("sigmoid_top8_e256_shared", dict(T=160, h=256, f=128, n_groups=8, group_limit=4)),
+    "switch_gelu_zipf": ("switch_top1_e64_zipf", dict(T=1000, h=128, f=256)),
+    "multihead_wo": ("multihead_h8_e32_top4", dict(T=300, h=512, f=128)),
+    "hash_switch": ("switch_top1_e64_zipf", dict(T=1000, h=128, f=256, gate="hash")),
+}
+
+
+def alloc_saved(cfg):
+    return moe.alloc_saved(moe.desc_from_cfg(cfg), G.DEV)
+
+
+def alloc_grads(cfg, inp):
+    gr = moe.alloc_grads(moe.desc_from_cfg(cfg), inp, inp["x"])
+    for t in gr.values():
+        t.fill_(7.0)  # every element must be written
+    return gr
+
+
+def run_train(cfg, inp, dy, aux_weight):
+    d = moe.desc_from_cfg(cfg)
+    y = torch.empty_like(inp["x"])
+    sv = alloc_saved(cfg)
+    moe.moe_layer_forward_train(d, inp, inp["x"], y, sv, ws=moe.workspace(d))
+    gr = alloc_grads(cfg, inp)
+    moe.moe_layer_backward(d, inp, inp["x"], dy, sv, gr, aux_weight=aux_weight,
+                           ws=moe.workspace(d, moe.MOE_WS_BACKWARD))
+    torch.cuda.synchronize()
+    return y, sv, gr
+
+
+ORACLE_KEY = {"dx": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up", "w_down": "dw_down",
+              "sh_gate": "dsh_gate", "sh_up": "dsh_up", "sh_down": "dsh_down", "w_o": "dw_o"}
+
+
+def _check(case, aux_weight, zero_dy=False):
+    name, over = CASES[case]
+    cfg = inputs.variant(name, **over)
+    G.log(f"[backward] {case} aux_weight={aux_weight} zero_dy={zero_dy}")
+    inp = G.dev_inputs(cfg)
+    g = torch.Generator().manual_seed(21)
+    dy_h = torch.zeros((cfg["T"], cfg["h"])) if zero_dy else torch.randn((cfg["T"], cfg["h"]), generator=g)
+    dy = dy_h.to(torch.bfloat16)
+    y, sv, gr = run_train(cfg, inp, dy.to(G.DEV), aux_weight)
+    host = G.np_inputs(inp)
+    fwd = orc.layer_forward(cfg, host, host["x"])
+    # routing of the training forward = the oracle's
+    assert np.array_equal(sv["topk_idx"].cpu().numpy(), fwd["topk_idx"])
+    assert np.array_equal(sv["dest_row"].cpu().numpy(), fwd["dest_row"])
+    # the training forward's output within the forward bound
+    G.assert_close(G.host(y), fwd["y"], cfg["dtype"], f"y {case}", mag=fwd["ymag"])
+    dyn = dy.float().numpy().astype(np.float64)
+    ref = orc.layer_backward(cfg, host, host["x"], dyn, c_aux=aux_weight)
+    mag = orc.layer_backward(cfg, host, host["x"], dyn, c_aux=aux_weight, magnitude=True)
+    for k, t in gr.items():
+        rk = ORACLE_KEY[k]
+        st = G.assert_close(G.host(t).reshape(ref[rk].shape), ref[rk], "bf16", f"{k} {case}", mag=mag[rk],
+                            mag_unit=BWD_MAG / G.MAG_FACTOR, rms_bound=1e-2)
+        G.log(f"   {k}: {st}")
+    return cfg, inp, dy, gr
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_backward_matches_oracle(case):
+    _check(case, aux_weight=1.0)
+
+
+@pytest.mark.parametrize("case", ["top2_swiglu", "sigmoid_shared", "multihead_wo", "switch_gelu_zipf"])
+def test_backward_aux_loss_alone(case):
+    """dy = 0: only aux_weight * L_aux remains; it reaches the router and x
+    only, and the expert weight gradients are exactly zero."""
+    cfg, inp, dy, gr = _check(case, aux_weight=1e3, zero_dy=True)
+    for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down", "w_o"):
+        if k in gr:
+            assert not gr[k].any(), k
+    assert gr["w_router"].abs().max() > 0
+
+
+def test_backward_deterministic():
+    name, over = CASES["sigmoid_shared_grouped"]
+    cfg = inputs.variant(name, **over)
+    inp = G.dev_inputs(cfg)
+    dy = torch.randn((cfg["T"], cfg["h"]), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(G.DEV)
+    _, _, g1 = run_train(cfg, inp, dy, 1.0)
+    _, _, g2 = run_train(cfg, inp, dy, 1.0)
+    for k in g1:
+        assert torch.equal(g1[k].view(torch.int16), g2[k].view(torch.int16)), k
+
+
+def test_training_forward_matches_forward():
+    """The training forward gives the forward pass's routing bit for bit and an
+    output within the same bound."""
+    name, over = CASES["top2_drops_choice"]
+    cfg = inputs.variant(name, **over)
+    inp = G.dev_inputs(cfg)
+    y0, aux = G.run_layer(cfg, inp)
+    d = moe.desc_from_cfg(cfg)
+    y1 = torch.empty_like(y0)
+    sv = alloc_saved(cfg)
+    moe.moe_layer_forward_train(d, inp, inp["x"], y1, sv, ws=moe.workspace(d))
+    torch.cuda.synchronize()
+    assert torch.equal(sv["topk_idx"], aux["topk_idx"]) and torch.equal(sv["dest_row"], aux["dest_row"])
+    # the inference GEMMs may split a short last round of tiles along K (another
+    # fp32 summation order, so other roundings of the expert rows): both outputs
+    # are held to the forward bound against the oracle
+    host = G.np_inputs(inp)
+    ref = orc.layer_forward(cfg, host, host["x"])
+    for yy in (y0, y1):
+        G.assert_close(G.host(yy), ref["y"], cfg["dtype"], "y", mag=ref["ymag"])
