@@ -119,15 +119,17 @@ Plan plan_of(const moe_desc* d) {
     p.cap = capacity_of(d);
     const int64_t byc = p.cap >= INT32_MAX ? (int64_t)p.A : (int64_t)p.Et * p.cap;
     p.max_rows = (int)(byc < p.A ? byc : p.A);
-    p.route_nbx = route_blocks(d->T, d->E, d->dtype);
+    p.route_nbx = route_blocks(d->T, d->h, d->H, d->E, d->dtype);
     p.nch = permute_chunks(p.A);
     return p;
 }
 
-struct RouteWs { float* prob_part; };
-RouteWs carve_route(Carver& c, const Plan& p) {
+struct RouteWs { float* prob_part; void* split; };
+RouteWs carve_route(Carver& c, const Plan& p, int dtype) {
     RouteWs w;
     w.prob_part = c.take<float>((size_t)p.H * p.route_nbx * p.E + 1);
+    const size_t sb = route_split_ws_bytes(p.T, p.h, p.H, p.E, dtype);
+    w.split = sb ? c.take<char>(sb) : nullptr;
     return w;
 }
 int32_t* carve_permute(Carver& c, const Plan& p) { return c.take<int32_t>((size_t)p.nch * p.Et + 1); }
@@ -140,6 +142,7 @@ struct LayerWs {
     float *topk_w, *prob_part, *prob_mean;
     GemmTile *tiles, *tiles_sh, *tiles_wo;
     void *h_tmp, *y_perm, *h_sh, *y_sh, *y_cat;
+    void* route_split;
 };
 
 LayerWs carve_layer(Carver& c, const Plan& p, const moe_desc* d) {
@@ -148,6 +151,10 @@ LayerWs carve_layer(Carver& c, const Plan& p, const moe_desc* d) {
     w.topk_w = c.take<float>((size_t)p.A + 1);
     w.counts = c.take<int32_t>(p.Et);
     w.prob_part = c.take<float>((size_t)p.H * p.route_nbx * p.E + 1);
+    {
+        const size_t sb = route_split_ws_bytes(p.T, p.h, p.H, p.E, d->dtype);
+        w.route_split = sb ? c.take<char>(sb) : nullptr;
+    }
     w.prob_mean = c.take<float>(p.Et);
     w.kept = c.take<int32_t>(p.Et);
     w.offsets = c.take<int32_t>(p.Et + 1);
@@ -290,7 +297,7 @@ size_t ws_bytes_of(const moe_desc* d, int kind) {
     const Plan p = plan_of(d);
     Carver c(nullptr);
     switch (kind) {
-        case MOE_WS_ROUTE: carve_route(c, p); break;
+        case MOE_WS_ROUTE: carve_route(c, p, d->dtype); break;
         case MOE_WS_PERMUTE: carve_permute(c, p); break;
         case MOE_WS_FFN: carve_ffn(c, p, d->dtype); break;
         case MOE_WS_BACKWARD: carve_bwd(c, p, bwd_plan_of(d, p)); break;
@@ -351,10 +358,13 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
     if (!topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "topk_idx or topk_w is NULL");
     const Plan p = plan_of(d);
     const size_t need = ws_bytes_of(d, MOE_WS_ROUTE);
-    if (prob_mean && (s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
+    // a workspace is needed for P and for the split router GEMM of many experts
+    const bool need_ws = prob_mean || route_split_ws_bytes(p.T, p.h, p.H, p.E, d->dtype) > 0;
+    if (need_ws && (s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     Carver c(ws);
-    RouteWs w = prob_mean ? carve_route(c, p) : RouteWs{nullptr};
+    RouteWs w = need_ws ? carve_route(c, p, d->dtype) : RouteWs{nullptr, nullptr};
+    if (!prob_mean) w.prob_part = nullptr;
     hipError_t e;
     if (counts && (e = launch_fill_i32(counts, p.Et, 0, st)) != hipSuccess) return dev_fail(e, "fill");
     RouteArgs a{};
@@ -363,6 +373,7 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
     a.flags = flags; a.x = x; a.w_router = w_router; a.logit_bias = logit_bias;
     a.select_bias = d->score == MOE_SIGMOID ? select_bias : nullptr;
     a.logits = logits; a.topk_idx = topk_idx; a.topk_w = topk_w; a.counts = counts; a.prob_part = w.prob_part;
+    a.split_ws = w.split;
     if ((e = launch_route(a, st)) != hipSuccess) return dev_fail(e, "route kernel");
     if (prob_mean && (e = launch_prob_mean(w.prob_part, p.route_nbx, p.H, p.E, p.T, prob_mean, st)) != hipSuccess)
         return dev_fail(e, "prob_mean kernel");
@@ -533,6 +544,7 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
         ra.select_bias = d->score == MOE_SIGMOID ? w->select_bias : nullptr;
         ra.logits = sv ? sv->logits : nullptr; ra.topk_idx = topk_idx; ra.topk_w = topk_w; ra.counts = nullptr;
         ra.prob_part = want_stats ? L.prob_part : nullptr;
+        ra.split_ws = L.route_split;
         if ((e = launch_route(ra, st)) != hipSuccess) return dev_fail(e, "route kernel");
         if (want_stats && (e = launch_prob_mean(L.prob_part, p.route_nbx, p.H, p.E, p.T, L.prob_mean, st)) != hipSuccess)
             return dev_fail(e, "prob_mean kernel");

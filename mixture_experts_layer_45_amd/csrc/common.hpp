@@ -51,8 +51,13 @@ struct RouteArgs {
     float* topk_w;
     int32_t* counts;      // may be null
     float* prob_part;     // [n_blocks][H*E] partial sums of the score distribution, may be null
+    void* split_ws;       // route_split_ws_bytes() of workspace for the split-K router GEMM, or null
+    const float* logit_parts;  // internal: [n_parts][T][E] partial logits to sum (fixed order)
+    int n_parts;
 };
-int route_blocks(int T, int E, int dtype);  // route blocks per head (= rows of prob_part per head)
+// workspace of the split-K router GEMM (0 where that path does not apply)
+size_t route_split_ws_bytes(int T, int h, int H, int E, int dtype);
+int route_blocks(int T, int h, int H, int E, int dtype);  // route blocks per head (= rows of prob_part per head)
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 // hash gate: topk_idx/topk_w [T*H] (K = 1); counts (may be null) accumulated
 hipError_t launch_route_hash(const int32_t* keys, int T, int H, int E, int32_t* topk_idx, float* topk_w,
@@ -109,7 +114,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t st);
 // One grouped bf16 GEMM on the 64-wide kernel: C[rows][Nout] = A[rows][K] B_g^T
 // with group g owning rows [offsets[g], offsets[g+1]).  K % 64 == 0.
 enum GemmMode { GEMM_SWIGLU = 0, GEMM_GELU = 1, GEMM_PLAIN = 2, GEMM_SWIGLU_SAVE = 3, GEMM_GELU_SAVE = 4,
-                GEMM_DSWIGLU = 5, GEMM_DGELU = 6 };
+                GEMM_DSWIGLU = 5, GEMM_DGELU = 6, GEMM_F32OUT = 7 };
 struct GemmSpec {
     const void* A;          // [rows][K], or [a_mod][K] shared by the groups
     const void* B0;         // [G][Nout][K], or [Nout][K] with b_shared
@@ -124,8 +129,9 @@ struct GemmSpec {
     int b_shared;           // 1: one B for all groups
 };
 size_t grouped_gemm_ws_bytes(int G, int max_rows);  // its tile table
+// bm: 128 or 256 forces the row-tile height, anything else picks it
 hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offsets, int G, int max_rows,
-                               GemmTile* tiles, hipStream_t st);
+                               GemmTile* tiles, hipStream_t st, int bm = 0);
 // Dense GEMM y[rows][n] = x[rows][k] W^T with W [n][k] (one group; used for W_o).
 hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const void* w, void* y,
                         GemmTile* tiles, int32_t* offsets2, hipStream_t st);

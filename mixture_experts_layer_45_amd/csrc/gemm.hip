@@ -21,6 +21,8 @@
 //   * gemm_bf16_kernel -- any K (zero-filled tail), 4 waves, one tile per block.
 // Measured on one MI355X: the 64-wide kernel is 10-25 % faster on 128-row tiles
 // (256 experts x ~128 rows, d = 7168) and on short K (d = 512, f = 1024).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -39,8 +41,10 @@ namespace moe {
 //   DSWIGLU / DGELU          a plain product dH whose epilogue multiplies it by
 //                            those derivatives: da = dH dh/da, du = dH dh/du,
 //                            stored to C [rows][n_act*Nout].
+//   F32OUT                   a plain product stored in fp32 (C [rows][Nout] float):
+//                            the router's partial logits.
 enum { MODE_SWIGLU = 0, MODE_GELU = 1, MODE_PLAIN = 2, MODE_SWIGLU_SAVE = 3, MODE_GELU_SAVE = 4, MODE_DSWIGLU = 5,
-       MODE_DGELU = 6 };
+       MODE_DGELU = 6, MODE_F32OUT = 7 };
 __host__ __device__ constexpr bool gated_mode(int m) { return m == MODE_SWIGLU || m == MODE_SWIGLU_SAVE; }
 
 // tile-claim counters after the tile table's header: 4 GemmTile entries = 16
@@ -513,6 +517,28 @@ __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int r
                             for (int j = 0; j < 8; ++j) dv[j] *= g[j];
                             *(u32x4*)(Cp + at + (size_t)m * Nout * 2) = f32_to_bf16x8(dv);
                         }
+                    }
+                }
+            }
+        }
+        return;
+    }
+    if constexpr (MODE == MODE_F32OUT) {
+        const bool hi = lane >= 32;
+#pragma clang loop unroll(full)
+        for (int tm = 0; tm < C::TM; ++tm) {
+            const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+#pragma clang loop unroll(full)
+            for (int tn = 0; tn < C::TN; ++tn) {
+#pragma clang loop unroll(full)
+                for (int pp = 0; pp < 2; ++pp) {
+                    float g[8];
+                    row8(acc[tm * C::TN + tn], pp, g);
+                    const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+                    if (row < row_end && col < Nout) {
+                        float* o = (float*)Cp + (size_t)row * Nout + col;
+                        *(floatx4*)o = floatx4{g[0], g[1], g[2], g[3]};
+                        *(floatx4*)(o + 4) = floatx4{g[4], g[5], g[6], g[7]};
                     }
                 }
             }
@@ -1253,6 +1279,7 @@ static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st)
         MOE_K64_CASE(MODE_GELU_SAVE)
         MOE_K64_CASE(MODE_DSWIGLU)
         MOE_K64_CASE(MODE_DGELU)
+        MOE_K64_CASE(MODE_F32OUT)
     }
 #undef MOE_K64_CASE
     return hipErrorInvalidValue;
@@ -1342,13 +1369,13 @@ hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const 
 }
 
 size_t grouped_gemm_ws_bytes(int G, int max_rows) {
-    return table_bytes(pick_bm(MOE_BF16, G, max_rows), G, max_rows);
+    return std::max(table_bytes(128, G, max_rows), table_bytes(256, G, max_rows));
 }
 
 hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offsets, int G, int max_rows,
-                               GemmTile* tiles, hipStream_t st) {
+                               GemmTile* tiles, hipStream_t st, int bm) {
     if (max_rows <= 0 || G <= 0) return hipSuccess;
-    const int BM = pick_bm(MOE_BF16, G, max_rows);
+    const int BM = bm == 128 || bm == 256 ? bm : pick_bm(MOE_BF16, G, max_rows);
     const int mtiles = max_m_tiles(BM, G, max_rows);
     hipError_t err = build_tiles(offsets, G, BM, max_rows, mtiles, tiles, st);
     if (err != hipSuccess) return err;

@@ -30,19 +30,28 @@
 // "3. 理论基础") has no router: route_hash_kernel maps sub-token t*H + g to
 // expert fmix32(key_t*H + g) mod E of head g, fmix32 being MurmurHash3's
 // 32-bit finaliser.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
 
 constexpr int RT_ROWS = 16;
+constexpr int kMaxParts = 8;  // partial-logit slices of the split-K router GEMM
 constexpr int RT_THREADS = 256;
 
 // tokens per route block: 16, except for bf16 routers with 17..64 experts
-int route_rows(int E, int dtype) {
+static bool route_split_applies(int T, int h, int H, int E, int dtype);
+constexpr int RT_ROWS_SPLIT = 4;  // tokens per selection block behind the split-K router GEMM
+int route_rows(int T, int h, int H, int E, int dtype) {
+    if (route_split_applies(T, h, H, E, dtype)) return RT_ROWS_SPLIT;
     if (dtype != MOE_BF16 || E <= 16 || E > 64) return RT_ROWS;
     return E <= 32 ? 2 * RT_ROWS : 4 * RT_ROWS;
 }
-int route_blocks(int T, int E, int dtype) { return (T + route_rows(E, dtype) - 1) / route_rows(E, dtype); }
+int route_blocks(int T, int h, int H, int E, int dtype) {
+    const int r = route_rows(T, h, H, E, dtype);
+    return (T + r - 1) / r;
+}
 
 // Routing-key exp: a fixed sequence of fp32 operations (Cody and Waite's range
 // reduction with ln 2 split into a 16-bit head and an fp32 tail, the Taylor
@@ -95,12 +104,15 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// NB = 16-expert column blocks of the logit tile (E <= 16*NB); EJ = E/64 slots per lane.
-template <int NB, bool BF16>
+// NB = 16-expert column blocks of the logit tile (E <= 16*NB); EJ = E/64 slots
+// per lane; ROWS tokens per block (16, or 4 -- one token per wave -- behind
+// the split-K router GEMM, where the logits are given and only selection runs).
+template <int NB, bool BF16, int ROWS = RT_ROWS>
 __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     constexpr int LDE = NB * 16 + 1;
     constexpr int EJ = (NB * 16 + 63) / 64;
-    __shared__ float part[4][RT_ROWS][LDE];  // per-wave partial logits; part[0] ends as the tile
+    constexpr int RT_ROWS = ROWS;
+    __shared__ float part[ROWS == 16 ? 4 : 1][RT_ROWS][LDE];  // per-wave partial logits; part[0] ends as the tile
     __shared__ int hist[NB * 16];
     __shared__ float pw[4][NB * 16];
 
@@ -114,12 +126,41 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     for (int i = threadIdx.x; i < NB * 16; i += RT_THREADS) hist[i] = 0;
 
     // ---------------------------------------------------------------- logits
-    if (a.flags & MOE_LOGITS_IN) {
-        for (int i = threadIdx.x; i < RT_ROWS * E; i += RT_THREADS) {
-            const int r = i / E, e = i - r * E, t = t0 + r;
-            part[0][r][e] = t < T ? a.logits[((size_t)t * H + g) * E + e] : 0.0f;
+    if (a.logit_parts || (a.flags & MOE_LOGITS_IN)) {
+        // logits given: the split-K router GEMM's partial logits (at most
+        // kMaxParts, summed in part order), or the caller's.  Four elements per
+        // thread per pass, every load of a pass issued before the first add.
+        const int n = RT_ROWS * E;
+        const int np = a.logit_parts ? a.n_parts : 1;
+        for (int i0 = threadIdx.x; i0 < n; i0 += 4 * RT_THREADS) {
+            float v[4][kMaxParts];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * RT_THREADS;
+                const int r = i / E, e = i - r * E, t = t0 + r;
+                const bool ok = i < n && t < T;
+#pragma unroll
+                for (int q = 0; q < kMaxParts; ++q) {
+                    float x = 0.0f;
+                    if (ok && q < np)
+                        x = a.logit_parts ? a.logit_parts[((size_t)q * T + t) * E + e]
+                                          : a.logits[((size_t)t * H + g) * E + e];
+                    v[u][q] = x;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * RT_THREADS;
+                if (i >= n) continue;
+                const int r = i / E, e = i - r * E;
+                float sum = v[u][0];
+#pragma unroll
+                for (int q = 1; q < kMaxParts; ++q)
+                    if (q < np) sum += v[u][q];
+                part[0][r][e] = sum;
+            }
         }
-    } else if constexpr (BF16) {
+    } else if constexpr (BF16 && ROWS == 16) {
         floatx4 acc[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -166,7 +207,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
             s += part[3][r][e];
             part[0][r][e] = s;
         }
-    } else {
+    } else if constexpr (ROWS == 16) {
         const float* x = (const float*)a.x;
         const float* wg = (const float*)a.w_router + (size_t)g * E * d;
         for (int i = threadIdx.x; i < RT_ROWS * E; i += RT_THREADS) {
@@ -609,7 +650,86 @@ static hipError_t launch_small(const RouteArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// Split-K router GEMM for bf16 routers with more than 64 experts (one head):
+// the 16-token blocks of route_kernel would each pull all E x d router weights
+// through one CU; instead the 64-wide grouped GEMM computes fp32 partial logits
+// over KS slices of d (group q = slice q: every group reads the same token
+// rows and router rows, with its own k span), and route_kernel sums the KS
+// partials in slice order before selecting.
+struct RouteSplit {
+    int KS, nst;
+};
+static RouteSplit route_split_of(int T, int h, int H, int E, int dtype);
+static bool route_split_applies(int T, int h, int H, int E, int dtype) {
+    return route_split_of(T, h, H, E, dtype).KS > 0;
+}
+static RouteSplit route_split_of(int T, int h, int H, int E, int dtype) {
+    RouteSplit r{0, 0};
+    if (dtype != MOE_BF16 || H != 1 || E <= 64 || E % 8 != 0 || h % 64 != 0 || T < 256) return r;
+    r.nst = h / 64;
+    const int m_tiles = (T + 127) / 128;
+    int ks = 256 / m_tiles;
+    ks = std::max(1, std::min(ks, std::min(kMaxParts, r.nst / 4)));
+    r.KS = ks;
+    return r;
+}
+static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t route_split_ws_bytes(int T, int h, int H, int E, int dtype) {
+    const RouteSplit r = route_split_of(T, h, H, E, dtype);
+    if (r.KS == 0) return 0;
+    return al256((size_t)r.KS * T * E * 4) + al256((size_t)(r.KS + 1) * 4) + al256((size_t)r.KS * 8) +
+           grouped_gemm_ws_bytes(r.KS, r.KS * T) + 256;
+}
+
+__global__ void route_split_tables_kernel(int KS, int T, int nst, int32_t* offsets, int2* kspan) {
+    const int q = threadIdx.x;
+    if (q <= KS) offsets[q] = q * T;
+    if (q < KS) {
+        const int k0 = q * nst / KS, k1 = (q + 1) * nst / KS;
+        kspan[q] = make_int2(k0, k1 - k0);
+    }
+}
+
+hipError_t launch_route(const RouteArgs& a0, hipStream_t st) {
+    RouteArgs a = a0;
+    const RouteSplit rs = route_split_of(a.T, a.h, a.H, a.E, a.dtype);
+    if (rs.KS > 0 && !(a.flags & MOE_LOGITS_IN)) {
+        if (!a.split_ws) return hipErrorInvalidValue;
+        char* w = (char*)a.split_ws;
+        float* parts = (float*)w;
+        w += al256((size_t)rs.KS * a.T * a.E * 4);
+        int32_t* offs = (int32_t*)w;
+        w += al256((size_t)(rs.KS + 1) * 4);
+        int2* kspan = (int2*)w;
+        w += al256((size_t)rs.KS * 8);
+        GemmTile* tiles = (GemmTile*)w;
+        hipLaunchKernelGGL(route_split_tables_kernel, dim3(1), dim3(64), 0, st, rs.KS, a.T, rs.nst, offs, kspan);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        GemmSpec gs{};
+        gs.A = a.x;
+        gs.B0 = a.w_router;
+        gs.C = parts;
+        gs.K = a.h;
+        gs.Nout = a.E;
+        gs.a_bytes = (long long)a.T * a.h * 2;
+        gs.kspan = kspan;
+        gs.a_mod = a.T;
+        gs.b_shared = 1;
+        if ((err = launch_grouped_gemm(GEMM_F32OUT, gs, offs, rs.KS, rs.KS * a.T, tiles, st, 128)) != hipSuccess)
+            return err;
+        a.logit_parts = parts;
+        a.n_parts = rs.KS;
+    }
+    if (rs.KS > 0) {  // selection only, one token per wave (the logits are given)
+        dim3 grid((a.T + RT_ROWS_SPLIT - 1) / RT_ROWS_SPLIT, a.H);
+        if (a.E <= 128)
+            hipLaunchKernelGGL((route_kernel<8, true, RT_ROWS_SPLIT>), grid, dim3(RT_THREADS), 0, st, a);
+        else
+            hipLaunchKernelGGL((route_kernel<16, true, RT_ROWS_SPLIT>), grid, dim3(RT_THREADS), 0, st, a);
+        return hipGetLastError();
+    }
     if (a.dtype == MOE_BF16 && a.E <= 64) {
         if (a.E <= 16) return launch_small<1, 1>(a, st);
         if (a.E <= 32) return launch_small<2, 2>(a, st);
