@@ -48,8 +48,8 @@ def parse():
                    help="time a training step instead: the training forward (it keeps what the backward "
                         "reads) and moe_layer_backward of sum(dy * y) + L_aux")
     p.add_argument("--counters", action="store_true",
-                   help="for rocprofv3 --pmc runs: a 1 GiB device copy (counter calibration), then the "
-                        "dominant kernel three times; prints nothing else")
+                   help="for rocprofv3 --pmc runs: a 1 GiB device copy (counter calibration), then each "
+                        "stage (route, gather permute, GEMM1, GEMM2, combine) three times; prints one line")
     return p.parse_args()
 
 
@@ -358,9 +358,12 @@ def main():
         cp_dst = torch.empty_like(cp_src)
         cp_dst.copy_(cp_src)
         torch.cuda.synchronize()
-        for _ in range(3):
-            gemm1()
-        torch.cuda.synchronize()
+        # every stage three times, each on its own (the layer's routing tables,
+        # the stage-wise gather, both expert GEMMs, the combine)
+        for fn in (route, permute, gemm1, gemm2, combine):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
         print(json.dumps({"counters_run": name, "copy_bytes": 1 << 30}), flush=True)
         return
     gemm1()
@@ -383,7 +386,9 @@ def main():
     gemm1_flops = 2.0 * n_act * n_kept * d * f
     gemm2_flops = 2.0 * n_kept * f * d
     route_bytes = A * 8 if cfg.get("gate") == "hash" else T * h * esz + Et * d * esz + A * 8
-    distinct_rows = n_kept  # every kept row is a distinct (token, expert) pair; x rows read once per row
+    # the gather reads each (sub-)token's slice once (token-major) and writes it to each of its kept rows
+    dest = aux["dest_row"].view(T * H, K)
+    distinct_rows = int((dest >= 0).any(dim=1).sum().item())
     permute_bytes = distinct_rows * d * esz + n_kept * d * esz + A * 4 * 2
     combine_bytes = n_kept * d * esz + A * 8 + T * h * esz + (T * h * esz if cfg.get("n_shared") else 0)
     w_bytes = nonempty * (n_act + 1) * d * f * esz
