@@ -331,20 +331,30 @@ __global__ __launch_bounds__(256) void dx_kernel(const uint16_t* dXp, const int3
     const int g = col / d, i = col - g * d;
     const int s = t * H + g;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto add = [&](const uint16_t* p) {
-        const u32x4 v = *(const u32x4*)p;
+    auto add = [&](const u32x4 v) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             acc[2 * q] += __uint_as_float(v[q] << 16);
             acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
         }
     };
-    for (int k = 0; k < K; ++k) {
-        const int row = dest_row[(size_t)s * K + k];
-        if (row >= 0) add(dXp + (size_t)row * d + i);
+    // up to 8 slots' rows are loaded before the first is added (in slot order)
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        u32x4 v[8];
+        bool kept[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + u;
+            const int row = k < K ? dest_row[(size_t)s * K + k] : -1;
+            kept[u] = row >= 0;
+            v[u] = kept[u] ? *(const u32x4*)(dXp + (size_t)row * d + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (kept[u]) add(v[u]);
     }
-    if (dxr) add(dxr + ((size_t)g * T + t) * d + i);
-    if (dxs) add(dxs + (size_t)t * h + col);
+    if (dxr) add(*(const u32x4*)(dxr + ((size_t)g * T + t) * d + i));
+    if (dxs) add(*(const u32x4*)(dxs + (size_t)t * h + col));
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);

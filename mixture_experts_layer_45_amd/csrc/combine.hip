@@ -28,19 +28,39 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int tpr) {
     const float* wr = a.topk_w + s * K;
     for (int j0 = c * 8; j0 < d; j0 += tpr * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < K; ++k) {
-            const int row = dr[k];
-            if (row < 0) continue;
-            const float w = wr[k];
-            if constexpr (BF16) {
-                const uint4 v = *(const uint4*)((const uint16_t*)a.y_perm + (size_t)row * d + j0);
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (BF16) {
+            // up to KB slots' rows are loaded before the first is added, so their
+            // latencies overlap; the sums still run in slot order
+            constexpr int KB = 8;
+            for (int k0 = 0; k0 < K; k0 += KB) {
+                uint4 v[KB];
+                float w[KB];
+                bool kept[KB];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = fmaf(w, __uint_as_float(u[q] << 16), acc[2 * q]);
-                    acc[2 * q + 1] = fmaf(w, __uint_as_float(u[q] & 0xffff0000u), acc[2 * q + 1]);
+                for (int u = 0; u < KB; ++u) {
+                    const int k = k0 + u;
+                    const int row = k < K ? dr[k] : -1;
+                    kept[u] = row >= 0;
+                    w[u] = kept[u] ? wr[k] : 0.0f;
+                    v[u] = kept[u] ? *(const uint4*)((const uint16_t*)a.y_perm + (size_t)row * d + j0)
+                                   : make_uint4(0u, 0u, 0u, 0u);
                 }
-            } else {
+#pragma unroll
+                for (int u = 0; u < KB; ++u) {
+                    if (!kept[u]) continue;
+                    const uint32_t uu[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = fmaf(w[u], __uint_as_float(uu[q] << 16), acc[2 * q]);
+                        acc[2 * q + 1] = fmaf(w[u], __uint_as_float(uu[q] & 0xffff0000u), acc[2 * q + 1]);
+                    }
+                }
+            }
+        } else {
+            for (int k = 0; k < K; ++k) {
+                const int row = dr[k];
+                if (row < 0) continue;
+                const float w = wr[k];
                 const float* yp = (const float*)a.y_perm + (size_t)row * d + j0;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) acc[q] = fmaf(w, yp[q], acc[q]);
