@@ -385,10 +385,11 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
 // per block (R = 1, 2, 4 for E <= 16, 32, 64, so that the router rows a block
 // reads stay small next to its token rows).  Phase 1 as above, the four waves
 // splitting the reduction over d, with R x NB MFMA tiles per wave and U k steps
-// of loads in flight.  Phase 2 gives each token one lane: the lane reads its
-// row of logits from LDS into registers and selects sequentially (key
-// descending, index ascending), with no cross-lane traffic; its full score
-// distribution goes to an LDS tile whose columns are summed in token order.
+// of loads in flight.  Phase 2 gives each token 256/RS lanes (16, 8 or 4), each
+// holding every LPT-th expert of the token's row of logits in registers: an
+// arg-max round (key descending, index ascending) is a lane-local scan and a
+// butterfly over the token's lanes.  The full score distribution goes to an
+// LDS tile whose columns are summed in token order.
 template <int NB, int R, bool SIG>
 __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
     constexpr int RS = 16 * R;
@@ -474,72 +475,99 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
         }
     }
 
-    // ------------------------------------------ selection: one lane per token
+    // ------------------- selection: LPT = 256 / RS lanes per token, each lane
+    // holding experts lq, lq + LPT, ...; every arg-max round is a lane-local scan
+    // then a butterfly over the token's lanes on the (key desc, index asc) order
+    constexpr int LPT = RT_THREADS / RS;
+    constexpr int EPL = EP / LPT;
     const float NEG = -__builtin_inff();
-    const int r = threadIdx.x;
+    const int r = threadIdx.x / LPT, lq = threadIdx.x % LPT;
     const int t = t0 + r;
-    if (r < RS && t < T) {
+    // arg-max of (key, expert, value) over the token's lanes
+    auto group_best = [&](float& bk, int& be, float& bv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int off = 1; off < LPT; off <<= 1) {
+            const float ok = __shfl_xor(bk, off);
+            const int oe = __shfl_xor(be, off);
+            const float ov = __shfl_xor(bv, off);
+            if (better(ok, oe, bk, be)) { bk = ok; be = oe; bv = ov; }
+        }
+    };
+    auto group_sum = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int off = 1; off < LPT; off <<= 1) v += __shfl_xor(v, off);
+        return v;
+    };
+    auto group_max = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int off = 1; off < LPT; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+        return v;
+    };
+    if (t < T) {  // uniform over a token's lanes
         const size_t sidx = (size_t)t * H + g;
         // softmax router: key = biased logit; sigmoid router: key = sigma + bias,
         // weights from sigma
-        float key[EP], sg[SIG ? EP : 1];
+        float key[EPL], sg[SIG ? EPL : 1];
 #pragma unroll
-        for (int e = 0; e < EP; ++e) {
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lq + LPT * j;
             const bool valid = e < E;
             float l = valid ? part[0][r][e] : NEG;
             if (valid && a.logit_bias) l = l + a.logit_bias[g * E + e];
             if constexpr (SIG) {
-                sg[e] = valid ? key_sigmoid(l) : 0.0f;
-                key[e] = valid ? (a.select_bias ? sg[e] + a.select_bias[g * E + e] : sg[e]) : NEG;
+                sg[j] = valid ? key_sigmoid(l) : 0.0f;
+                key[j] = valid ? (a.select_bias ? sg[j] + a.select_bias[g * E + e] : sg[j]) : NEG;
             } else {
-                key[e] = l;
+                key[j] = l;
             }
         }
         // group limit: experts outside the group_limit best groups are excluded
-        uint64_t excl = 0;
+        // (the best remaining key lies in the best remaining group)
+        uint32_t excl = 0;  // bit j: expert lq + LPT*j excluded
         if (a.n_groups > 1) {
-            const int gsz = E / a.n_groups;  // <= 32 here (E <= 64, n_groups >= 2)
-            const uint64_t gbits = (1ull << gsz) - 1ull;
-            uint64_t kept = 0;
+            const int gsz = E / a.n_groups;
+            uint32_t kept = 0;
             for (int m = 0; m < a.group_limit; ++m) {
-                float bk = NEG;
-                int be = 0;
+                float bk = NEG, bv = 0.0f;
+                int be = 0x7fffffff;
 #pragma unroll
-                for (int e = 0; e < EP; ++e) {
-                    const bool free_e = e < E && !((kept >> e) & 1ull);
-                    if (free_e && better(key[e], e, bk, be)) {
-                        bk = key[e];
-                        be = e;
-                    }
+                for (int j = 0; j < EPL; ++j) {
+                    const int e = lq + LPT * j;
+                    if (e < E && !((kept >> j) & 1u) && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
                 }
-                kept |= gbits << ((be / gsz) * gsz);
+                group_best(bk, be, bv);
+                const int gb = be / gsz;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j)
+                    if ((lq + LPT * j) / gsz == gb) kept |= 1u << j;
             }
             excl = ~kept;
         }
-        // two passes of K sequential arg-max rounds: the first sums the kept
-        // scores, the second writes the normalised weights
+        // two passes of K arg-max rounds: the first sums the kept scores, the
+        // second writes the normalised weights (lane k % LPT writes slot k)
         float den = 0.0f, vmax = 0.0f;
         for (int pass = 0; pass < 2; ++pass) {
-            uint64_t used = excl;
+            uint32_t used = excl;
             for (int k = 0; k < K; ++k) {
                 float bk = NEG, bv = 0.0f;
-                int be = EP;
+                int be = 0x7fffffff;
 #pragma unroll
-                for (int e = 0; e < EP; ++e) {
-                    const bool free_e = e < E && !((used >> e) & 1ull);
-                    if (free_e && better(key[e], e, bk, be)) {
-                        bk = key[e];
+                for (int j = 0; j < EPL; ++j) {
+                    const int e = lq + LPT * j;
+                    if (e < E && !((used >> j) & 1u) && better(key[j], e, bk, be)) {
+                        bk = key[j];
                         be = e;
-                        if constexpr (SIG) bv = sg[e];
-                        else bv = key[e];
+                        if constexpr (SIG) bv = sg[j];
+                        else bv = key[j];
                     }
                 }
-                used |= 1ull << be;
+                group_best(bk, be, bv);
+                if (be % LPT == lq) used |= 1u << (be / LPT);
                 if (k == 0) vmax = bv;  // the first kept has the largest biased logit
                 const float u = SIG ? bv : expf(bv - vmax);
                 if (pass == 0) {
                     den += u;
-                } else {
+                } else if (k % LPT == lq) {
                     a.topk_idx[sidx * K + k] = g * E + be;
                     a.topk_w[sidx * K + k] = u / den;
                     atomicAdd(&hist[be], 1);
@@ -551,20 +579,26 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
             if constexpr (SIG) {
                 float tot = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EP; ++e) tot += sg[e];
+                for (int j = 0; j < EPL; ++j) tot += sg[j];
+                tot = group_sum(tot);
 #pragma unroll
-                for (int e = 0; e < EP; ++e)
-                    if (e < E) part[1][r][e] = sg[e] / tot;
+                for (int j = 0; j < EPL; ++j)
+                    if (lq + LPT * j < E) part[1][r][lq + LPT * j] = sg[j] / tot;
             } else {
                 float m = NEG;
 #pragma unroll
-                for (int e = 0; e < EP; ++e) m = fmaxf(m, key[e]);
-                float tot = 0.0f;
+                for (int j = 0; j < EPL; ++j) m = fmaxf(m, key[j]);
+                m = group_max(m);
+                float ex[EPL], tot = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EP; ++e) tot += e < E ? expf(key[e] - m) : 0.0f;
+                for (int j = 0; j < EPL; ++j) {
+                    ex[j] = lq + LPT * j < E ? expf(key[j] - m) : 0.0f;
+                    tot += ex[j];
+                }
+                tot = group_sum(tot);
 #pragma unroll
-                for (int e = 0; e < EP; ++e)
-                    if (e < E) part[1][r][e] = expf(key[e] - m) / tot;
+                for (int j = 0; j < EPL; ++j)
+                    if (lq + LPT * j < E) part[1][r][lq + LPT * j] = ex[j] / tot;
             }
         }
     }
