@@ -383,8 +383,8 @@ struct IntC {
 
 template <int BM, int MODE>
 struct Ring8Cfg {
-    static constexpr int NMAT = MODE == MODE_SWIGLU ? 2 : 1;
-    static constexpr int BNM = MODE == MODE_SWIGLU ? 128 : 256;  // output columns per matrix
+    static constexpr int NMAT = gated_mode(MODE) ? 2 : 1;
+    static constexpr int BNM = gated_mode(MODE) ? 128 : 256;  // output columns per matrix
     static constexpr int WM = BM / 2;
     static constexpr int WNM = BNM / 4;
     static constexpr int TM = WM / 32;
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
         const uint8_t* B0 = (const uint8_t*)a.B0 + (size_t)tl.group * Nout * rowbytes;
-        const uint8_t* B1 = MODE == MODE_SWIGLU ? (const uint8_t*)a.B1 + (size_t)tl.group * Nout * rowbytes : B0;
+        const uint8_t* B1 = gated_mode(MODE) ? (const uint8_t*)a.B1 + (size_t)tl.group * Nout * rowbytes : B0;
         t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
         const int lr = lane >> 2, pc = lane & 3;
 #pragma unroll
@@ -787,7 +787,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
             setup(s_next, nxt);
             prologue(nxt);
         }
-        rowstore_epilogue<C, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane);
+        rowstore_epilogue<C, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane, (uint8_t*)a.aux);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -1267,7 +1267,25 @@ static hipError_t run_k64_only(GArgs g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// the ring kernel with a training epilogue (the shapes where it leads: gated,
+// 256-row tiles, K >= 4096, K % 32 == 0)
+template <int MODE>
+static hipError_t run_ring8_save(GArgs g, hipStream_t st) {
+    using R = Ring8Cfg<256, MODE>;
+    g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+    g.total = g.m_tiles * g.n_tiles;
+    g.per_xcd = (g.total + 7) / 8;
+    g.partial = nullptr;
+    if (g.total == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_bf16_ring8_kernel<256, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+    return hipGetLastError();
+}
+
 static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st) {
+    if (mode == MODE_SWIGLU_SAVE && BM == 256 && g.K >= 4096 && g.K % 32 == 0 && g.Nout % 8 == 0 &&
+        ((uintptr_t)g.C & 15) == 0 && g.a_bytes < (1ll << 31) && (long long)g.Nout * g.K * 2 < (1ll << 31) &&
+        !g.kspan && !g.a_mod && !g.b_shared)
+        return run_ring8_save<MODE_SWIGLU_SAVE>(g, st);
 #define MOE_K64_CASE(M)                                                         \
     case M:                                                                     \
         return BM == 256 ? run_k64_only<256, M>(g, st) : run_k64_only<128, M>(g, st);

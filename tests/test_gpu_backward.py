@@ -136,3 +136,44 @@ def test_training_forward_matches_forward():
     ref = orc.layer_forward(cfg, host, host["x"])
     for yy in (y0, y1):
         G.assert_close(G.host(yy), ref["y"], cfg["dtype"], "y", mag=ref["ymag"])
+
+
+def test_training_forward_long_k_saves_activation_derivatives():
+    """The shape where the gate/up GEMM runs on the ring kernel (256-row tiles,
+    K = 4096): the training forward's output equals the inference forward's bit
+    for bit (same kernel and k order), and the saved dh/da, dh/du of sampled
+    rows match an fp64 recomputation from x and the expert weights within one
+    bf16 rounding."""
+    cfg = inputs.variant("top2_e8_h4096", T=2048, f=256)
+    inp = G.dev_inputs(cfg)
+    y0, aux = G.run_layer(cfg, inp)
+    d = moe.desc_from_cfg(cfg)
+    y1 = torch.empty_like(y0)
+    sv = alloc_saved(cfg)
+    moe.moe_layer_forward_train(d, inp, inp["x"], y1, sv, ws=moe.workspace(d))
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    f = cfg["f"]
+    n = int(sv["offsets"][-1].item())
+    rows = np.unique(np.random.default_rng(5).integers(0, n, 24))
+    off = sv["offsets"].cpu().numpy()
+    src = sv["src_token"].cpu().numpy()
+    x = G.host(inp["x"])
+    wg, wu = G.host(inp["w_gate"]), G.host(inp["w_up"])
+    ag = G.host(sv["act_grad"])
+    for r in rows:
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        xr = x[src[r]]
+        a = wg[e] @ xr
+        u = wu[e] @ xr
+        sg = 1.0 / (1.0 + np.exp(-a))
+        want = np.concatenate([u * sg * (1.0 + a * (1.0 - sg)), a * sg])
+        got = ag[r]
+        # a and u carry fp32 accumulation error (at most 1e-5 of the sum of the
+        # absolute products here); |silu''| <= 0.5 and |silu'| <= 1.1 carry it into
+        # the derivatives, which are then rounded once to bf16
+        da = 1e-5 * (np.abs(wg[e]) @ np.abs(xr))
+        du = 1e-5 * (np.abs(wu[e]) @ np.abs(xr))
+        slack = np.concatenate([1.1 * du + 0.5 * np.abs(u) * da, 1.1 * da])
+        tol = G.ulp_bf16(np.abs(want)) + slack
+        assert np.all(np.abs(got - want) <= tol), (int(r), float(np.max(np.abs(got - want) - tol)))
