@@ -470,25 +470,6 @@ __device__ __forceinline__ float dgelu_f(float a) {
     return 0.5f * (1.0f + erf_as(a * 0.70710678118654752f)) + a * 0.39894228040143268f * __expf(-0.5f * a * a);
 }
 
-// Stores one 32x32 tile (tm, tn) of a wave's output block as bf16 rows of ld
-// elements at column offset coff (the same lane swap as the epilogue below).
-template <typename C>
-__device__ __forceinline__ void store_tile_rows(const floatx16& v, int tm, int tn, int row0, int row_end, int n0,
-                                                int Nout, uint8_t* base, int ld, int coff, int wm, int wn, int lane) {
-    const bool hi = lane >= 32;
-    const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
-#pragma clang loop unroll(full)
-    for (int pp = 0; pp < 2; ++pp) {
-        uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
-        uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-        const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
-        const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
-        if (row < row_end && col < Nout) *(u32x4*)(base + ((size_t)row * ld + coff + col) * 2) = o;
-    }
-}
-
 template <typename C, int MODE>
 __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
                                                   int wm, int wn, int lane, uint8_t* aux = nullptr) {
@@ -546,27 +527,45 @@ __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int r
         return;
     }
     if constexpr (MODE == MODE_SWIGLU_SAVE) {
-        // dh/da and dh/du of h = silu(a) u, one 32x32 tile at a time
+        // dh/da and dh/du of h = silu(a) u, eight outputs at a time (few live
+        // registers next to the accumulators)
+        const bool hi = lane >= 32;
 #pragma clang loop unroll(full)
         for (int t = 0; t < C::TM * C::TN; ++t) {
-            floatx16 ga, gu;
+            const int row = row0 + wm * C::WM + (t / C::TN) * 32 + (lane & 31);
 #pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) {
-                const float a = acc[t][i], u = acc[C::TM * C::TN + t][i];
-                const float sg = sigma_f(a);
-                ga[i] = u * (sg * (1.0f + a * (1.0f - sg)));
-                gu[i] = a * sg;
+            for (int pp = 0; pp < 2; ++pp) {
+                float av[8], uv[8], ga[8], gu[8];
+                row8(acc[t], pp, av);
+                row8(acc[C::TM * C::TN + t], pp, uv);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float sg = sigma_f(av[j]);
+                    ga[j] = uv[j] * (sg * (1.0f + av[j] * (1.0f - sg)));
+                    gu[j] = av[j] * sg;
+                }
+                const int col = n0 + wn * C::WNM + (t % C::TN) * 32 + 16 * pp + (hi ? 8 : 0);
+                if (row < row_end && col < Nout) {
+                    uint8_t* p = aux + ((size_t)row * 2 * Nout + col) * 2;
+                    *(u32x4*)p = f32_to_bf16x8(ga);
+                    *(u32x4*)(p + (size_t)Nout * 2) = f32_to_bf16x8(gu);
+                }
             }
-            store_tile_rows<C>(ga, t / C::TN, t % C::TN, row0, row_end, n0, Nout, aux, 2 * Nout, 0, wm, wn, lane);
-            store_tile_rows<C>(gu, t / C::TN, t % C::TN, row0, row_end, n0, Nout, aux, 2 * Nout, Nout, wm, wn, lane);
         }
     } else if constexpr (MODE == MODE_GELU_SAVE) {
+        const bool hi = lane >= 32;
 #pragma clang loop unroll(full)
         for (int t = 0; t < C::TM * C::TN; ++t) {
-            floatx16 ga;
+            const int row = row0 + wm * C::WM + (t / C::TN) * 32 + (lane & 31);
 #pragma clang loop unroll(full)
-            for (int i = 0; i < 16; ++i) ga[i] = dgelu_f(acc[t][i]);
-            store_tile_rows<C>(ga, t / C::TN, t % C::TN, row0, row_end, n0, Nout, aux, Nout, 0, wm, wn, lane);
+            for (int pp = 0; pp < 2; ++pp) {
+                float av[8], ga[8];
+                row8(acc[t], pp, av);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ga[j] = dgelu_f(av[j]);
+                const int col = n0 + wn * C::WNM + (t % C::TN) * 32 + 16 * pp + (hi ? 8 : 0);
+                if (row < row_end && col < Nout) *(u32x4*)(aux + ((size_t)row * Nout + col) * 2) = f32_to_bf16x8(ga);
+            }
         }
     }
     if constexpr (gated_mode(MODE)) {
