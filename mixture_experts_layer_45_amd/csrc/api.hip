@@ -204,7 +204,7 @@ BwdPlan bwd_plan_of(const moe_desc* d, const Plan& p) {
 struct BwdWs {
     int2 *kspan_r, *kspan_d, *kspan_h;
     int32_t *stage_r, *stage_d, *stage_h, *off_T, *off_h, *off_w, *off_f, *off_E, *off_hr, *off_fr;
-    void *w_downT, *w_guT, *wgT, *sh_downT, *sh_guT, *w_oT;
+    void* wgT;
     void *dcat, *dYp, *dAU, *dXp, *dl, *dxr, *dAUs, *dxs;
     float* dw;
     void *dYpT, *hT, *dAT, *dUT, *xpT, *dlT, *xhT, *dcatT, *shT, *dAsT, *dUsT, *xT, *dyT, *ycT;
@@ -246,8 +246,6 @@ BwdWs carve_bwd(Carver& c, const Plan& p, const BwdPlan& b) {
     w.off_E = c.take<int32_t>(p.H + 1);
     w.off_hr = c.take<int32_t>(2);
     w.off_fr = c.take<int32_t>(2);
-    w.w_downT = c.take<char>((size_t)p.Et * p.f * p.d * e2);
-    w.w_guT = c.take<char>((size_t)p.Et * p.d * nf * e2);
     w.dYp = c.take<char>(N * p.d * e2 + 16);
     w.dw = c.take<float>((size_t)p.A + 1);
     w.dAU = c.take<char>(N * nf * e2 + 16);
@@ -265,14 +263,11 @@ BwdWs carve_bwd(Carver& c, const Plan& p, const BwdPlan& b) {
         w.xhT = c.take<char>((size_t)p.d * b.Np_h * e2);
     }
     if (b.wo) {
-        w.w_oT = c.take<char>((size_t)p.h * p.h * e2);
         w.dcat = c.take<char>(T * p.h * e2 + 16);
         w.dyT = c.take<char>((size_t)p.h * b.Np_d * e2);
         w.ycT = c.take<char>((size_t)p.h * b.Np_d * e2);
     }
     if (b.shared) {
-        w.sh_downT = c.take<char>((size_t)p.f * p.h * e2);
-        w.sh_guT = c.take<char>((size_t)p.h * nf * e2);
         w.dAUs = c.take<char>(T * nf * e2 + 16);
         w.dxs = c.take<char>(T * p.h * e2 + 16);
         w.dcatT = c.take<char>((size_t)p.h * b.Np_d * e2);
@@ -689,6 +684,15 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
         gs.a_rows = a_rows; gs.kspan = kspan; gs.a_mod = a_mod; gs.b_shared = b_shared;
         return launch_grouped_gemm(mode, gs, offs, G, rows, W.tiles, st);
     };
+    // C = A B with B the forward weights as stored ([G][K][Nout]: the product by
+    // their transpose); with B1, k rows >= kb1 are B1's
+    auto gemm_t = [&](int mode, const void* A, long long a_bytes, const void* B0, const void* B1, int kb1, void* C,
+                      void* aux, int Kc, int Nout, const int32_t* offs, int G, int rows) -> hipError_t {
+        GemmSpec gs{};
+        gs.A = A; gs.B0 = B0; gs.B1 = B1; gs.C = C; gs.aux = aux; gs.K = Kc; gs.Nout = Nout; gs.a_bytes = a_bytes;
+        gs.b_kmajor = 1; gs.kb1 = kb1;
+        return launch_grouped_gemm(mode, gs, offs, G, rows, W.tiles, st);
+    };
     // ---- group tables
     MOE_TRY(launch_set2(W.off_T, 0, T, st), "offsets");
     MOE_TRY(launch_set2(W.off_hr, 0, h, st), "offsets");
@@ -700,16 +704,11 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
     MOE_TRY(launch_kspan(sv->offsets, Et, b.ms_r, W.kspan_r, W.stage_r, st), "row-block table");
     MOE_TRY(launch_kspan(W.off_T, 1, b.ms_d, W.kspan_d, W.stage_d, st), "row-block table");
     MOE_TRY(launch_kspan(W.off_h, H, b.ms_h, W.kspan_h, W.stage_h, st), "row-block table");
-    // ---- weights with the other index contiguous
-    MOE_TRY(launch_transpose_batched(w->w_down, Et, dd, f, W.w_downT, dd, 0, st), "transpose");
-    MOE_TRY(launch_transpose_batched(w->w_gate, Et, f, dd, W.w_guT, NA * f, 0, st), "transpose");
-    if (NA == 2) MOE_TRY(launch_transpose_batched(w->w_up, Et, f, dd, W.w_guT, NA * f, f, st), "transpose");
     const void* dc = dy;
     // ---- W_o: dcat = dy W_o, dW_o = dy^T y_cat
     if (b.wo) {
-        MOE_TRY(launch_transpose_batched(w->w_o, 1, h, h, W.w_oT, h, 0, st), "transpose");
-        MOE_TRY(gemm(GEMM_PLAIN, dy, (long long)T * h * 2, W.w_oT, nullptr, W.dcat, nullptr, h, h, W.off_T, 1, T,
-                     nullptr, 0, 0, nullptr), "W_o dgrad");
+        MOE_TRY(gemm_t(GEMM_PLAIN, dy, (long long)T * h * 2, w->w_o, nullptr, 0, W.dcat, nullptr, h, h, W.off_T, 1, T),
+                "W_o dgrad");
         MOE_TRY(launch_row_blocks(dy, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.dyT, b.Np_d, st),
                 "row blocks");
         MOE_TRY(launch_row_blocks(sv->y_cat, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.ycT,
@@ -721,10 +720,10 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
     // ---- combine: dYp = w dcat, dw = <dcat, y_perm>
     MOE_TRY(launch_combine_bwd(dc, H, dd, K, p.A, sv->dest_row, sv->topk_w, sv->y_perm, W.dYp, W.dw, st), "combine bwd");
     // ---- routed experts
-    MOE_TRY(gemm(NA == 2 ? GEMM_DSWIGLU : GEMM_DGELU, W.dYp, (long long)N * dd * 2, W.w_downT, nullptr, W.dAU,
-                 sv->act_grad, dd, f, sv->offsets, Et, N, nullptr, 0, 0, nullptr), "expert down dgrad");
-    MOE_TRY(gemm(GEMM_PLAIN, W.dAU, (long long)N * nf * 2, W.w_guT, nullptr, W.dXp, nullptr, (int)nf, dd, sv->offsets,
-                 Et, N, nullptr, 0, 0, nullptr), "expert gate/up dgrad");
+    MOE_TRY(gemm_t(NA == 2 ? GEMM_DSWIGLU : GEMM_DGELU, W.dYp, (long long)N * dd * 2, w->w_down, nullptr, 0, W.dAU,
+                   sv->act_grad, dd, f, sv->offsets, Et, N), "expert down dgrad");
+    MOE_TRY(gemm_t(GEMM_PLAIN, W.dAU, (long long)N * nf * 2, w->w_gate, NA == 2 ? w->w_up : nullptr, NA == 2 ? f : 0,
+                   W.dXp, nullptr, (int)nf, dd, sv->offsets, Et, N), "expert gate/up dgrad");
     MOE_TRY(launch_row_blocks(W.dYp, dd, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, dd, W.dYpT,
                               b.Np_r, st), "row blocks");
     MOE_TRY(launch_row_blocks(sv->h, f, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f, W.hT, b.Np_r,
@@ -760,13 +759,10 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
     }
     // ---- shared expert (H = 1)
     if (b.shared) {
-        MOE_TRY(launch_transpose_batched(w->sh_down, 1, h, f, W.sh_downT, h, 0, st), "transpose");
-        MOE_TRY(launch_transpose_batched(w->sh_gate, 1, f, h, W.sh_guT, (int)nf, 0, st), "transpose");
-        if (NA == 2) MOE_TRY(launch_transpose_batched(w->sh_up, 1, f, h, W.sh_guT, (int)nf, f, st), "transpose");
-        MOE_TRY(gemm(NA == 2 ? GEMM_DSWIGLU : GEMM_DGELU, dc, (long long)T * h * 2, W.sh_downT, nullptr, W.dAUs,
-                     sv->sh_act_grad, h, f, W.off_T, 1, T, nullptr, 0, 0, nullptr), "shared down dgrad");
-        MOE_TRY(gemm(GEMM_PLAIN, W.dAUs, (long long)T * nf * 2, W.sh_guT, nullptr, W.dxs, nullptr, (int)nf, h, W.off_T,
-                     1, T, nullptr, 0, 0, nullptr), "shared gate/up dgrad");
+        MOE_TRY(gemm_t(NA == 2 ? GEMM_DSWIGLU : GEMM_DGELU, dc, (long long)T * h * 2, w->sh_down, nullptr, 0, W.dAUs,
+                       sv->sh_act_grad, h, f, W.off_T, 1, T), "shared down dgrad");
+        MOE_TRY(gemm_t(GEMM_PLAIN, W.dAUs, (long long)T * nf * 2, w->sh_gate, NA == 2 ? w->sh_up : nullptr,
+                       NA == 2 ? f : 0, W.dxs, nullptr, (int)nf, h, W.off_T, 1, T), "shared gate/up dgrad");
         MOE_TRY(launch_row_blocks(dc, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.dcatT, b.Np_d,
                                   st), "row blocks");
         MOE_TRY(launch_row_blocks(sv->sh_h, f, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f, W.shT,

@@ -117,7 +117,7 @@ enum GemmMode { GEMM_SWIGLU = 0, GEMM_GELU = 1, GEMM_PLAIN = 2, GEMM_SWIGLU_SAVE
                 GEMM_DSWIGLU = 5, GEMM_DGELU = 6, GEMM_F32OUT = 7 };
 struct GemmSpec {
     const void* A;          // [rows][K], or [a_mod][K] shared by the groups
-    const void* B0;         // [G][Nout][K], or [Nout][K] with b_shared
+    const void* B0;         // [G][Nout][K], or [Nout][K] with b_shared ([G][K][Nout] with b_kmajor)
     const void* B1;         // gated modes: the up weights, like B0
     void* C;                // [rows][Nout] ([rows][2*Nout] for GEMM_DSWIGLU)
     void* aux;              // SAVE / D modes: pre-activations [rows][n_act*Nout]
@@ -127,6 +127,10 @@ struct GemmSpec {
     const int2* kspan;      // optional per-group {first k stage, k stages}
     int a_mod;              // > 0: tile row r reads A row r % a_mod
     int b_shared;           // 1: one B for all groups
+    int b_kmajor;           // 1: B0/B1 are [G][K][Nout] (the forward weights, for products by their
+                            // transpose); ungated modes only
+    int kb1;                // with b_kmajor: k rows >= kb1 are B1's rows k - kb1 (B0 and B1 then hold
+                            // kb1 rows each per group); 0: every k row is B0's
 };
 size_t grouped_gemm_ws_bytes(int G, int max_rows);  // its tile table
 // bm: 128 or 256 forces the row-tile height, anything else picks it

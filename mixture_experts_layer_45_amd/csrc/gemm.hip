@@ -132,6 +132,7 @@ struct GArgs {
     const int2* kspan;      // per group {first 64-wide k stage, k stages}, or null (0, K/64)
     int a_mod;              // > 0: tile row r reads A row r % a_mod (every group reads the same rows)
     int b_shared;           // 1: every group reads B0 itself (no per-group weight offset)
+    int kb1;                // k-major B only: k rows >= kb1 come from B1 (row k - kb1); 0: all from B0
 };
 
 // the A row behind tile row r, clamped to the nrows rows of A
@@ -404,6 +405,9 @@ struct Ring8Cfg {
 __device__ __forceinline__ int swz32(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) const uint8_t* lds_u8_ptr;
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v* lds_s4_ptr;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt/lgkmcnt at maximum).
@@ -831,6 +835,13 @@ struct K64Cfg {
 
 __device__ __forceinline__ int swz64(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
+// k-major weights (B stored [K][Nout], as the forward weights are when the
+// backward multiplies by their transpose): a stage holds 64 k rows of 512
+// bytes (256 columns).  Row k's 16-byte chunk c sits at chunk c ^ kmaj_swz(k),
+// so that the transposing fragment reads (4 rows x 32 bytes per 16 lanes, 4
+// rows x 64 bytes per 32 lanes) touch distinct LDS banks.
+__device__ __forceinline__ int kmaj_swz(int k) { return ((k & 3) << 1) ^ ((k & 1) << 3); }
+
 
 // fp32 partial tile of one piece: register (ai, 4q..4q+3) of thread tid at
 // float4 index (ai*4 + q)*512 + tid of the slot (coalesced 16-byte stores)
@@ -845,10 +856,14 @@ __device__ __forceinline__ void k64_store_partial(const floatx16* acc, float* pa
             P[(ai * 4 + q) * 512 + tid] = floatx4{acc[ai][4 * q], acc[ai][4 * q + 1], acc[ai][4 * q + 2], acc[ai][4 * q + 3]};
 }
 
-template <int BM, int MODE>
+// BT: B is k-major ([G][K][Nout]); its fragments are read with the LDS
+// transposing load (each 16-lane group turns 4 k rows of 16 columns into 16
+// lanes of 4 consecutive k), two reads per 8-k fragment.
+template <int BM, int MODE, bool BT>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = K64Cfg<BM, MODE>;
+    static_assert(!BT || !gated_mode(MODE), "k-major weights are read by the ungated modes only");
     constexpr int NS = C::NS;
     // the stages, then one word for the tile this block claimed for after the
     // current one (inside the same LDS array, so the compiler sees a single
@@ -881,10 +896,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
     const int a_nrows = (int)(a.a_bytes / rowbytes);
 
+    // k-major B: bytes per k row, and the k rows each matrix holds
+    const uint32_t ldb = (uint32_t)Nout * 2u;
+    const int kmat = BT && a.kb1 > 0 ? a.kb1 : K;
+
     struct Tile {
         int row0, row_end, n0;
         int kb, nkl, slot;  // first k stage, k stages, partial slot (-1: a whole tile)
-        __amdgpu_buffer_rsrc_t rB;
+        __amdgpu_buffer_rsrc_t rB, rB1;
         uint32_t va[C::A_PW], vb[C::B_PW];
     };
     // per-lane byte offsets: lane l fills LDS chunk l%8 of row l/8 of its 8-row
@@ -913,11 +932,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             t.kb = ks.x;
             t.nkl = ks.y;
         }
-        const size_t bgo = a.b_shared ? 0 : (size_t)tl.group * Nout * rowbytes;
-        const uint8_t* B0 = (const uint8_t*)a.B0 + bgo;
-        const uint8_t* B1 = gated_mode(MODE) ? (const uint8_t*)a.B1 + bgo : B0;
-        t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
         const int lr = lane >> 3, pc = lane & 7;
+        if constexpr (BT) {
+            const size_t mbytes = (size_t)kmat * ldb;
+            const size_t bgo = a.b_shared ? 0 : (size_t)tl.group * mbytes;
+            t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.B0 + bgo), (short)0, (int)mbytes, kBufWord3);
+            t.rB1 = a.kb1 > 0 ? __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.B1 + bgo), (short)0, (int)mbytes,
+                                                                  kBufWord3)
+                              : t.rB;
+        } else {
+            const size_t bgo = a.b_shared ? 0 : (size_t)tl.group * Nout * rowbytes;
+            const uint8_t* B0 = (const uint8_t*)a.B0 + bgo;
+            const uint8_t* B1 = gated_mode(MODE) ? (const uint8_t*)a.B1 + bgo : B0;
+            t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes),
+                                                     kBufWord3);
+            t.rB1 = t.rB;
+        }
 #pragma unroll
         for (int i = 0; i < C::A_PW; ++i) {
             const int r = wu * (BM / 8) + 8 * i + lr;
@@ -925,13 +955,26 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
             t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
+        if constexpr (BT) {
+            // load i of wave wu fills k rows 8wu+2i and 8wu+2i+1: lane l the
+            // chunk at position l%32 of row l/32; chunks past Nout (whose
+            // columns are never stored) reread the last real one
 #pragma unroll
-        for (int i = 0; i < C::B_PW; ++i) {
-            const int r = wu * 32 + 8 * i + lr;
-            const int c = pc ^ ((r >> 1) & 7);
-            const int mat = r / C::BNM;
-            const int col = min(t.n0 + r - mat * C::BNM, Nout - 1);
-            t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+            for (int i = 0; i < C::B_PW; ++i) {
+                const int kr = wu * 8 + 2 * i + (lane >> 5);
+                const int c = (lane & 31) ^ kmaj_swz(kr);
+                const int col = min(t.n0 + c * 8, Nout - 8);
+                t.vb[i] = (uint32_t)kr * ldb + (uint32_t)col * 2u - 1024u * i;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::B_PW; ++i) {
+                const int r = wu * 32 + 8 * i + lr;
+                const int c = pc ^ ((r >> 1) & 7);
+                const int mat = r / C::BNM;
+                const int col = min(t.n0 + r - mat * C::BNM, Nout - 1);
+                t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+            }
         }
     };
     // stage ks of the tile's k range
@@ -939,7 +982,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         LdsRun<C::A_PW>::go(rA, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + a_dst), t.va, (t.kb + ks) * 128);
     };
     auto issue_b = [&](const Tile& t, int ks) __attribute__((always_inline)) {
-        LdsRun<C::B_PW>::go(t.rB, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + b_dst), t.vb, (t.kb + ks) * 128);
+        lds_void_ptr dst = (lds_void_ptr)(smem + (ks % NS) * C::STAGE + b_dst);
+        if constexpr (BT) {
+            const int k0 = (t.kb + ks) * 64;
+            if (k0 >= kmat) LdsRun<C::B_PW>::go(t.rB1, dst, t.vb, (int)((uint32_t)(k0 - kmat) * ldb));
+            else LdsRun<C::B_PW>::go(t.rB, dst, t.vb, (int)((uint32_t)k0 * ldb));
+        } else {
+            LdsRun<C::B_PW>::go(t.rB, dst, t.vb, (t.kb + ks) * 128);
+        }
     };
     auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
 #pragma unroll
@@ -956,6 +1006,20 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     };
     // nv: this wave's 32-row blocks that hold rows of the tile (the others are
     // neither read nor multiplied; their accumulators stay zero, stores skip them)
+    // k-major B: lane l's byte offset for column block tn of k step 0 (the
+    // others add 8 KB per k step and 2 KB for the second 4-k read).  Lane
+    // i = l%16 of group g = l/16 reads 4 columns (8 bytes) of k row
+    // 8(g/2) + i/4 starting at column 16(g%2) + 4(i%4) of the block; the read
+    // hands lane i the 4 rows of column 16(g%2) + i.
+    int bt_off[C::TN];
+    if constexpr (BT) {
+        const int kr = 8 * (lane >> 5) + ((lane >> 2) & 3);
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const int chunk = (wn * C::WNM + tn * 32) / 8 + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+            bt_off[tn] = kr * 512 + ((chunk ^ kmaj_swz(kr)) << 4) + 8 * (lane & 1);
+        }
+    }
     auto read_frags = [&](int st, int kk, bf16x8* fr, int nv) __attribute__((always_inline)) {
         const uint8_t* As = smem + st * C::STAGE;
         const uint8_t* Bs = As + C::A_BYTES;
@@ -963,11 +1027,22 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
 #pragma unroll
         for (int tm = 0; tm < C::TM; ++tm)
             if (tm < nv) fr[tm] = *(const bf16x8*)(As + swz64(wm * C::WM + tm * 32 + (lane & 31), ch));
+        if constexpr (BT) {
 #pragma unroll
-        for (int m = 0; m < C::NMAT; ++m)
+            for (int tn = 0; tn < C::TN; ++tn) {
+                const uint8_t* p = Bs + bt_off[tn] + kk * 8192;
+                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_u8_ptr)p);
+                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_u8_ptr)(p + 2048));
+                fr[C::TM + tn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        } else {
 #pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn)
-                fr[C::TM + m * C::TN + tn] = *(const bf16x8*)(Bs + swz64(m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31), ch));
+            for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+                for (int tn = 0; tn < C::TN; ++tn)
+                    fr[C::TM + m * C::TN + tn] =
+                        *(const bf16x8*)(Bs + swz64(m * C::BNM + wn * C::WNM + tn * 32 + (lane & 31), ch));
+        }
     };
     floatx16 acc[C::NACC];
     auto mfmas = [&](const bf16x8* fr, int nv) __attribute__((always_inline)) {
@@ -1209,7 +1284,7 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
         using R = K64Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
         const int pb = persistent_blocks();
-        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(pb), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, false>), dim3(pb), dim3(512), 0, st, g);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || !g.partial) return err;
         hipLaunchKernelGGL((gemm_k64_tail_kernel<BM, MODE>), dim3(8 * kTailSlots), dim3(512), 0, st, g, pb / 8);
@@ -1250,7 +1325,7 @@ static hipError_t run_gemm(int dtype, int BM, int mode, const GArgs& g, hipStrea
 
 // the 64-wide kernel alone, without split tail tiles (the training and
 // backward modes, per-group k ranges)
-template <int BM, int MODE>
+template <int BM, int MODE, bool BT = false>
 static hipError_t run_k64_only(GArgs g, hipStream_t st) {
     using R = K64Cfg<BM, MODE>;
     g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
@@ -1258,11 +1333,12 @@ static hipError_t run_k64_only(GArgs g, hipStream_t st) {
     g.per_xcd = (g.total + 7) / 8;
     g.partial = nullptr;
     if (g.total == 0) return hipSuccess;
-    const long long b_bytes = (long long)g.Nout * g.K * 2;
+    const long long b_bytes = (long long)g.Nout * (BT && g.kb1 > 0 ? g.kb1 : g.K) * 2;
     if (g.a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31) || g.K % 64 != 0 || g.Nout % 8 != 0 ||
         ((uintptr_t)g.C & 15) != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+    if (BT && g.kb1 != 0 && (g.kb1 < 0 || g.kb1 % 64 != 0 || g.kb1 >= g.K || !g.B1)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, BT>), dim3(persistent_blocks()), dim3(512), 0, st, g);
     return hipGetLastError();
 }
 
@@ -1280,7 +1356,19 @@ static hipError_t run_ring8_save(GArgs g, hipStream_t st) {
     return hipGetLastError();
 }
 
-static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st) {
+static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st, bool b_kmajor = false) {
+    if (b_kmajor) {
+        switch (mode) {
+            case MODE_PLAIN:
+                return BM == 256 ? run_k64_only<256, MODE_PLAIN, true>(g, st) : run_k64_only<128, MODE_PLAIN, true>(g, st);
+            case MODE_DSWIGLU:
+                return BM == 256 ? run_k64_only<256, MODE_DSWIGLU, true>(g, st)
+                                 : run_k64_only<128, MODE_DSWIGLU, true>(g, st);
+            case MODE_DGELU:
+                return BM == 256 ? run_k64_only<256, MODE_DGELU, true>(g, st) : run_k64_only<128, MODE_DGELU, true>(g, st);
+        }
+        return hipErrorInvalidValue;
+    }
     if (mode == MODE_SWIGLU_SAVE && BM == 256 && g.K >= 4096 && g.K % 32 == 0 && g.Nout % 8 == 0 &&
         ((uintptr_t)g.C & 15) == 0 && g.a_bytes < (1ll << 31) && (long long)g.Nout * g.K * 2 < (1ll << 31) &&
         !g.kspan && !g.a_mod && !g.b_shared)
@@ -1412,7 +1500,8 @@ hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offse
     g.kspan = s.kspan;
     g.a_mod = s.a_mod;
     g.b_shared = s.b_shared;
-    return run_k64_mode(BM, mode, g, st);
+    g.kb1 = s.kb1;
+    return run_k64_mode(BM, mode, g, st, s.b_kmajor != 0);
 }
 
 hipError_t launch_set2(int32_t* p, int32_t a, int32_t b, hipStream_t st) {
