@@ -842,6 +842,13 @@ __device__ __forceinline__ int swz64(int row, int chunk) { return row * 128 + ((
 // rows x 64 bytes per 32 lanes) touch distinct LDS banks.
 __device__ __forceinline__ int kmaj_swz(int k) { return ((k & 3) << 1) ^ ((k & 1) << 3); }
 
+// One transposing LDS read.  Through a restrict parameter the inlined read
+// carries alias-scope information, without which the compiler waits for every
+// LDS-DMA load in flight (the next stage's prefetch) before it.
+__device__ __forceinline__ short4v lds_read_tr16(const uint8_t* __restrict__ p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_u8_ptr)p);
+}
+
 
 // fp32 partial tile of one piece: register (ai, 4q..4q+3) of thread tid at
 // float4 index (ai*4 + q)*512 + tid of the slot (coalesced 16-byte stores)
@@ -1031,8 +1038,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
 #pragma unroll
             for (int tn = 0; tn < C::TN; ++tn) {
                 const uint8_t* p = Bs + bt_off[tn] + kk * 8192;
-                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_u8_ptr)p);
-                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(lds_u8_ptr)(p + 2048));
+                const short4v lo = lds_read_tr16(p);
+                const short4v hi = lds_read_tr16(p + 2048);
                 fr[C::TM + tn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         } else {
