@@ -180,8 +180,8 @@ LayerWs carve_layer(Carver& c, const Plan& p, const moe_desc* d) {
 
 // ---- backward pass: sizes and workspace
 struct BwdPlan {
-    int NA, Ep, ms_r, ms_d, ms_h;
-    long long Np_r, Np_d, Np_h;
+    int NA, Ep, ms_h;
+    long long Np_h;
     bool router, shared, wo;
 };
 BwdPlan bwd_plan_of(const moe_desc* d, const Plan& p) {
@@ -189,11 +189,7 @@ BwdPlan bwd_plan_of(const moe_desc* d, const Plan& p) {
     b.NA = d->act == MOE_SWIGLU ? 2 : 1;
     b.Ep = (p.E + 63) / 64 * 64;
     const int tst = (p.T + 63) / 64;
-    b.ms_r = (p.max_rows + 63) / 64 + p.Et;
-    b.ms_d = tst + 1;
     b.ms_h = p.H * (tst + 1);
-    b.Np_r = 64ll * b.ms_r;
-    b.Np_d = 64ll * b.ms_d;
     b.Np_h = 64ll * b.ms_h;
     b.router = d->gate == MOE_GATE_TOPK;
     b.shared = d->n_shared != 0;
@@ -202,12 +198,12 @@ BwdPlan bwd_plan_of(const moe_desc* d, const Plan& p) {
 }
 
 struct BwdWs {
-    int2 *kspan_r, *kspan_d, *kspan_h;
-    int32_t *stage_r, *stage_d, *stage_h, *off_T, *off_h, *off_w, *off_f, *off_E, *off_hr, *off_fr;
+    int2* kspan_h;
+    int32_t *stage_h, *off_T, *off_h, *off_w, *off_f, *off_E, *off_hr, *off_fr;
     void* wgT;
     void *dcat, *dYp, *dAU, *dXp, *dl, *dxr, *dAUs, *dxs;
     float* dw;
-    void *dYpT, *hT, *dAT, *dUT, *xpT, *dlT, *xhT, *dcatT, *shT, *dAsT, *dUsT, *xT, *dyT, *ycT;
+    void *xp, *dlT, *xhT;
     GemmTile* tiles;
 };
 
@@ -233,10 +229,6 @@ BwdWs carve_bwd(Carver& c, const Plan& p, const BwdPlan& b) {
     BwdWs w{};
     const size_t e2 = 2;  // bf16
     const size_t N = p.max_rows, T = p.T, S = (size_t)p.T * p.H, nf = (size_t)b.NA * p.f;
-    w.kspan_r = c.take<int2>(p.Et);
-    w.stage_r = c.take<int32_t>(b.ms_r);
-    w.kspan_d = c.take<int2>(1);
-    w.stage_d = c.take<int32_t>(b.ms_d);
     w.kspan_h = c.take<int2>(p.H);
     w.stage_h = c.take<int32_t>(b.ms_h);
     w.off_T = c.take<int32_t>(2);
@@ -250,11 +242,7 @@ BwdWs carve_bwd(Carver& c, const Plan& p, const BwdPlan& b) {
     w.dw = c.take<float>((size_t)p.A + 1);
     w.dAU = c.take<char>(N * nf * e2 + 16);
     w.dXp = c.take<char>(N * p.d * e2 + 16);
-    w.dYpT = c.take<char>((size_t)p.d * b.Np_r * e2);
-    w.hT = c.take<char>((size_t)p.f * b.Np_r * e2);
-    w.dAT = c.take<char>((size_t)p.f * b.Np_r * e2);
-    if (b.NA == 2) w.dUT = c.take<char>((size_t)p.f * b.Np_r * e2);
-    w.xpT = c.take<char>((size_t)p.d * b.Np_r * e2);
+    w.xp = c.take<char>(N * p.d * e2 + 16);
     if (b.router) {
         w.wgT = c.take<char>((size_t)p.H * p.d * b.Ep * e2);
         w.dl = c.take<char>(S * b.Ep * e2);
@@ -264,17 +252,10 @@ BwdWs carve_bwd(Carver& c, const Plan& p, const BwdPlan& b) {
     }
     if (b.wo) {
         w.dcat = c.take<char>(T * p.h * e2 + 16);
-        w.dyT = c.take<char>((size_t)p.h * b.Np_d * e2);
-        w.ycT = c.take<char>((size_t)p.h * b.Np_d * e2);
     }
     if (b.shared) {
         w.dAUs = c.take<char>(T * nf * e2 + 16);
         w.dxs = c.take<char>(T * p.h * e2 + 16);
-        w.dcatT = c.take<char>((size_t)p.h * b.Np_d * e2);
-        w.shT = c.take<char>((size_t)p.f * b.Np_d * e2);
-        w.dAsT = c.take<char>((size_t)p.f * b.Np_d * e2);
-        if (b.NA == 2) w.dUsT = c.take<char>((size_t)p.f * b.Np_d * e2);
-        w.xT = c.take<char>((size_t)p.h * b.Np_d * e2);
     }
     w.tiles = c.take<GemmTile>(bwd_tiles_bytes(p, b) / sizeof(GemmTile) + 1);
     return w;
@@ -661,10 +642,10 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
     // the 64-wide kernel addresses each operand through a 32-bit buffer range
     const long long lim = 1ll << 31;
     const long long nf = (long long)b.NA * p.f;
-    if ((long long)p.f * b.Np_r * 2 >= lim || (long long)p.d * b.Np_r * 2 >= lim || (long long)p.max_rows * nf * 2 >= lim ||
+    if ((long long)p.max_rows * p.f * 2 >= lim || (long long)p.max_rows * nf * 2 >= lim ||
         (long long)p.max_rows * p.d * 2 >= lim || (long long)p.f * p.d * 2 >= lim || (long long)p.d * nf * 2 >= lim ||
-        (long long)b.Ep * b.Np_h * 2 >= lim || (long long)p.d * b.Np_h * 2 >= lim || (long long)p.h * b.Np_d * 2 >= lim ||
-        (long long)p.f * b.Np_d * 2 >= lim || (long long)p.T * p.h * 2 >= lim)
+        (long long)b.Ep * b.Np_h * 2 >= lim || (long long)p.d * b.Np_h * 2 >= lim || (long long)p.T * nf * 2 >= lim ||
+        (long long)p.T * p.f * 2 >= lim || (long long)p.T * p.h * 2 >= lim)
         return fail(MOE_ERR_UNSUPPORTED, "an operand of the backward GEMMs exceeds 2 GB");
     const size_t need = ws_bytes_of(d, MOE_WS_BACKWARD);
     if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
@@ -684,13 +665,22 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
         gs.a_rows = a_rows; gs.kspan = kspan; gs.a_mod = a_mod; gs.b_shared = b_shared;
         return launch_grouped_gemm(mode, gs, offs, G, rows, W.tiles, st);
     };
+    // weight gradient: C rows [g*m, (g+1)*m) of group g = sum over its rows k in
+    // [krows[g], krows[g+1]) of A[k][0:m]^T B[k][0:Nout] (A, B as stored)
+    auto wgrad = [&](const void* A, long long a_bytes, int lda, int m, const void* B, long long b_bytes, int ldb, void* C,
+                     int Nout, const int32_t* krows, const int32_t* c_offs, int G) -> hipError_t {
+        GemmSpec gs{};
+        gs.A = A; gs.B0 = B; gs.C = C; gs.K = 64; gs.Nout = Nout; gs.a_bytes = a_bytes; gs.a_mod = m;
+        gs.kmajor = 2; gs.krows = krows; gs.lda = lda; gs.ldb = ldb; gs.b_bytes = b_bytes;
+        return launch_grouped_gemm(GEMM_PLAIN, gs, c_offs, G, G * m, W.tiles, st);
+    };
     // C = A B with B the forward weights as stored ([G][K][Nout]: the product by
     // their transpose); with B1, k rows >= kb1 are B1's
     auto gemm_t = [&](int mode, const void* A, long long a_bytes, const void* B0, const void* B1, int kb1, void* C,
                       void* aux, int Kc, int Nout, const int32_t* offs, int G, int rows) -> hipError_t {
         GemmSpec gs{};
         gs.A = A; gs.B0 = B0; gs.B1 = B1; gs.C = C; gs.aux = aux; gs.K = Kc; gs.Nout = Nout; gs.a_bytes = a_bytes;
-        gs.b_kmajor = 1; gs.kb1 = kb1;
+        gs.kmajor = 1; gs.kb1 = kb1;
         return launch_grouped_gemm(mode, gs, offs, G, rows, W.tiles, st);
     };
     // ---- group tables
@@ -701,20 +691,14 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
     MOE_TRY(launch_iota(W.off_w, Et, dd, st), "offsets");
     MOE_TRY(launch_iota(W.off_f, Et, f, st), "offsets");
     MOE_TRY(launch_iota(W.off_E, H, E, st), "offsets");
-    MOE_TRY(launch_kspan(sv->offsets, Et, b.ms_r, W.kspan_r, W.stage_r, st), "row-block table");
-    MOE_TRY(launch_kspan(W.off_T, 1, b.ms_d, W.kspan_d, W.stage_d, st), "row-block table");
     MOE_TRY(launch_kspan(W.off_h, H, b.ms_h, W.kspan_h, W.stage_h, st), "row-block table");
     const void* dc = dy;
     // ---- W_o: dcat = dy W_o, dW_o = dy^T y_cat
     if (b.wo) {
         MOE_TRY(gemm_t(GEMM_PLAIN, dy, (long long)T * h * 2, w->w_o, nullptr, 0, W.dcat, nullptr, h, h, W.off_T, 1, T),
                 "W_o dgrad");
-        MOE_TRY(launch_row_blocks(dy, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.dyT, b.Np_d, st),
-                "row blocks");
-        MOE_TRY(launch_row_blocks(sv->y_cat, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.ycT,
-                                  b.Np_d, st), "row blocks");
-        MOE_TRY(gemm(GEMM_PLAIN, W.dyT, (long long)h * b.Np_d * 2, W.ycT, nullptr, gr->w_o, nullptr, (int)b.Np_d, h,
-                     W.off_hr, 1, h, W.kspan_d, 0, 1, nullptr), "W_o wgrad");
+        MOE_TRY(wgrad(dy, (long long)T * h * 2, h, h, sv->y_cat, (long long)T * h * 2, h, gr->w_o, h, W.off_T, W.off_hr, 1),
+                "W_o wgrad");
         dc = W.dcat;
     }
     // ---- combine: dYp = w dcat, dw = <dcat, y_perm>
@@ -724,24 +708,15 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
                    sv->act_grad, dd, f, sv->offsets, Et, N), "expert down dgrad");
     MOE_TRY(gemm_t(GEMM_PLAIN, W.dAU, (long long)N * nf * 2, w->w_gate, NA == 2 ? w->w_up : nullptr, NA == 2 ? f : 0,
                    W.dXp, nullptr, (int)nf, dd, sv->offsets, Et, N), "expert gate/up dgrad");
-    MOE_TRY(launch_row_blocks(W.dYp, dd, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, dd, W.dYpT,
-                              b.Np_r, st), "row blocks");
-    MOE_TRY(launch_row_blocks(sv->h, f, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f, W.hT, b.Np_r,
-                              st), "row blocks");
-    MOE_TRY(launch_row_blocks(W.dAU, (int)nf, 0, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f, W.dAT,
-                              b.Np_r, st), "row blocks");
+    MOE_TRY(launch_gather_rows(x, sv->src_token, T * H, sv->offsets + Et, N, dd, W.xp, st), "gather x");
+    const long long nb = (long long)N * nf * 2;
+    MOE_TRY(wgrad(W.dYp, (long long)N * dd * 2, dd, dd, sv->h, (long long)N * f * 2, f, gr->w_down, f, sv->offsets,
+                  W.off_w, Et), "expert down wgrad");
+    MOE_TRY(wgrad(W.dAU, nb, (int)nf, f, W.xp, (long long)N * dd * 2, dd, gr->w_gate, dd, sv->offsets, W.off_f, Et),
+            "expert gate wgrad");
     if (NA == 2)
-        MOE_TRY(launch_row_blocks(W.dAU, (int)nf, f, 0, nullptr, N, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, f,
-                                  W.dUT, b.Np_r, st), "row blocks");
-    MOE_TRY(launch_row_blocks(x, dd, 0, 0, sv->src_token, T * H, 0, sv->offsets, W.kspan_r, W.stage_r, b.ms_r, dd,
-                              W.xpT, b.Np_r, st), "row blocks");
-    MOE_TRY(gemm(GEMM_PLAIN, W.dYpT, (long long)dd * b.Np_r * 2, W.hT, nullptr, gr->w_down, nullptr, (int)b.Np_r, f,
-                 W.off_w, Et, Et * dd, W.kspan_r, dd, 1, nullptr), "expert down wgrad");
-    MOE_TRY(gemm(GEMM_PLAIN, W.dAT, (long long)f * b.Np_r * 2, W.xpT, nullptr, gr->w_gate, nullptr, (int)b.Np_r, dd,
-                 W.off_f, Et, Et * f, W.kspan_r, f, 1, nullptr), "expert gate wgrad");
-    if (NA == 2)
-        MOE_TRY(gemm(GEMM_PLAIN, W.dUT, (long long)f * b.Np_r * 2, W.xpT, nullptr, gr->w_up, nullptr, (int)b.Np_r, dd,
-                     W.off_f, Et, Et * f, W.kspan_r, f, 1, nullptr), "expert up wgrad");
+        MOE_TRY(wgrad((const char*)W.dAU + (size_t)f * 2, nb - (long long)f * 2, (int)nf, f, W.xp, (long long)N * dd * 2,
+                      dd, gr->w_up, dd, sv->offsets, W.off_f, Et), "expert up wgrad");
     // ---- router: through the gate weights and the aux loss
     if (router) {
         const float caux = aux_weight * d->aux_alpha * (float)E / ((float)H * (float)T);
@@ -763,24 +738,14 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
                        sv->sh_act_grad, h, f, W.off_T, 1, T), "shared down dgrad");
         MOE_TRY(gemm_t(GEMM_PLAIN, W.dAUs, (long long)T * nf * 2, w->sh_gate, NA == 2 ? w->sh_up : nullptr,
                        NA == 2 ? f : 0, W.dxs, nullptr, (int)nf, h, W.off_T, 1, T), "shared gate/up dgrad");
-        MOE_TRY(launch_row_blocks(dc, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.dcatT, b.Np_d,
-                                  st), "row blocks");
-        MOE_TRY(launch_row_blocks(sv->sh_h, f, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f, W.shT,
-                                  b.Np_d, st), "row blocks");
-        MOE_TRY(launch_row_blocks(W.dAUs, (int)nf, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f, W.dAsT,
-                                  b.Np_d, st), "row blocks");
+        const long long sb = (long long)T * nf * 2;
+        MOE_TRY(wgrad(dc, (long long)T * h * 2, h, h, sv->sh_h, (long long)T * f * 2, f, gr->sh_down, f, W.off_T, W.off_hr,
+                      1), "shared down wgrad");
+        MOE_TRY(wgrad(W.dAUs, sb, (int)nf, f, x, (long long)T * h * 2, h, gr->sh_gate, h, W.off_T, W.off_fr, 1),
+                "shared gate wgrad");
         if (NA == 2)
-            MOE_TRY(launch_row_blocks(W.dAUs, (int)nf, f, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, f,
-                                      W.dUsT, b.Np_d, st), "row blocks");
-        MOE_TRY(launch_row_blocks(x, h, 0, 0, nullptr, T, 0, W.off_T, W.kspan_d, W.stage_d, b.ms_d, h, W.xT, b.Np_d, st),
-                "row blocks");
-        MOE_TRY(gemm(GEMM_PLAIN, W.dcatT, (long long)h * b.Np_d * 2, W.shT, nullptr, gr->sh_down, nullptr, (int)b.Np_d, f,
-                     W.off_hr, 1, h, W.kspan_d, 0, 1, nullptr), "shared down wgrad");
-        MOE_TRY(gemm(GEMM_PLAIN, W.dAsT, (long long)f * b.Np_d * 2, W.xT, nullptr, gr->sh_gate, nullptr, (int)b.Np_d, h,
-                     W.off_fr, 1, f, W.kspan_d, 0, 1, nullptr), "shared gate wgrad");
-        if (NA == 2)
-            MOE_TRY(gemm(GEMM_PLAIN, W.dUsT, (long long)f * b.Np_d * 2, W.xT, nullptr, gr->sh_up, nullptr, (int)b.Np_d,
-                         h, W.off_fr, 1, f, W.kspan_d, 0, 1, nullptr), "shared up wgrad");
+            MOE_TRY(wgrad((const char*)W.dAUs + (size_t)f * 2, sb - (long long)f * 2, (int)nf, f, x, (long long)T * h * 2,
+                          h, gr->sh_up, h, W.off_T, W.off_fr, 1), "shared up wgrad");
     }
     // ---- dx
     MOE_TRY(launch_dx(W.dXp, sv->dest_row, T, H, dd, K, router ? W.dxr : nullptr, b.shared ? W.dxs : nullptr, gr->dx, st),

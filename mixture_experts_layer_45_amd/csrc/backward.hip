@@ -9,15 +9,19 @@
 // aux loss through P_i, and finally dx as the sum of the rows' input
 // gradients and the router's.  Selection itself is piecewise constant.
 //
-// The heavy products run on the grouped 64-wide GEMM kernel (gemm.hip):
-//   * input gradients (dgrad) need each weight with its other index
-//     contiguous, so the weights are first transposed into the workspace;
-//   * weight gradients (wgrad) sum over an expert's rows, so the activations
-//     are transposed into "row blocks": for group g with n_g rows, a column
-//     segment of max(1, ceil(n_g / 64)) 64-wide stages starting at stage kb_g
-//     (the prefix of the earlier groups' stage counts), zero-filled past n_g.
-//     The GEMM then reads, for group g, only the stages [kb_g, kb_g + nk_g) of
-//     every row of both operands.
+// The heavy products run on the grouped 64-wide GEMM kernel (gemm.hip), which
+// reads k-major operands where they lie through the LDS transposing load:
+//   * input gradients (dgrad) multiply by each weight's transpose, reading the
+//     forward weights as stored;
+//   * weight gradients (wgrad) sum over an expert's rows: both operands are
+//     the activations as stored (rows of a group contiguous); the x rows of
+//     the gate/up gradients are first gathered into routed order.
+// The router's weight gradient (per-head column slices of x, a small product)
+// still uses "row blocks": for group g with n_g rows, a column segment of
+// max(1, ceil(n_g / 64)) 64-wide stages starting at stage kb_g (the prefix of
+// the earlier groups' stage counts), zero-filled past n_g; the GEMM then reads,
+// for group g, only the stages [kb_g, kb_g + nk_g) of every row of both
+// operands.
 #include "common.hpp"
 
 namespace moe {
@@ -374,6 +378,26 @@ hipError_t launch_row_blocks(const void* in, int ld_in, int col0, int gcol, cons
     if (max_stages <= 0 || ncols <= 0) return hipSuccess;
     hipLaunchKernelGGL(row_blocks_kernel, dim3(ncols / 64, max_stages), dim3(256), 0, st, (const uint16_t*)in, ld_in,
                        col0, gcol, rowmap, nrows_in, local_rows, offsets, kspan, stage_grp, (uint16_t*)out, ld_out);
+    return hipGetLastError();
+}
+
+// out[r] = in[rowmap[r]] (rows of ncols elements) for r < *n_rows; one block per row
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* in, const int32_t* rowmap, int nrows_in,
+                                                          const int32_t* n_rows, int ncols, uint16_t* out) {
+    const int r = blockIdx.x;
+    if (r >= *n_rows) return;
+    const int src = min(max(rowmap[r], 0), nrows_in - 1);
+    const u32x4* a = (const u32x4*)(in + (size_t)src * ncols);
+    u32x4* b = (u32x4*)(out + (size_t)r * ncols);
+    for (int c = threadIdx.x; c < ncols / 8; c += 256) b[c] = a[c];
+}
+
+hipError_t launch_gather_rows(const void* in, const int32_t* rowmap, int nrows_in, const int32_t* n_rows, int max_rows,
+                              int ncols, void* out, hipStream_t st) {
+    if (max_rows <= 0 || ncols <= 0) return hipSuccess;
+    if (ncols % 8 != 0 || ((uintptr_t)in & 15) != 0 || ((uintptr_t)out & 15) != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(max_rows), dim3(256), 0, st, (const uint16_t*)in, rowmap, nrows_in,
+                       n_rows, ncols, (uint16_t*)out);
     return hipGetLastError();
 }
 

@@ -127,10 +127,15 @@ struct GemmSpec {
     const int2* kspan;      // optional per-group {first k stage, k stages}
     int a_mod;              // > 0: tile row r reads A row r % a_mod
     int b_shared;           // 1: one B for all groups
-    int b_kmajor;           // 1: B0/B1 are [G][K][Nout] (the forward weights, for products by their
-                            // transpose); ungated modes only
-    int kb1;                // with b_kmajor: k rows >= kb1 are B1's rows k - kb1 (B0 and B1 then hold
-                            // kb1 rows each per group); 0: every k row is B0's
+    int kmajor;             // 1: B0/B1 are [G][K][Nout] (the forward weights, for products by their
+                            // transpose); ungated modes only.  2: A [rows][lda] and B0 [rows][ldb] are
+                            // both k-major and group g sums their rows [krows[g], krows[g+1]) into its
+                            // C rows (C row r of the group: column r % a_mod of A); plain mode only
+    int kb1;                // kmajor 1: k rows >= kb1 are B1's rows k - kb1 (B0 and B1 then hold kb1
+                            // rows each per group); 0: every k row is B0's
+    const int32_t* krows;   // kmajor 2: the groups' k row ranges (G + 1 entries)
+    int lda, ldb;           // kmajor 2: row strides of A and B0 in elements
+    long long b_bytes;      // kmajor 2: bytes of B0 the loads may address
 };
 size_t grouped_gemm_ws_bytes(int G, int max_rows);  // its tile table
 // bm: 128 or 256 forces the row-tile height, anything else picks it
@@ -172,6 +177,8 @@ hipError_t launch_kspan(const int32_t* offsets, int G, int max_stages, int2* ksp
 hipError_t launch_row_blocks(const void* in, int ld_in, int col0, int gcol, const int32_t* rowmap, int nrows_in,
                              int local_rows, const int32_t* offsets, const int2* kspan, const int32_t* stage_grp,
                              int max_stages, int ncols, void* out, long long ld_out, hipStream_t st);
+hipError_t launch_gather_rows(const void* in, const int32_t* rowmap, int nrows_in, const int32_t* n_rows, int max_rows,
+                              int ncols, void* out, hipStream_t st);
 hipError_t launch_transpose_batched(const void* in, int B, int R, int Cc, void* out, int ld_out, int out_col0,
                                     hipStream_t st);
 hipError_t launch_iota(int32_t* out, int n, int step, hipStream_t st);

@@ -133,6 +133,11 @@ struct GArgs {
     int a_mod;              // > 0: tile row r reads A row r % a_mod (every group reads the same rows)
     int b_shared;           // 1: every group reads B0 itself (no per-group weight offset)
     int kb1;                // k-major B only: k rows >= kb1 come from B1 (row k - kb1); 0: all from B0
+    // both operands k-major (A [rows][lda], B [rows][ldb], C row r = group g's
+    // row r % a_mod): group g sums k rows [krows[g], krows[g+1]) of both
+    const int32_t* krows;
+    int lda, ldb;           // row strides in elements (k-major B alone: ldb 0 = Nout)
+    long long b_bytes;      // bytes of B the loads may address
 };
 
 // the A row behind tile row r, clamped to the nrows rows of A
@@ -863,14 +868,21 @@ __device__ __forceinline__ void k64_store_partial(const floatx16* acc, float* pa
             P[(ai * 4 + q) * 512 + tid] = floatx4{acc[ai][4 * q], acc[ai][4 * q + 1], acc[ai][4 * q + 2], acc[ai][4 * q + 3]};
 }
 
-// BT: B is k-major ([G][K][Nout]); its fragments are read with the LDS
+// KM = 1: B is k-major ([G][K][Nout]); its fragments are read with the LDS
 // transposing load (each 16-lane group turns 4 k rows of 16 columns into 16
-// lanes of 4 consecutive k), two reads per 8-k fragment.
-template <int BM, int MODE, bool BT>
+// lanes of 4 consecutive k), two reads per 8-k fragment.  KM = 2: A and B are
+// both k-major, as the activations of a weight gradient are stored ([rows][.]
+// with the rows of every group contiguous); group g's k range is its rows
+// [krows[g], krows[g+1]), and the rows of a last stage past it load as zeros
+// (their offsets are put past the buffer's range, which the load turns into
+// zeros).
+template <int BM, int MODE, int KM>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = K64Cfg<BM, MODE>;
+    constexpr bool BT = KM >= 1, AT = KM == 2;
     static_assert(!BT || !gated_mode(MODE), "k-major weights are read by the ungated modes only");
+    static_assert(!AT || BM == 256, "k-major activations fill 64 rows of 512 bytes per stage");
     constexpr int NS = C::NS;
     // the stages, then one word for the tile this block claimed for after the
     // current one (inside the same LDS array, so the compiler sees a single
@@ -903,13 +915,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
     const int a_nrows = (int)(a.a_bytes / rowbytes);
 
-    // k-major B: bytes per k row, and the k rows each matrix holds
-    const uint32_t ldb = (uint32_t)Nout * 2u;
+    // k-major operands: bytes per k row, and the k rows each weight matrix holds
+    const uint32_t ldb = (uint32_t)(AT || a.ldb > 0 ? a.ldb : Nout) * 2u;
+    const uint32_t lda = (uint32_t)a.lda * 2u;
     const int kmat = BT && a.kb1 > 0 ? a.kb1 : K;
 
     struct Tile {
         int row0, row_end, n0;
-        int kb, nkl, slot;  // first k stage, k stages, partial slot (-1: a whole tile)
+        int kb, nkl, slot;  // first k stage (KM = 2: first k row), k stages, partial slot (-1: a whole tile)
+        int kend;           // KM = 2: the group's end row
         __amdgpu_buffer_rsrc_t rB, rB1;
         uint32_t va[C::A_PW], vb[C::B_PW];
     };
@@ -939,8 +953,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             t.kb = ks.x;
             t.nkl = ks.y;
         }
+        if constexpr (AT) {  // at least one stage, so that an empty group stores zeros
+            t.kb = a.krows[tl.group];
+            t.kend = a.krows[tl.group + 1];
+            t.nkl = max(1, (t.kend - t.kb + 63) / 64);
+        }
         const int lr = lane >> 3, pc = lane & 7;
-        if constexpr (BT) {
+        if constexpr (AT) {
+            t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)a.B0, (short)0, (int)a.b_bytes, kBufWord3);
+            t.rB1 = t.rB;
+        } else if constexpr (BT) {
             const size_t mbytes = (size_t)kmat * ldb;
             const size_t bgo = a.b_shared ? 0 : (size_t)tl.group * mbytes;
             t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.B0 + bgo), (short)0, (int)mbytes, kBufWord3);
@@ -955,12 +977,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
                                                      kBufWord3);
             t.rB1 = t.rB;
         }
+        if constexpr (AT) {
+            // as the k-major B below, columns = this tile's rows of the group
+            const int m0 = t.row0 % a.a_mod;
 #pragma unroll
-        for (int i = 0; i < C::A_PW; ++i) {
-            const int r = wu * (BM / 8) + 8 * i + lr;
-            const int c = pc ^ ((r >> 1) & 7);
-            const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
-            t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+            for (int i = 0; i < C::A_PW; ++i) {
+                const int kr = wu * 8 + 2 * i + (lane >> 5);
+                const int c = (lane & 31) ^ kmaj_swz(kr);
+                const int col = min(m0 + c * 8, a.a_mod - 8);
+                t.va[i] = (uint32_t)kr * lda + (uint32_t)col * 2u - 1024u * i;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::A_PW; ++i) {
+                const int r = wu * (BM / 8) + 8 * i + lr;
+                const int c = pc ^ ((r >> 1) & 7);
+                const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
+                t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
+            }
         }
         if constexpr (BT) {
             // load i of wave wu fills k rows 8wu+2i and 8wu+2i+1: lane l the
@@ -984,13 +1018,32 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             }
         }
     };
+    // KM = 2: the offsets of stage ks, with the rows at or past the group's end
+    // moved out of the buffer's range (they load as zeros); load i covers k
+    // rows 8wu+2i (lanes 0-31) and 8wu+2i+1 (lanes 32-63) of the stage
+    auto masked = [&](const Tile& t, int ks, const uint32_t* v, uint32_t* m) __attribute__((always_inline)) {
+        const int rem = t.kend - (t.kb + 64 * ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m[i] = wu * 8 + 2 * i + (lane >> 5) < rem ? v[i] : 0x80000000u;
+    };
     // stage ks of the tile's k range
     auto issue_a = [&](const Tile& t, int ks) __attribute__((always_inline)) {
-        LdsRun<C::A_PW>::go(rA, (lds_void_ptr)(smem + (ks % NS) * C::STAGE + a_dst), t.va, (t.kb + ks) * 128);
+        lds_void_ptr dst = (lds_void_ptr)(smem + (ks % NS) * C::STAGE + a_dst);
+        if constexpr (AT) {
+            uint32_t m[C::A_PW];
+            masked(t, ks, t.va, m);
+            LdsRun<C::A_PW>::go(rA, dst, m, (int)((uint32_t)(t.kb + 64 * ks) * lda));
+        } else {
+            LdsRun<C::A_PW>::go(rA, dst, t.va, (t.kb + ks) * 128);
+        }
     };
     auto issue_b = [&](const Tile& t, int ks) __attribute__((always_inline)) {
         lds_void_ptr dst = (lds_void_ptr)(smem + (ks % NS) * C::STAGE + b_dst);
-        if constexpr (BT) {
+        if constexpr (AT) {
+            uint32_t m[C::B_PW];
+            masked(t, ks, t.vb, m);
+            LdsRun<C::B_PW>::go(t.rB, dst, m, (int)((uint32_t)(t.kb + 64 * ks) * ldb));
+        } else if constexpr (BT) {
             const int k0 = (t.kb + ks) * 64;
             if (k0 >= kmat) LdsRun<C::B_PW>::go(t.rB1, dst, t.vb, (int)((uint32_t)(k0 - kmat) * ldb));
             else LdsRun<C::B_PW>::go(t.rB, dst, t.vb, (int)((uint32_t)k0 * ldb));
@@ -1018,22 +1071,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     // i = l%16 of group g = l/16 reads 4 columns (8 bytes) of k row
     // 8(g/2) + i/4 starting at column 16(g%2) + 4(i%4) of the block; the read
     // hands lane i the 4 rows of column 16(g%2) + i.
-    int bt_off[C::TN];
+    // (k-major A alike, with column block wm*WM + 32 tm)
+    int bt_off[C::TN], at_off[C::TM];
     if constexpr (BT) {
         const int kr = 8 * (lane >> 5) + ((lane >> 2) & 3);
+        auto off = [&](int col0) {
+            const int chunk = col0 / 8 + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+            return kr * 512 + ((chunk ^ kmaj_swz(kr)) << 4) + 8 * (lane & 1);
+        };
 #pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn) {
-            const int chunk = (wn * C::WNM + tn * 32) / 8 + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
-            bt_off[tn] = kr * 512 + ((chunk ^ kmaj_swz(kr)) << 4) + 8 * (lane & 1);
-        }
+        for (int tn = 0; tn < C::TN; ++tn) bt_off[tn] = off(wn * C::WNM + tn * 32);
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) at_off[tm] = off(wm * C::WM + tm * 32);
     }
     auto read_frags = [&](int st, int kk, bf16x8* fr, int nv) __attribute__((always_inline)) {
         const uint8_t* As = smem + st * C::STAGE;
         const uint8_t* Bs = As + C::A_BYTES;
         const int ch = kk * 2 + (lane >> 5);
+        if constexpr (AT) {
 #pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm)
-            if (tm < nv) fr[tm] = *(const bf16x8*)(As + swz64(wm * C::WM + tm * 32 + (lane & 31), ch));
+            for (int tm = 0; tm < C::TM; ++tm)
+                if (tm < nv) {
+                    const uint8_t* p = As + at_off[tm] + kk * 8192;
+                    const short4v lo = lds_read_tr16(p);
+                    const short4v hi = lds_read_tr16(p + 2048);
+                    fr[tm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+        } else {
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+                if (tm < nv) fr[tm] = *(const bf16x8*)(As + swz64(wm * C::WM + tm * 32 + (lane & 31), ch));
+        }
         if constexpr (BT) {
 #pragma unroll
             for (int tn = 0; tn < C::TN; ++tn) {
@@ -1291,7 +1359,7 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
         using R = K64Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
         const int pb = persistent_blocks();
-        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, false>), dim3(pb), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, 0>), dim3(pb), dim3(512), 0, st, g);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess || !g.partial) return err;
         hipLaunchKernelGGL((gemm_k64_tail_kernel<BM, MODE>), dim3(8 * kTailSlots), dim3(512), 0, st, g, pb / 8);
@@ -1332,8 +1400,9 @@ static hipError_t run_gemm(int dtype, int BM, int mode, const GArgs& g, hipStrea
 
 // the 64-wide kernel alone, without split tail tiles (the training and
 // backward modes, per-group k ranges)
-template <int BM, int MODE, bool BT = false>
+template <int BM, int MODE, int KM = 0>
 static hipError_t run_k64_only(GArgs g, hipStream_t st) {
+    constexpr bool BT = KM >= 1;
     using R = K64Cfg<BM, MODE>;
     g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
     g.total = g.m_tiles * g.n_tiles;
@@ -1344,8 +1413,11 @@ static hipError_t run_k64_only(GArgs g, hipStream_t st) {
     if (g.a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31) || g.K % 64 != 0 || g.Nout % 8 != 0 ||
         ((uintptr_t)g.C & 15) != 0)
         return hipErrorInvalidValue;
-    if (BT && g.kb1 != 0 && (g.kb1 < 0 || g.kb1 % 64 != 0 || g.kb1 >= g.K || !g.B1)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, BT>), dim3(persistent_blocks()), dim3(512), 0, st, g);
+    if (KM == 1 && g.kb1 != 0 && (g.kb1 < 0 || g.kb1 % 64 != 0 || g.kb1 >= g.K || !g.B1)) return hipErrorInvalidValue;
+    if (KM == 2 && (!g.krows || g.a_mod < 8 || g.a_mod % 8 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0 || g.lda < g.a_mod ||
+                    g.ldb < g.Nout || g.b_bytes >= (1ll << 31) || g.b_bytes < 0))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, KM>), dim3(persistent_blocks()), dim3(512), 0, st, g);
     return hipGetLastError();
 }
 
@@ -1363,16 +1435,19 @@ static hipError_t run_ring8_save(GArgs g, hipStream_t st) {
     return hipGetLastError();
 }
 
-static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st, bool b_kmajor = false) {
-    if (b_kmajor) {
+static hipError_t run_k64_mode(int BM, int mode, const GArgs& g, hipStream_t st, int kmajor = 0) {
+    if (kmajor == 2) {
+        if (mode != MODE_PLAIN || BM != 256) return hipErrorInvalidValue;
+        return run_k64_only<256, MODE_PLAIN, 2>(g, st);
+    }
+    if (kmajor == 1) {
         switch (mode) {
             case MODE_PLAIN:
-                return BM == 256 ? run_k64_only<256, MODE_PLAIN, true>(g, st) : run_k64_only<128, MODE_PLAIN, true>(g, st);
+                return BM == 256 ? run_k64_only<256, MODE_PLAIN, 1>(g, st) : run_k64_only<128, MODE_PLAIN, 1>(g, st);
             case MODE_DSWIGLU:
-                return BM == 256 ? run_k64_only<256, MODE_DSWIGLU, true>(g, st)
-                                 : run_k64_only<128, MODE_DSWIGLU, true>(g, st);
+                return BM == 256 ? run_k64_only<256, MODE_DSWIGLU, 1>(g, st) : run_k64_only<128, MODE_DSWIGLU, 1>(g, st);
             case MODE_DGELU:
-                return BM == 256 ? run_k64_only<256, MODE_DGELU, true>(g, st) : run_k64_only<128, MODE_DGELU, true>(g, st);
+                return BM == 256 ? run_k64_only<256, MODE_DGELU, 1>(g, st) : run_k64_only<128, MODE_DGELU, 1>(g, st);
         }
         return hipErrorInvalidValue;
     }
@@ -1487,7 +1562,7 @@ size_t grouped_gemm_ws_bytes(int G, int max_rows) {
 hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offsets, int G, int max_rows,
                                GemmTile* tiles, hipStream_t st, int bm) {
     if (max_rows <= 0 || G <= 0) return hipSuccess;
-    const int BM = bm == 128 || bm == 256 ? bm : pick_bm(MOE_BF16, G, max_rows);
+    const int BM = s.kmajor == 2 ? 256 : bm == 128 || bm == 256 ? bm : pick_bm(MOE_BF16, G, max_rows);
     const int mtiles = max_m_tiles(BM, G, max_rows);
     hipError_t err = build_tiles(offsets, G, BM, max_rows, mtiles, tiles, st);
     if (err != hipSuccess) return err;
@@ -1508,7 +1583,11 @@ hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offse
     g.a_mod = s.a_mod;
     g.b_shared = s.b_shared;
     g.kb1 = s.kb1;
-    return run_k64_mode(BM, mode, g, st, s.b_kmajor != 0);
+    g.krows = s.krows;
+    g.lda = s.lda;
+    g.ldb = s.ldb;
+    g.b_bytes = s.b_bytes;
+    return run_k64_mode(BM, mode, g, st, s.kmajor);
 }
 
 hipError_t launch_set2(int32_t* p, int32_t a, int32_t b, hipStream_t st) {
