@@ -407,7 +407,10 @@ struct Ring8Cfg {
     static constexpr int LOADS = A_LOADS + B_LOADS;
 };
 
-__device__ __forceinline__ int swz32(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// 64-byte rows (32-wide stages): a 16-lane fragment read covers 16 rows at one
+// logical chunk, i.e. 4 rows per 256-byte bank period; XOR-ing the chunk with
+// (row/4)%4 gives those 16 lanes 16 distinct 16-byte bank groups
+__device__ __forceinline__ int swz32(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) const uint8_t* lds_u8_ptr;
@@ -686,14 +689,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
             const int r = w4 * (BM / 4) + 16 * i + lr;
-            const int c = pc ^ ((r >> 1) & 3);
+            const int c = pc ^ ((r >> 2) & 3);
             const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
             t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * i;
         }
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
             const int r = w4 * 64 + 16 * i + lr;
-            const int c = pc ^ ((r >> 1) & 3);
+            const int c = pc ^ ((r >> 2) & 3);
             const int mat = r / C::BNM;
             const int col = min(t.n0 + r - mat * C::BNM, Nout - 1);
             t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * i;
