@@ -199,7 +199,7 @@ def train_bench(args, cfg, name, inp, desc, ws, y, stream):
         "n_kept": n_kept,
         "stages": {"forward_train_ms": t_fwd, "backward_ms": t_bwd,
                    "forward_tflops": fwd_flops / (t_fwd * 1e-3) / 1e12, "backward_tflops": bwd_tfs},
-        "roofline": {"kernel": "whole backward pass (dgrad + wgrad grouped GEMMs, transposes, router)",
+        "roofline": {"kernel": "whole backward pass (dgrad + wgrad grouped GEMMs on k-major operands, router, dx)",
                      "bound": "mfma", "achieved": bwd_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": bwd_tfs / MFMA_BF16_PEAK_TFS, "traffic": None, "flops_per_launch": bwd_flops,
                      "launch_ms": t_bwd},

@@ -333,7 +333,8 @@ moe_status moe_layer_forward_train(const moe_desc *desc, const moe_weights *w, c
 /* Gradients of L = sum(dy * y) + aux_weight * L_aux for the batch that the
  * training forward saved.  x [T][h] and the weights as in that call, dy
  * [T][h].  Needs moe_workspace_size(MOE_WS_BACKWARD) bytes (it holds the
- * transposed weights and the row gradients).  Deterministic. */
+ * row gradients, the routed copy of x's rows and the router's transposed
+ * operands; the expert weights are read in place).  Deterministic. */
 moe_status moe_layer_backward(const moe_desc *desc, const moe_weights *w, const void *x, const void *dy,
                               const moe_saved *saved, float aux_weight, moe_grads *grads, void *ws,
                               size_t ws_bytes, void *stream);
