@@ -8,7 +8,9 @@ in HBM.  W untimed steps, then exactly K steps bracketed by device
 synchronisation and timed with HIP events on the stream the library launches
 on; value = tokens per second.  The same step is then timed call by call, warm
 and cache-cold (a 512 MB buffer, twice the last-level cache, written before
-each call outside the event window), for the median, p10 and p90.  Per-stage times come from the stage entry
+each call outside the event window), for the median, p10 and p90, and once
+more replayed from a HIP graph that captured one step (no host launches; the
+replay must give the eager output bit for bit).  Per-stage times come from the stage entry
 points timed the same way.  The dominant kernel (the grouped gate/up GEMM with
 the fused activation) is timed on its own for the roofline figure.  The CPU
 oracle is timed on a bounded sample of the same workload for the CPU baseline.
@@ -93,6 +95,36 @@ def timed(fn, reps, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / reps  # ms
+
+
+def graph_per_step(step, reps, stream, T, out):
+    """The same step captured once into a HIP graph (torch.cuda.CUDAGraph on
+    the stream the library launches on) and replayed: per-replay spread, and
+    whether a replay's output equals the eager step's bit for bit."""
+    import torch
+    try:
+        step()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                                ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref))
+        res = dict(spread(per_step(g.replay, reps, stream), T), bitwise_equal_to_eager=same)
+        del g
+        return res
+    except Exception as e:  # reported, not fatal: the eager figures stand
+        return {"error": f"{type(e).__name__}: {e}"[:300]}
 
 
 def traffic_from_profile(kernel_tag, workload):
@@ -277,6 +309,7 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = dict(spread(per_step(step, args.steps, stream, flush), T), flush_bytes=512 << 20)
     del flush
+    graph = graph_per_step(step, args.steps, stream, T, y)
 
     # ---- routing facts of this batch (N, non-empty experts)
     n_kept = int(aux["n_kept"].item())
@@ -484,7 +517,7 @@ def main():
                    "parallelism": "single GPU", **({"variant": over} if over else {})},
         "tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "n_kept": n_kept, "n_dropped": A - n_kept, "nonempty_experts": nonempty, "l_aux": l_aux,
-        "warm_per_step": warm, "cold_per_step": cold,
+        "warm_per_step": warm, "cold_per_step": cold, "graph_per_step": graph,
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
