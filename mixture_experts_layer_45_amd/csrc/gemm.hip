@@ -1002,7 +1002,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         if constexpr (BT) {
             // load i of wave wu fills k rows 8wu+2i and 8wu+2i+1: lane l the
             // chunk at position l%32 of row l/32; chunks past Nout (whose
-            // columns are never stored) reread the last real one
+            // columns are never stored) reread the last real one.  With rows
+            // under 512 bytes the offset less 1024*i can go below zero: the
+            // unit adds offset and immediate in 32 bits, so the sum is exact
 #pragma unroll
             for (int i = 0; i < C::B_PW; ++i) {
                 const int kr = wu * 8 + 2 * i + (lane >> 5);
