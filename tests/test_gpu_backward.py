@@ -32,6 +32,10 @@ CASES = {
     "switch_gelu_zipf": ("switch_top1_e64_zipf", dict(T=1000, h=128, f=256)),
     "multihead_wo": ("multihead_h8_e32_top4", dict(T=300, h=512, f=128)),
     "hash_switch": ("switch_top1_e64_zipf", dict(T=1000, h=128, f=256, gate="hash")),
+    # edge cases: one token; every expert selected (K = E); most rows dropped
+    "single_token": ("top2_e8_h4096", dict(T=1, h=128, f=128)),
+    "all_experts_selected": ("top2_e8_h4096", dict(T=200, h=256, f=128, E=4, K=4)),
+    "heavy_drops": ("top2_e8_h4096", dict(T=600, h=256, f=192, capacity_factor=0.25)),
 }
 
 
@@ -83,8 +87,13 @@ def _check(case, aux_weight, zero_dy=False):
     mag = orc.layer_backward(cfg, host, host["x"], dyn, c_aux=aux_weight, magnitude=True)
     for k, t in gr.items():
         rk = ORACLE_KEY[k]
+        # one token: the router gradient is the single outer product dl (x) x, each
+        # row carrying the cancellation error of one dl_e (a softmax or sigmoid
+        # Jacobian applied to nearly equal terms) with no averaging over tokens;
+        # the elementwise magnitude bound covers it, the aggregate RMS check does not apply
+        rb = None if (case == "single_token" and k == "w_router") else 1e-2
         st = G.assert_close(G.host(t).reshape(ref[rk].shape), ref[rk], "bf16", f"{k} {case}", mag=mag[rk],
-                            mag_unit=BWD_MAG / G.MAG_FACTOR, rms_bound=1e-2)
+                            mag_unit=BWD_MAG / G.MAG_FACTOR, rms_bound=rb)
         G.log(f"   {k}: {st}")
     return cfg, inp, dy, gr
 
