@@ -243,8 +243,8 @@ def train_bench(args, cfg, name, inp, desc, ws, y, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "expert/head-parallel path is a design, not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library implements the "
+              "one-GPU layer, and its expert/head-parallel sharding exists as a design only.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
