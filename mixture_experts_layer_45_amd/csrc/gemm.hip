@@ -493,6 +493,21 @@ __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int r
 #pragma clang loop unroll(full)
         for (int tm = 0; tm < C::TM; ++tm) {
             const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+            // the row block's saved derivatives are loaded first, all in flight
+            // together (loads placed after a store to C would wait for it: the
+            // compiler cannot tell that C and aux do not overlap)
+            u32x4 sv[C::TN][2][NA];
+#pragma clang loop unroll(full)
+            for (int tn = 0; tn < C::TN; ++tn)
+#pragma clang loop unroll(full)
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
+                    const bool ok = row < row_end && col < Nout;
+                    const size_t at = ((size_t)row * ld + col) * 2;
+#pragma unroll
+                    for (int m = 0; m < NA; ++m)
+                        sv[tn][pp][m] = ok ? *(const u32x4*)(aux + at + (size_t)m * Nout * 2) : u32x4{0u, 0u, 0u, 0u};
+                }
 #pragma clang loop unroll(full)
             for (int tn = 0; tn < C::TN; ++tn) {
 #pragma clang loop unroll(full)
@@ -505,7 +520,7 @@ __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int r
 #pragma unroll
                         for (int m = 0; m < NA; ++m) {
                             float dv[8];
-                            bf16x8_to_f32(*(const u32x4*)(aux + at + (size_t)m * Nout * 2), dv);
+                            bf16x8_to_f32(sv[tn][pp][m], dv);
 #pragma unroll
                             for (int j = 0; j < 8; ++j) dv[j] *= g[j];
                             *(u32x4*)(Cp + at + (size_t)m * Nout * 2) = f32_to_bf16x8(dv);
