@@ -36,6 +36,9 @@ CASES = {
     "single_token": ("top2_e8_h4096", dict(T=1, h=128, f=128)),
     "all_experts_selected": ("top2_e8_h4096", dict(T=200, h=256, f=128, E=4, K=4)),
     "heavy_drops": ("top2_e8_h4096", dict(T=600, h=256, f=192, capacity_factor=0.25)),
+    # two experts, every token in both: 1100 rows per expert, so the weight
+    # gradients run 18 k stages per group (the other cases 1 to 5)
+    "two_experts_long_k": ("top2_e8_h4096", dict(T=1100, h=256, f=128, E=2, K=2)),
 }
 
 
