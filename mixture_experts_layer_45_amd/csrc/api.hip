@@ -645,7 +645,7 @@ moe_status moe_layer_backward(const moe_desc* d, const moe_weights* w, const voi
     if ((long long)p.max_rows * p.f * 2 >= lim || (long long)p.max_rows * nf * 2 >= lim ||
         (long long)p.max_rows * p.d * 2 >= lim || (long long)p.f * p.d * 2 >= lim || (long long)p.d * nf * 2 >= lim ||
         (long long)b.Ep * b.Np_h * 2 >= lim || (long long)p.d * b.Np_h * 2 >= lim || (long long)p.T * nf * 2 >= lim ||
-        (long long)p.T * p.f * 2 >= lim || (long long)p.T * p.h * 2 >= lim)
+        (long long)p.T * p.f * 2 >= lim || (long long)p.T * p.h * 2 >= lim || (b.wo && (long long)p.h * p.h * 2 >= lim))
         return fail(MOE_ERR_UNSUPPORTED, "an operand of the backward GEMMs exceeds 2 GB");
     const size_t need = ws_bytes_of(d, MOE_WS_BACKWARD);
     if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
