@@ -14,7 +14,9 @@ replay must give the eager output bit for bit).  Per-stage times come from the s
 points timed the same way.  The dominant kernel (the grouped gate/up GEMM with
 the fused activation) is timed on its own for the roofline figure.  The CPU
 oracle is timed on a bounded sample of the same workload for the CPU baseline.
-Prints one JSON line.
+Prints one JSON line.  `--train` times a training step instead, `--shard` the
+grouped FFN on one GPU's share of the 8-GPU expert/head-parallel layers, and
+`--counters` runs each stage a few times for rocprofv3 counter passes.
 """
 import argparse
 import hashlib
@@ -49,6 +51,9 @@ def parse():
     p.add_argument("--train", action="store_true",
                    help="time a training step instead: the training forward (it keeps what the backward "
                         "reads) and moe_layer_backward of sum(dy * y) + L_aux")
+    p.add_argument("--shard", action="store_true",
+                   help="time the grouped FFN on one GPU's share of the expert/head-parallel layers at their "
+                        "real shapes (8 GPUs): prints one line")
     p.add_argument("--counters", action="store_true",
                    help="for rocprofv3 --pmc runs: a 1 GiB device copy (counter calibration), then each "
                         "stage (route, gather permute, GEMM1, GEMM2, combine) three times; prints one line")
@@ -240,6 +245,62 @@ def train_bench(args, cfg, name, inp, desc, ws, y, stream):
     print(json.dumps(out), flush=True)
 
 
+# One GPU's share of the sharded layers (8 GPUs, each with the workload's T
+# tokens): expert parallelism puts E/8 experts on a GPU, which receives every
+# GPU's rows routed to them; head parallelism puts one head's 32 experts on a
+# GPU, with the d-slices of all 8*T tokens.  (base workload, local groups,
+# rows per group)
+SHARDS = {
+    "ep8_top2_e8_h4096": ("top2_e8_h4096", 1, 16384),        # 8*8192 tokens x K=2 / 8 experts
+    "ep8_sigmoid_top8_e256": ("sigmoid_top8_e256_shared", 32, 1024),  # 8*4096 x 8 / 256
+    "hp8_multihead_h8_e32": ("multihead_h8_e32_top4", 32, 8192),  # 8*8192 x 4 / 32 per head
+}
+
+
+def shard_bench(args):
+    """Grouped FFN (GEMM1 + activation + GEMM2, moe_grouped_ffn) on each
+    shard's real shape: uniform rows per local expert, synthetic inputs."""
+    import torch
+
+    import mixture_experts_layer_45_amd as moe
+    from mixture_experts_layer_45_amd import inputs
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    res = []
+    for sname, (base, G, rows) in SHARDS.items():
+        b = inputs.CONFIGS[base]
+        d = b["h"] // b.get("H", 1)
+        N = G * rows
+        cfg = dict(b, T=N, h=d, H=1, E=G, K=1, n_shared=0, has_wo=0, logit_bias=None, select_bias=None, **DENSE)
+        log(f"[bench] shard {sname}: {G} groups x {rows} rows, d={d}, f={cfg['f']}")
+        inp = inputs.make_inputs(cfg, "cuda", seed=0)
+        desc = moe.desc_from_cfg(cfg)
+        offsets = torch.arange(0, N + 1, rows, dtype=torch.int32, device="cuda")
+        dt = inputs.torch_dtype(cfg)
+        h_tmp = torch.empty((N, cfg["f"]), dtype=dt, device="cuda")
+        y_perm = torch.empty((N, d), dtype=dt, device="cuda")
+        ws = moe.workspace(desc, moe.MOE_WS_FFN)
+
+        def ffn():
+            moe.moe_grouped_ffn(desc, inp["x"], offsets, N, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
+                                y_perm, 0, ws)
+
+        for _ in range(args.warmup):
+            ffn()
+        ms = timed(ffn, args.stage_reps, stream)
+        n_act = 2 if cfg["act"] == "swiglu" else 1
+        flops = 2.0 * N * d * cfg["f"] * (n_act + 1)
+        tfs = flops / (ms * 1e-3) / 1e12
+        res.append({"shard": sname, "groups": G, "rows_per_group": rows, "d": d, "f": cfg["f"], "ffn_ms": ms,
+                    "tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS})
+        del inp, h_tmp, y_perm, ws
+        torch.cuda.empty_cache()
+    out = {"metric": "grouped FFN on one GPU's share of the 8-GPU expert/head-parallel layers", "unit": "TFLOP/s",
+           "n_gpus": 1, "dtype": "bf16", "data": "synthetic", "shards": res}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -252,6 +313,8 @@ def main():
     import mixture_experts_layer_45_amd as moe
     from mixture_experts_layer_45_amd import inputs
 
+    if args.shard:
+        return shard_bench(args)
     name = args.workload or inputs.BENCH_WORKLOAD
     over = {}
     for kv in args.set:
