@@ -21,6 +21,9 @@
 //   * gemm_bf16_kernel -- any K (zero-filled tail), 4 waves, one tile per block.
 // Measured on one MI355X: the 64-wide kernel is 10-25 % faster on 128-row tiles
 // (256 experts x ~128 rows, d = 7168) and on short K (d = 512, f = 1024).
+// The backward pass runs the 64-wide kernel on k-major operands, read where
+// they lie through the LDS transposing load: the forward weights for the input
+// gradients (KM = 1) and the activations for the weight gradients (KM = 2).
 #include <algorithm>
 
 #include "common.hpp"
