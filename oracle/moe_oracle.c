@@ -53,6 +53,11 @@
  * contiguous d = h/H slice of each token with its own router and its own E
  * experts, concatenates the head outputs and applies W_o.
  *
+ * Parity unpinned: P_i of the sigmoid router (the mean of sigma_i / sum sigma)
+ * and L_aux of the multi-head layer (the mean over heads of alpha E sum f P,
+ * f and P per head).  No page fixes either; the tests check them only through
+ * invariants (P sums to 1 per head, L_aux recomputed from the returned f and P).
+ *
  * Layouts (the same bytes the HIP library receives):
  *   x            [T][h]                  row-major, fp32 or bf16
  *   w_router     [H][E][d]               one row of d inputs per expert (out-major)

@@ -9,6 +9,9 @@ report of the worked example in lesson 10 of the expert-parallelism course
 code exercise (expert-to-rank map, per-rank load, max/mean imbalance, routed
 volume).
 
+Parity unpinned (no page fixes them; checked through invariants only): P of
+the sigmoid router and L_aux of the multi-head layer (see moe_oracle.c).
+
 Arrays in bf16 are passed as numpy uint16 holding the raw bf16 bits.
 A layer configuration is a plain dict with keys
   T, h, H, E, K, f, n_shared, has_wo, dtype ('f32'|'bf16'),
