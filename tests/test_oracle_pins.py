@@ -332,6 +332,25 @@ def test_aux_loss_closed_forms():
     assert r["l_aux"] == pytest.approx(float(np.float32(0.01)) * 4, rel=1e-12)
 
 
+def test_unpinned_aux_statistics_invariants():
+    """P of the sigmoid router and L_aux of the multi-head layer have no value
+    fixed by the pages (parity unpinned); what holds at any size: per head, P is
+    a distribution over its E experts and f sums to 1, and L_aux is the mean over
+    heads of alpha E sum f P recomputed from the returned f and P."""
+    for cfg in (small("sigmoid_top8_e256_shared", T=40, h=64, f=48, E=16, K=4),
+                small("multihead_h8_e32_top4", T=24, h=128, f=32, H=4, E=8, K=2)):
+        inp = inputs_np(inputs.make_inputs(cfg))
+        r = _layer(cfg, inp)
+        H, E = cfg.get("H", 1), cfg["E"]
+        f = np.asarray(r["f"], np.float64).reshape(H, E)
+        P = np.asarray(r["P"], np.float64).reshape(H, E)
+        assert np.all(P >= 0) and np.allclose(P.sum(1), 1.0, rtol=1e-9)
+        assert np.allclose(f.sum(1), 1.0, rtol=1e-12)
+        alpha = float(np.float32(cfg["alpha"]))
+        want = float(np.mean([alpha * E * (f[g] * P[g]).sum() for g in range(H)]))
+        assert r["l_aux"] == pytest.approx(want, rel=1e-9)
+
+
 def test_shared_expert_adds_dense_ffn():
     cfg = small("sigmoid_top8_e256_shared", T=24, h=64, f=48, E=16, K=4)
     inp = inputs_np(inputs.make_inputs(cfg))
