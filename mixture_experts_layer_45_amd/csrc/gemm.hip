@@ -94,7 +94,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
             t.group = g;
             t.row0 = r0 + i * BM;
             t.row_end = r1;
-            t.pad = 0;
+            t.pad = i;  // index within the group (the schedule finds the group's first tile from it)
             tiles[pos + i] = t;
         }
         pos += nt[q];
@@ -165,15 +165,36 @@ __device__ __forceinline__ void tail_split(int Tx, int B, int nk, bool enabled, 
         if (S < 2) S = 1;
     }
 }
-// schedule index -> (row tile, column tile): groups of NGROUP column tiles,
-// each sweeping every real row tile
-__device__ __forceinline__ void sched_decode(int si, int n_m, int n_tiles, int& mt, int& nt) {
+// schedule index -> (row tile, column tile) and the row tile's table entry:
+// groups of NGROUP column tiles, each sweeping every real row tile.  Within a
+// column group the items of one group's (expert's) ne row tiles are
+// consecutive.  Groups of at most kPairedRows rows run column tile by column
+// tile, so the row tiles that read one weight tile run back to back (measured:
+// the 256-expert layer's gate/up GEMM, 128-row tiles, 3.30 -> 3.23 ms and 9 %
+// fewer L2 misses); larger groups run row tile by row tile (four 256-row tiles
+// of the multi-head layer's ~1000-row groups in the other order: 0.73 -> 0.74 ms).
+// tiles[m].pad is the row tile's index within its group, so the group's first
+// tile and tile count follow from any one of its tiles.
+constexpr int kPairedRows = 512;
+__device__ __forceinline__ GemmTile sched_decode(int si, int n_m, int n_tiles, const GemmTile* tiles, int BM, int& mt,
+                                                 int& nt) {
     const int gsz = n_m * NGROUP;
     const int nb = si / gsz;
     const int rem = si - nb * gsz;
     const int width = min(NGROUP, n_tiles - nb * NGROUP);
-    mt = rem / width;
-    nt = nb * NGROUP + (rem - mt * width);
+    const int m0 = rem / width;
+    const GemmTile t0 = tiles[m0];
+    const int f = m0 - t0.pad;  // the group's first row tile
+    const int ne = min((t0.row_end - (t0.row0 - t0.pad * BM) + BM - 1) / BM, n_m - f);
+    if (ne > 1 && ne * BM <= kPairedRows) {
+        const int local = rem - width * f;
+        mt = f + local % ne;
+        nt = nb * NGROUP + local / ne;
+        return mt == m0 ? t0 : tiles[mt];
+    }
+    mt = m0;
+    nt = nb * NGROUP + (rem - m0 * width);
+    return t0;
 }
 
 
@@ -676,16 +697,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Ab, (short)0, (int)a.a_bytes, kBufWord3);
     const int a_nrows = (int)(a.a_bytes / rowbytes);
 
-    // schedule index -> (row tile, column tile): groups of NGROUP column tiles,
-    // each sweeping every real row tile
-    auto decode = [&](int si, int& mt, int& nt) __attribute__((always_inline)) {
-        const int gsz = n_m * NGROUP;
-        const int nb = si / gsz;
-        const int rem = si - nb * gsz;
-        const int width = min(NGROUP, a.n_tiles - nb * NGROUP);
-        mt = rem / width;
-        nt = nb * NGROUP + (rem - mt * width);
-    };
     struct Tile {
         int row0, row_end, n0;
         __amdgpu_buffer_rsrc_t rB;
@@ -695,8 +706,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     // immediate offset 1024*i, so the offset here is reduced by that amount
     auto setup = [&](int si, Tile& t) __attribute__((always_inline)) {
         int mt, nt;
-        decode(si, mt, nt);
-        const GemmTile tl = a.tiles[mt];
+        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, BM, mt, nt);
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
@@ -964,8 +974,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             t.slot = xcd * kTailSlots + j;
         }
         int mt, nt;
-        sched_decode(si, n_m, a.n_tiles, mt, nt);
-        const GemmTile tl = a.tiles[mt];
+        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, BM, mt, nt);
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
@@ -1242,8 +1251,7 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
     tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
     if (S < 2 || jt >= r_tail) return;
     int mt, nt;
-    sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, mt, nt);
-    const GemmTile tl = a.tiles[mt];
+    const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, BM, mt, nt);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     floatx16 acc[C::NACC];
 #pragma unroll
