@@ -200,6 +200,22 @@ def test_grouped_ffn_split_tail(case):
     _check_grouped_ffn(cfg, np.array(counts, dtype=np.int32), case)
 
 
+# 128-row tiles whose groups span 1, 2, 3 and 5 row tiles: groups of at most
+# 512 rows are scheduled column tile by column tile, larger ones row tile by
+# row tile, within the same column groups (8 and 2 column tiles)
+SCHEDULE_CASES = {
+    "paired_row_tiles_swiglu": ("top2_e8_h4096", dict(E=6, K=1, h=512, f=1024), [130, 256, 300, 513, 0, 90]),
+    "paired_row_tiles_gelu": ("switch_top1_e64_zipf", dict(E=5, K=1, h=512, f=1024), [512, 129, 0, 640, 384]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SCHEDULE_CASES))
+def test_grouped_ffn_schedule_orders(case):
+    name, over, counts = SCHEDULE_CASES[case]
+    cfg = inputs.variant(name, T=sum(counts), capacity_factor=0.0, **over)
+    _check_grouped_ffn(cfg, np.array(counts, dtype=np.int32), case)
+
+
 def _check_grouped_ffn(cfg, counts, label):
     H, E = cfg.get("H", 1), cfg["E"]
     Gn, dd, f = H * E, cfg["h"] // H, cfg["f"]
