@@ -445,15 +445,28 @@ void orc_permute(const orc_desc *d, const int32_t *topk_idx, int64_t capacity,
  *           silu(z) = z / (1 + e^{-z})
  *   GELU:   a = x W1^T, hdn = a * (1 + erf(a / sqrt 2)) / 2, out = hdn W2^T
  * W1, W3: [f][din]; W2: [din][f]; all in double.
- * out_abs (may be NULL) receives sum_j |hdn_j| |W2[o][j]|, the magnitude of the
- * terms of the last contraction: an evaluation that rounds hdn and out to a
- * format with unit roundoff u errs by at most about 2u times it (the scale of
- * the stated parity bound; it plays no part in out).                         */
+ * Two optional by-products size the parity bound of an evaluation in bf16
+ * (they play no part in out):
+ *   out_abs[o] = sum_j |hdn_j| |W2[o][j]|, the magnitude of the terms of the
+ *                last contraction (any rounding of hdn and out to a format
+ *                with unit roundoff u errs by at most about 2u times it);
+ *   out_var[o] = sum_j W2[o][j]^2 ulp(hdn_j)^2 / 12, the variance that
+ *                rounding every hdn_j to bf16 (to nearest: an error uniform
+ *                on half an ulp either side) adds to out[o]; 0 for fp32.   */
+static double ulp_bf16(double v)
+{
+    int ex;
+    if (v == 0.0) return 0.0;
+    frexp(v, &ex); /* |v| = m 2^ex, 1/2 <= m < 1: 8 significant bits give ulp 2^(ex-8) */
+    return ldexp(1.0, ex - 8 < -133 ? -133 : ex - 8);
+}
+
 void orc_expert_ffn(int32_t dtype, int32_t act, int32_t din, int32_t f,
                     const void *w1, const void *w3, const void *w2,
-                    const double *xin, double *out, double *out_abs)
+                    const double *xin, double *out, double *out_abs, double *out_var)
 {
     double *hdn = (double *)malloc(sizeof(double) * (size_t)f);
+    double *hu2 = (double *)malloc(sizeof(double) * (size_t)f);
     for (int32_t j = 0; j < f; ++j) {
         double a = 0.0;
         for (int32_t i = 0; i < din; ++i) a += xin[i] * ld(w1, dtype, (int64_t)j * din + i);
@@ -464,18 +477,35 @@ void orc_expert_ffn(int32_t dtype, int32_t act, int32_t din, int32_t f,
         } else {
             hdn[j] = 0.5 * a * (1.0 + erf(a / sqrt(2.0)));
         }
+        hu2[j] = dtype == 1 ? ulp_bf16(hdn[j]) * ulp_bf16(hdn[j]) / 12.0 : 0.0;
     }
     for (int32_t o = 0; o < din; ++o) {
-        double acc = 0.0, mag = 0.0;
+        double acc = 0.0, mag = 0.0, var = 0.0;
         for (int32_t j = 0; j < f; ++j) {
             double w = ld(w2, dtype, (int64_t)o * f + j);
             acc += hdn[j] * w;
             mag += fabs(hdn[j]) * fabs(w);
+            var += w * w * hu2[j];
         }
         out[o] = acc;
         if (out_abs) out_abs[o] = mag;
+        if (out_var) out_var[o] = var;
     }
     free(hdn);
+    free(hu2);
+}
+
+/* n rows of xin [n][din] through the same expert: orc_expert_ffn row by row
+ * (rows in parallel; each row's arithmetic is the same as above).          */
+void orc_expert_ffn_rows(int32_t dtype, int32_t act, int32_t din, int32_t f,
+                         const void *w1, const void *w3, const void *w2, int64_t n,
+                         const double *xin, double *out, double *out_abs, double *out_var)
+{
+    int64_t r;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (r = 0; r < n; ++r)
+        orc_expert_ffn(dtype, act, din, f, w1, w3, w2, xin + r * din, out + r * din,
+                       out_abs ? out_abs + r * din : NULL, out_var ? out_var + r * din : NULL);
 }
 
 /* ------------------------------------------------------------- combine
@@ -514,11 +544,22 @@ void orc_combine(const orc_desc *d, const int32_t *dest_row, const double *topk_
  * ymag (may be NULL) gets the magnitude that scales the rounding error of an
  * evaluation in a narrower format: sum over kept k of w_k * sum_j |hdn_j||W2_j|
  * (plus the shared expert's), and through W_o sum_i (|cat_i| + mag_i)|W_o[r][i]|.
+ * yvar (may be NULL; bf16 layers only, else 0) gets the variance that the
+ * intermediate roundings of a bf16 evaluation add to y when each rounds to
+ * nearest (an error uniform on half an ulp either side, variance ulp^2/12,
+ * the roundings independent): every hdn_j (orc_expert_ffn's out_var), every
+ * expert output row and the shared expert's output (stored in bf16 before the
+ * weighted sum), and, before W_o, the concatenated head outputs:
+ *   var(cat_j) = sum_k w_k^2 (out_var_k[j] + ulp(out_k[j])^2 / 12)
+ *                + shared (out_var[j] + ulp(out[j])^2 / 12)
+ *   var(y_r)   = sum_i W_o[r][i]^2 (var(cat_i) + ulp(cat_i)^2 / 12)  with W_o,
+ *                var(cat_r) without.
+ * The last rounding of y itself is not included.
  * Aux statistics ([L10] item 4): f = counts / (T K), P = psum / T,
  * L_aux = alpha * E * sum_e f_e P_e, averaged over heads.                     */
 int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
                       const int32_t *tokens, int32_t n_tokens, double *y, double *ymag,
-                      orc_aux *aux)
+                      double *yvar, orc_aux *aux)
 {
     const int32_t T = d->T, h = d->h, H = d->H, E = d->E, K = d->K, f = d->f;
     const int32_t dd = h / H, Et = H * E;
@@ -562,6 +603,9 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
         double *o = (double *)malloc(sizeof(double) * (size_t)h);
         double *om = (double *)malloc(sizeof(double) * (size_t)h);
         double *cm = (double *)calloc((size_t)h, sizeof(double));
+        double *ov = (double *)malloc(sizeof(double) * (size_t)h);
+        double *cv = (double *)calloc((size_t)h, sizeof(double));
+        const int bf = d->dtype == 1;
         for (int32_t j = 0; j < h; ++j) xin[j] = ld(x, d->dtype, t * h + j);
         for (int32_t g = 0; g < H; ++g) {
             int64_t s = t * H + g;
@@ -572,37 +616,45 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
                 const char *w1 = (const char *)w->w_gate + (size_t)e * f * dd * wsz;
                 const char *w3 = d->act == 0 ? (const char *)w->w_up + (size_t)e * f * dd * wsz : NULL;
                 const char *w2 = (const char *)w->w_down + (size_t)e * dd * f * wsz;
-                orc_expert_ffn(d->dtype, d->act, dd, f, w1, w3, w2, xin + g * dd, o, om);
+                orc_expert_ffn(d->dtype, d->act, dd, f, w1, w3, w2, xin + g * dd, o, om, ov);
+                const double wk = wts[s * K + k];
                 for (int32_t j = 0; j < dd; ++j) {
-                    cat[g * dd + j] += wts[s * K + k] * o[j];
-                    cm[g * dd + j] += wts[s * K + k] * om[j];
+                    cat[g * dd + j] += wk * o[j];
+                    cm[g * dd + j] += wk * om[j];
+                    if (bf) cv[g * dd + j] += wk * wk * (ov[j] + ulp_bf16(o[j]) * ulp_bf16(o[j]) / 12.0);
                 }
             }
         }
         if (d->n_shared > 0) {
-            orc_expert_ffn(d->dtype, d->act, h, f, w->sh_gate, w->sh_up, w->sh_down, xin, o, om);
+            orc_expert_ffn(d->dtype, d->act, h, f, w->sh_gate, w->sh_up, w->sh_down, xin, o, om, ov);
             for (int32_t j = 0; j < h; ++j) {
                 cat[j] += o[j];
                 cm[j] += om[j];
+                if (bf) cv[j] += ov[j] + ulp_bf16(o[j]) * ulp_bf16(o[j]) / 12.0;
             }
         }
         if (d->has_wo) {
             for (int32_t r = 0; r < h; ++r) {
-                double acc = 0.0, mag = 0.0;
+                double acc = 0.0, mag = 0.0, var = 0.0;
                 for (int32_t j = 0; j < h; ++j) {
                     double wo = ld(w->w_o, d->dtype, (int64_t)r * h + j);
                     acc += cat[j] * wo;
                     mag += (fabs(cat[j]) + cm[j]) * fabs(wo);
+                    if (bf) var += wo * wo * (cv[j] + ulp_bf16(cat[j]) * ulp_bf16(cat[j]) / 12.0);
                 }
                 y[(int64_t)i * h + r] = acc;
                 if (ymag) ymag[(int64_t)i * h + r] = mag;
+                if (yvar) yvar[(int64_t)i * h + r] = var;
             }
         } else {
             for (int32_t j = 0; j < h; ++j) {
                 y[(int64_t)i * h + j] = cat[j];
                 if (ymag) ymag[(int64_t)i * h + j] = cm[j];
+                if (yvar) yvar[(int64_t)i * h + j] = cv[j];
             }
         }
+        free(ov);
+        free(cv);
         free(xin);
         free(cat);
         free(o);

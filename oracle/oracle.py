@@ -95,12 +95,14 @@ def lib():
         _lib.orc_permute.restype = None
         _lib.orc_permute.argtypes = [C.POINTER(OrcDesc), C.c_void_p, C.c_int64] + [C.c_void_p] * 6
         _lib.orc_expert_ffn.restype = None
-        _lib.orc_expert_ffn.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 6
+        _lib.orc_expert_ffn.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 7
+        _lib.orc_expert_ffn_rows.restype = None
+        _lib.orc_expert_ffn_rows.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 3 + [C.c_int64] + [C.c_void_p] * 4
         _lib.orc_combine.restype = None
         _lib.orc_combine.argtypes = [C.POINTER(OrcDesc)] + [C.c_void_p] * 5
         _lib.orc_layer_forward.restype = C.c_int
         _lib.orc_layer_forward.argtypes = [C.POINTER(OrcDesc), C.POINTER(OrcWeights), C.c_void_p,
-                                           C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                            C.POINTER(OrcAux)]
         _lib.orc_layer_backward.restype = C.c_int
         _lib.orc_layer_backward.argtypes = [C.POINTER(OrcDesc), C.POINTER(OrcWeights), C.c_void_p, C.c_void_p,
@@ -231,8 +233,10 @@ def permute(cfg, topk_idx, cap, T=None):
 
 
 def expert_ffn(cfg, din, w1, w3, w2, xin, with_mag=False):
-    """Rows xin [n, din] (float64) through one expert; returns [n, din] float64
-    (and, with with_mag, the magnitude sum_j |hdn_j||W2[o][j]| per output)."""
+    """Rows xin [n, din] (float64) through one expert; returns [n, din] float64.
+    With with_mag also the magnitude sum_j |hdn_j||W2[o][j]| per output and the
+    standard deviation that rounding hdn to bf16 adds to each output
+    (sqrt(sum_j W2[o][j]^2 ulp(hdn_j)^2 / 12); 0 for fp32): (out, mag, sig)."""
     el = _elem(cfg)
     act = 1 if cfg.get("act", "swiglu") == "gelu" else 0
     dt = 1 if cfg["dtype"] == "bf16" else 0
@@ -243,10 +247,10 @@ def expert_ffn(cfg, din, w1, w3, w2, xin, with_mag=False):
     f = w1.size // din
     out = np.empty_like(xin)
     mag = np.empty_like(xin)
-    L = lib()
-    for r in range(xin.shape[0]):
-        L.orc_expert_ffn(dt, act, din, f, _p(w1), _p(w3), _p(w2), _p(xin[r]), _p(out[r]), _p(mag[r]))
-    return (out, mag) if with_mag else out
+    var = np.empty_like(xin)
+    lib().orc_expert_ffn_rows(dt, act, din, f, _p(w1), _p(w3), _p(w2), xin.shape[0], _p(xin), _p(out), _p(mag),
+                              _p(var))
+    return (out, mag, np.sqrt(var)) if with_mag else out
 
 
 def combine(cfg, dest_row, topk_w, y_perm, y_shared=None, T=None):
@@ -264,7 +268,10 @@ def combine(cfg, dest_row, topk_w, y_perm, y_shared=None, T=None):
 
 def layer_forward(cfg, weights, x, tokens=None, T=None):
     """Whole layer.  weights: dict with numpy arrays (keys as in OrcWeights).
-    Returns dict with y [n_tokens, h] float64 and the routing/aux arrays."""
+    Returns dict with y [n_tokens, h] float64 and the routing/aux arrays, plus
+    the two scales of the bf16 parity bound (moe_oracle.c): ymag, the
+    magnitude of the terms, and ysig, the standard deviation that the
+    intermediate bf16 roundings add (0 for fp32 layers)."""
     d = desc(cfg, T)
     el = _elem(cfg)
     S = d.T * d.H
@@ -292,6 +299,7 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
     nt = d.T if tok is None else tok.size
     y = np.zeros((nt, d.h), dtype=np.float64)
     ymag = np.zeros((nt, d.h), dtype=np.float64)
+    yvar = np.zeros((nt, d.h), dtype=np.float64)
     out = dict(
         topk_idx=np.empty((S, d.K), np.int32), topk_w=np.empty((S, d.K), np.float64),
         margin=np.empty(S, np.float64), counts=np.empty(Et, np.int32), kept=np.empty(Et, np.int32),
@@ -301,7 +309,8 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
         logits=np.empty((S, d.E), np.float32),
     )
     aux = OrcAux(**{k: _p(v) for k, v in out.items()})
-    rc = lib().orc_layer_forward(C.byref(d), C.byref(W), _p(x), _p(tok), nt, _p(y), _p(ymag), C.byref(aux))
+    rc = lib().orc_layer_forward(C.byref(d), C.byref(W), _p(x), _p(tok), nt, _p(y), _p(ymag), _p(yvar),
+                                 C.byref(aux))
     if rc != 0:
         raise ValueError("oracle rejected the layer description")
     out["n_kept"] = int(out["n_kept"][0])
@@ -309,6 +318,7 @@ def layer_forward(cfg, weights, x, tokens=None, T=None):
     out["l_aux"] = float(out["l_aux"][0])
     out["y"] = y
     out["ymag"] = ymag
+    out["ysig"] = np.sqrt(yvar)
     return out
 
 
@@ -389,13 +399,20 @@ def load_per_rank(tokens_per_expert, experts_per_rank):
 
 
 def imbalance(loads):
-    if not loads or sum(loads) == 0:
-        raise ValueError("loads must be non-empty with a positive total")
-    return max(loads) / (sum(loads) / len(loads))
+    """Busiest rank's load over the average rank load (1.0 = perfectly even)."""
+    n = len(loads)
+    total = sum(loads)
+    if n == 0 or total <= 0:
+        raise ValueError(f"imbalance is undefined for {n} ranks carrying {total} tokens")
+    return n * max(loads) / total
 
 
 def routing_volume(tokens_per_expert):
-    return sum(tokens_per_expert)
+    """Assignments that leave their token's rank, at most: one per (token, choice)."""
+    vol = 0
+    for n in tokens_per_expert:
+        vol += int(n)
+    return vol
 
 
 def utilisation(loads):
