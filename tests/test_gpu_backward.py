@@ -23,7 +23,12 @@ from tests._np_ref import to_np
 
 pytestmark = pytest.mark.gpu
 
-BWD_MAG = 3.0 * 2.0 ** -8
+# The gradient path rounds up to six intermediate rows to bf16, each moving a
+# value by at most 2^-8 of itself; the magnitude bound (tests/_bound.py, the
+# oracle's magnitude mode as M) allows three such roundings' worth, since
+# independent roundings do not all err the same way at once (measured RMS
+# error 2e-3 to 4e-3 of the RMS on every gradient).
+BWD_ROUNDINGS = 3
 CASES = {
     "top2_swiglu": ("top2_e8_h4096", dict(T=600, h=512, f=320)),
     "top2_drops_choice": ("top2_e8_h4096", dict(T=600, h=512, f=320, capacity_factor=0.8, queue="choice")),
@@ -84,7 +89,8 @@ def _check(case, aux_weight, zero_dy=False):
     assert np.array_equal(sv["topk_idx"].cpu().numpy(), fwd["topk_idx"])
     assert np.array_equal(sv["dest_row"].cpu().numpy(), fwd["dest_row"])
     # the training forward's output within the forward bound
-    G.assert_close(G.host(y), fwd["y"], cfg["dtype"], f"y {case}", mag=fwd["ymag"])
+    G.assert_close(G.host(y), fwd["y"], cfg["dtype"], f"y {case}", mag=fwd["ymag"], sig=fwd["ysig"],
+                   n_acc=G.n_acc(cfg))
     dyn = dy.float().numpy().astype(np.float64)
     ref = orc.layer_backward(cfg, host, host["x"], dyn, c_aux=aux_weight)
     mag = orc.layer_backward(cfg, host, host["x"], dyn, c_aux=aux_weight, magnitude=True)
@@ -96,7 +102,7 @@ def _check(case, aux_weight, zero_dy=False):
         # the elementwise magnitude bound covers it, the aggregate RMS check does not apply
         rb = None if (case == "single_token" and k == "w_router") else 1e-2
         st = G.assert_close(G.host(t).reshape(ref[rk].shape), ref[rk], "bf16", f"{k} {case}", mag=mag[rk],
-                            mag_unit=BWD_MAG / G.MAG_FACTOR, rms_bound=rb)
+                            n_round=BWD_ROUNDINGS, rms_bound=rb)
         G.log(f"   {k}: {st}")
     return cfg, inp, dy, gr
 
@@ -147,7 +153,7 @@ def test_training_forward_matches_forward():
     host = G.np_inputs(inp)
     ref = orc.layer_forward(cfg, host, host["x"])
     for yy in (y0, y1):
-        G.assert_close(G.host(yy), ref["y"], cfg["dtype"], "y", mag=ref["ymag"])
+        G.assert_close(G.host(yy), ref["y"], cfg["dtype"], "y", mag=ref["ymag"], sig=ref["ysig"], n_acc=G.n_acc(cfg))
 
 
 def test_training_forward_long_k_saves_activation_derivatives():
@@ -165,6 +171,13 @@ def test_training_forward_long_k_saves_activation_derivatives():
     moe.moe_layer_forward_train(d, inp, inp["x"], y1, sv, ws=moe.workspace(d))
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    # every token of the layer against the oracle (the gated ring kernel on
+    # 256-row tiles runs both schedule orders here)
+    host = G.np_inputs(inp)
+    ref = orc.layer_forward(cfg, host, host["x"])
+    from tests.test_gpu_parity import _compare_layer
+    st, n_ex = _compare_layer(cfg, y0, aux, ref)
+    G.log(f"   excluded={n_ex} {st}")
     f = cfg["f"]
     n = int(sv["offsets"][-1].item())
     rows = np.unique(np.random.default_rng(5).integers(0, n, 24))

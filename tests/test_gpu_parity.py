@@ -20,6 +20,8 @@ from tests._np_ref import to_np
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = list(inputs.CONFIGS)
+# tokens with a kept row compared at the workloads' full sizes (plus the first and the last)
+FULL_SAMPLES = 40
 # shapes the oracle runs in seconds; f not a multiple of the 128/256 tile width,
 # hidden widths leave a partial 64-wide K step
 SMALL = {
@@ -216,6 +218,27 @@ def test_grouped_ffn_schedule_orders(case):
     _check_grouped_ffn(cfg, np.array(counts, dtype=np.int32), case)
 
 
+# The ring kernel's shapes: gated and GELU products with K >= 4096 on 256-row
+# tiles (the top-2 layer's gate/up GEMM runs there), with groups of one and
+# two row tiles (column tile by column tile) and of five (row tile by row
+# tile); and K % 64 == 32 (both GEMMs), on 128- and 256-row tiles.
+RING_CASES = {
+    "ring_gated_k4096_bm256": ("top2_e8_h4096", dict(E=3, K=1, h=4096, f=512), [1100, 300, 1300]),
+    "ring_gated_k4096_two_orders": ("top2_e8_h4096", dict(E=3, K=1, h=4096, f=384), [200, 450, 1300]),
+    "ring_gelu_k4096_bm256": ("switch_top1_e64_zipf", dict(E=3, K=1, h=4096, f=512), [900, 200, 1400]),
+    "ring_k32_tail_bm128": ("top2_e8_h4096", dict(E=6, K=1, h=544, f=352), [130, 256, 300, 513, 0, 90]),
+    "ring_k32_tail_bm256": ("top2_e8_h4096", dict(E=2, K=1, h=544, f=352), [700, 650]),
+    "ring_k32_tail_gelu": ("switch_top1_e64_zipf", dict(E=3, K=1, h=544, f=352), [700, 0, 900]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RING_CASES))
+def test_grouped_ffn_ring_kernel(case):
+    name, over, counts = RING_CASES[case]
+    cfg = inputs.variant(name, T=sum(counts), capacity_factor=0.0, **over)
+    _check_grouped_ffn(cfg, np.array(counts, dtype=np.int32), case)
+
+
 def _check_grouped_ffn(cfg, counts, label):
     H, E = cfg.get("H", 1), cfg["E"]
     Gn, dd, f = H * E, cfg["h"] // H, cfg["f"]
@@ -240,14 +263,18 @@ def _check_grouped_ffn(cfg, counts, label):
     xin = (xin.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if xin.dtype == np.uint16 else xin.astype(np.float64)
     ref = np.empty((N, dd))
     mag = np.empty((N, dd))
+    sig = np.empty((N, dd))
     wg, wu, wd = to_np(inp["w_gate"]), to_np(inp["w_up"]), to_np(inp["w_down"])
     for e in range(Gn):
         a, b = offsets[e], offsets[e + 1]
         if a == b:
             continue
-        ref[a:b], mag[a:b] = orc.expert_ffn(cfg, dd, wg[e], None if wu is None else wu[e], wd[e], xin[a:b],
-                                            with_mag=True)
-    st = G.assert_close(got[:N], ref, cfg["dtype"], f"y_perm {label}", mag=mag, mag_unit=2.0 ** -9)
+        ref[a:b], mag[a:b], sig[a:b] = orc.expert_ffn(cfg, dd, wg[e], None if wu is None else wu[e], wd[e],
+                                                      xin[a:b], with_mag=True)
+    # every row: one intermediate rounding (H) before the stored bf16 row
+    st = G.assert_close(got[:N], ref, cfg["dtype"], f"y_perm {label}", mag=mag, sig=sig, n_round=1,
+                        n_acc=max(dd, f))
+    G.record(f"grouped_ffn {label}", st)
     G.log(f"   {st}")
     # rows past the last group are untouched
     assert np.all(got[N:] == 7.0)
@@ -373,7 +400,8 @@ def _compare_layer(cfg, y, aux, ref, tokens=None):
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     sel = keep_tok[tok]
     yg = G.host(y)[tok][sel]
-    st = G.assert_close(yg, ref["y"][sel], cfg["dtype"], f"y {cfg.get('name')}", mag=ref["ymag"][sel])
+    st = G.assert_close(yg, ref["y"][sel], cfg["dtype"], f"y {cfg.get('name')}", mag=ref["ymag"][sel],
+                        sig=ref["ysig"][sel], n_acc=G.n_acc(cfg))
     n_ex = int(excl.sum())
     if n_ex == 0:
         assert np.array_equal(aux["counts"].cpu().numpy(), ref["counts"])
@@ -398,6 +426,7 @@ def test_layer_small(name):
     y, aux = G.run_layer(cfg, inp)
     ref = orc.layer_forward(cfg, G.np_inputs(inp), to_np(inp["x"]))
     st, n_ex = _compare_layer(cfg, y, aux, ref)
+    G.record(f"layer_small {cfg['name']}", st)
     G.log(f"   excluded={n_ex} {st}")
 
 
@@ -410,13 +439,21 @@ def test_layer_full_size_sampled(name):
     y, aux = G.run_layer(cfg, inp)
     G.log(f"[layer full] {name}: copying inputs to the host for the oracle")
     host_inp = {k: to_np(v) for k, v in inp.items()}
+    # sampled tokens: the first and the last, then tokens with at least one kept
+    # assignment (on the GPU's routing; the comparison checks it against the
+    # oracle's), so a layer that drops most assignments still compares FFN rows
+    H, K = cfg.get("H", 1), cfg["K"]
+    kept_tok = np.nonzero((aux["dest_row"].cpu().numpy().reshape(T, H * K) >= 0).any(1))[0]
     rng = np.random.default_rng(3)
-    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 10, replace=False)])).astype(np.int32)
-    G.log(f"[layer full] {name}: oracle on {tokens.size} sampled tokens")
+    n_s = min(FULL_SAMPLES, kept_tok.size)
+    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(kept_tok, n_s, replace=False)])).astype(np.int32)
+    G.log(f"[layer full] {name}: oracle on {tokens.size} sampled tokens ({kept_tok.size} of {T} keep a row)")
     ref = orc.layer_forward(cfg, host_inp, host_inp["x"], tokens=tokens)
-    ref_full = dict(ref)
-    ref_full["y"] = ref["y"]
-    st, n_ex = _compare_layer(cfg, y, aux, ref_full, tokens=tokens)
+    st, n_ex = _compare_layer(cfg, y, aux, ref, tokens=tokens)
+    rk = (ref["dest_row"] >= 0).reshape(T, H * K)[tokens].any(1)
+    assert rk.sum() >= min(n_s, 24), "too few sampled tokens keep an expert row"
+    G.record(f"layer_full_size {name}", dict(st, tokens=int(tokens.size), tokens_with_rows=int(rk.sum()),
+                                              excluded_in_batch=n_ex))
     G.log(f"   excluded={n_ex} of {T}; sampled {st}")
     del inp
     torch.cuda.empty_cache()
