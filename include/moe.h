@@ -234,7 +234,9 @@ moe_status moe_grouped_ffn_rows(const moe_desc *desc, const void *x, const int32
  * order, of topk_w[s][k] * y_perm[dest_row[s][k]][j] (fp32), plus
  * y_shared[t][j] when given (weight 1), rounded once.  A token whose
  * assignments are all dropped gets 0.
- *   y_shared [T][h] | NULL (H = 1 only);  y [T][h]. */
+ *   y_shared [T][h] | NULL (H = 1 only);  y [T][h].
+ * dest_row, topk_w, y_perm and y must be non-NULL when T > 0 (a NULL one is
+ * MOE_ERR_INVALID_ARG, nothing launched). */
 moe_status moe_combine(const moe_desc *desc, const int32_t *dest_row, const float *topk_w,
                        const void *y_perm, const void *y_shared, void *y, void *stream);
 

@@ -458,7 +458,9 @@ moe_status moe_combine(const moe_desc* d, const int32_t* dest_row, const float* 
     moe_status s = check_desc(d);
     if (s != MOE_OK) return s;
     if (d->T == 0) return MOE_OK;
-    if (!dest_row || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "dest_row, topk_w or y is NULL");
+    // any kept row is read from y_perm, and whether one is kept is known only on
+    // the device: a NULL y_perm is refused whenever there are assignments
+    if (!dest_row || !topk_w || !y_perm || !y) return fail(MOE_ERR_INVALID_ARG, "dest_row, topk_w, y_perm or y is NULL");
     if (y_shared && d->H != 1) return fail(MOE_ERR_UNSUPPORTED, "y_shared needs H = 1");
     CombineArgs a{};
     a.T = d->T; a.H = d->H; a.K = d->K; a.d = d->h / d->H; a.h = d->h; a.dtype = d->dtype;

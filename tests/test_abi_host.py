@@ -119,6 +119,10 @@ def test_stage_calls_validate_before_launch():
     assert L.moe_grouped_ffn_rows(C.byref(d), None, None, None, 10**9, None, None, None, None, None, 0, None, 0,
                                   None) == 1
     assert L.moe_combine(C.byref(d), None, None, None, None, None, None) == 1
+    # a NULL y_perm alone is refused too (kept rows would be read from it)
+    one = C.c_void_p(4096)
+    assert L.moe_combine(C.byref(d), one, one, None, None, one, None) == 1
+    assert "y_perm" in L.moe_last_error().decode()
     W = _ffi.MoeWeights()
     assert L.moe_layer_forward(C.byref(d), C.byref(W), None, None, None, None, 0, None) == 1
     # workspace too small -> WORKSPACE
