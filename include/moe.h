@@ -200,6 +200,24 @@ moe_status moe_permute(const moe_desc *desc, const int32_t *topk_idx, const void
                        int32_t *dest_row, int32_t *src_token, void *x_perm, int32_t *n_kept,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and validation as moe_permute
+ * (bit-identical outputs), minus ws / ws_bytes: its one scratch buffer, the
+ * per-chunk expert histogram of ceil(T*H*K / 1024) * H*E + 1 int32, lives in
+ * a static device array of moe_permute_noalloc_max_ints() int32 (4 MiB) that
+ * the library holds on each GPU it runs on until the process ends.  A larger
+ * problem is MOE_ERR_UNSUPPORTED (nothing launched).  The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress); no call
+ * allocates or frees memory.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. */
+moe_status moe_permute_noalloc(const moe_desc *desc, const int32_t *topk_idx, const void *x,
+                               int32_t capacity, int32_t *counts, int32_t *kept, int32_t *offsets,
+                               int32_t *dest_row, int32_t *src_token, void *x_perm, int32_t *n_kept,
+                               void *stream);
+size_t moe_permute_noalloc_max_ints(void);
+
 /* Expert FFNs as a ragged grouped GEMM (lesson 10, item 3: rows grouped by
  * expert run as one grouped GEMM).  H*E groups; group e owns rows
  * [offsets[e], offsets[e+1]) of x_perm / h_tmp / y_perm.

@@ -17,7 +17,7 @@ from ._ffi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FFN_GEMM1, MOE_FFN_GEMM2, M
 
 __all__ = [
     "MoeError", "MoeDesc", "desc_from_cfg", "moe_capacity", "moe_workspace_size", "moe_route",
-    "moe_route_hash", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_rows", "moe_combine", "moe_layer_forward", "moe_version", "lib",
+    "moe_route_hash", "moe_permute", "moe_permute_noalloc", "moe_permute_noalloc_max_ints", "moe_grouped_ffn", "moe_grouped_ffn_rows", "moe_combine", "moe_layer_forward", "moe_version", "lib",
     "moe_max_rows", "moe_layer_forward_train", "moe_layer_backward", "SAVED_KEYS", "GRAD_KEYS",
     "alloc_saved", "alloc_grads",
     "workspace",
@@ -117,6 +117,17 @@ def moe_permute(desc, topk_idx, x, capacity, counts, kept, offsets, dest_row, sr
     _check(lib().moe_permute(C.byref(desc), _ptr(topk_idx), _ptr(x), int(capacity), _ptr(counts),
                              _ptr(kept), _ptr(offsets), _ptr(dest_row), _ptr(src_token), _ptr(x_perm),
                              _ptr(n_kept), wp, wn, _stream(stream)))
+
+
+def moe_permute_noalloc(desc, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm,
+                        n_kept=None, stream=None):
+    _check(lib().moe_permute_noalloc(C.byref(desc), _ptr(topk_idx), _ptr(x), int(capacity), _ptr(counts),
+                                     _ptr(kept), _ptr(offsets), _ptr(dest_row), _ptr(src_token), _ptr(x_perm),
+                                     _ptr(n_kept), _stream(stream)))
+
+
+def moe_permute_noalloc_max_ints():
+    return int(lib().moe_permute_noalloc_max_ints())
 
 
 def moe_grouped_ffn(desc, x_perm, offsets, max_rows, w_gate, w_up, w_down, h_tmp, y_perm, flags=0,

@@ -69,6 +69,9 @@ SIGNATURES = {
     "moe_route_hash": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, _VP, _VP]),
     "moe_permute": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                               _VP, C.c_size_t, _VP]),
+    "moe_permute_noalloc": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP, _VP,
+                                      _VP, _VP]),
+    "moe_permute_noalloc_max_ints": (C.c_size_t, []),
     "moe_grouped_ffn": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP,
                                   C.c_uint32, _VP, C.c_size_t, _VP]),
     "moe_grouped_ffn_rows": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP,

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -372,11 +373,14 @@ moe_status moe_route_hash(const moe_desc* d, const int32_t* hash_keys, int32_t* 
     return MOE_OK;
 }
 
-moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t capacity,
-                       int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* dest_row,
-                       int32_t* src_token, void* x_perm, int32_t* n_kept, void* ws, size_t ws_bytes,
-                       void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// argument checks shared by moe_permute and moe_permute_noalloc
+moe_status check_permute(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t capacity,
+                         const int32_t* counts, const int32_t* kept, const int32_t* offsets, const int32_t* dest_row,
+                         const int32_t* src_token, const void* x_perm) {
     moe_status s = check_desc(d);
     if (s != MOE_OK) return s;
     if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity = %d < 0", capacity);
@@ -385,19 +389,93 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, const void* x
     if (p.A > 0 && (!topk_idx || !dest_row || !src_token))
         return fail(MOE_ERR_INVALID_ARG, "topk_idx, dest_row or src_token is NULL");
     if (x && !x_perm) return fail(MOE_ERR_INVALID_ARG, "x given but x_perm is NULL");
-    const size_t need = ws_bytes_of(d, MOE_WS_PERMUTE);
-    if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
-    Carver c(ws);
+    return MOE_OK;
+}
+
+moe_status run_permute(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t capacity, int32_t* counts,
+                       int32_t* kept, int32_t* offsets, int32_t* dest_row, int32_t* src_token, void* x_perm,
+                       int32_t* n_kept, int32_t* hist, hipStream_t stream) {
+    const Plan p = plan_of(d);
     PermuteArgs a{};
     a.A = p.A; a.K = p.K; a.H = p.H; a.Et = p.Et; a.d = p.d; a.h = p.h; a.dtype = d->dtype;
     a.capacity = capacity; a.queue = d->queue; a.topk_idx = topk_idx; a.x = x; a.counts = counts; a.kept = kept;
     a.offsets = offsets; a.dest_row = dest_row; a.src_token = src_token; a.x_perm = x_perm;
-    a.n_kept = n_kept; a.hist = carve_permute(c, p);
+    a.n_kept = n_kept; a.hist = hist;
     const int64_t byc = capacity >= INT32_MAX ? (int64_t)p.A : (int64_t)p.Et * capacity;
     a.max_rows = (int)(byc < p.A ? byc : p.A);
-    hipError_t e = launch_permute(a, (hipStream_t)stream);
+    hipError_t e = launch_permute(a, stream);
     if (e != hipSuccess) return dev_fail(e, "permute kernels");
     return MOE_OK;
+}
+
+// The scratch of moe_permute_noalloc: the per-chunk histogram [nch][H*E] int32
+// (nch = ceil(T*H*K / 1024)), at most kScratchInts entries.  One copy per GPU,
+// alive until the process ends, shared by every call on that GPU.  Nothing in
+// it has to start at zero (the histogram kernel writes every entry the scan
+// and rank kernels read).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchInts = (size_t)1 << 20;  // 4 MiB
+__device__ __align__(256) int32_t scratch[kScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_of_current_device(int32_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return dev_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return dev_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = (int32_t*)g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t capacity,
+                       int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* dest_row,
+                       int32_t* src_token, void* x_perm, int32_t* n_kept, void* ws, size_t ws_bytes,
+                       void* stream) {
+    g_err[0] = 0;
+    moe_status s = check_permute(d, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm);
+    if (s != MOE_OK) return s;
+    const size_t need = ws_bytes_of(d, MOE_WS_PERMUTE);
+    if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
+    Carver c(ws);
+    const Plan p = plan_of(d);
+    return run_permute(d, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm, n_kept,
+                       carve_permute(c, p), (hipStream_t)stream);
+}
+
+size_t moe_permute_noalloc_max_ints(void) { return kScratchInts; }
+
+moe_status moe_permute_noalloc(const moe_desc* d, const int32_t* topk_idx, const void* x, int32_t capacity,
+                               int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* dest_row,
+                               int32_t* src_token, void* x_perm, int32_t* n_kept, void* stream) {
+    g_err[0] = 0;
+    moe_status s = check_permute(d, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm);
+    if (s != MOE_OK) return s;
+    const Plan p = plan_of(d);
+    const size_t need = (size_t)p.nch * p.Et + 1;
+    if (need > kScratchInts)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_permute_noalloc: the histogram needs %zu int32 (ceil(T*H*K/1024) * H*E + 1), more than the "
+                    "%zu of its static scratch; use moe_permute with a workspace",
+                    need, kScratchInts);
+    int32_t* hist = nullptr;
+    if ((s = scratch_of_current_device(&hist)) != MOE_OK) return s;
+    return run_permute(d, topk_idx, x, capacity, counts, kept, offsets, dest_row, src_token, x_perm, n_kept, hist,
+                       (hipStream_t)stream);
 }
 
 static moe_status grouped_ffn(const moe_desc* d, const void* x_perm, const int32_t* src_rows,

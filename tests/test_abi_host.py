@@ -132,6 +132,19 @@ def test_stage_calls_validate_before_launch():
     assert L.moe_permute(C.byref(d), one, None, 4, one, one, one, one, one, None, None, None, 0, None) == 3
 
 
+def test_permute_noalloc_validates_before_launch():
+    L = _ffi.lib()
+    one = C.c_void_p(4096)
+    assert moe.moe_permute_noalloc_max_ints() == 1 << 20
+    d = _desc()
+    assert L.moe_permute_noalloc(C.byref(d), None, None, -1, None, None, None, None, None, None, None, None) == 1
+    assert L.moe_permute_noalloc(C.byref(d), None, None, 4, one, one, one, None, None, None, None, None) == 1
+    # a histogram beyond the static scratch (ceil(A/1024) * H*E + 1 > 2^20 int32) is refused
+    big = _desc(T=1 << 19, E=256, K=8, h=64, f=64)
+    assert L.moe_permute_noalloc(C.byref(big), one, None, 4, one, one, one, one, one, None, None, None) == 2
+    assert "static scratch" in L.moe_last_error().decode()
+
+
 def test_routing_variant_entry_points_validate():
     L = _ffi.lib()
     one = C.c_void_p(4096)
