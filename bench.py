@@ -13,7 +13,10 @@ more replayed from a HIP graph that captured one step (no host launches; the
 replay must give the eager output bit for bit).  Per-stage times come from the stage entry
 points timed the same way.  The dominant kernel (the grouped gate/up GEMM with
 the fused activation) is timed on its own for the roofline figure.  The CPU
-oracle is timed on a bounded sample of the same workload for the CPU baseline.
+oracle is timed on a bounded sample of the same workload for the CPU baseline
+(plus the tiny fp32 layer on one thread and on all threads).  The other four
+workloads are then timed the same way (layer step and stages) into the line's
+"workloads" object (--only skips them).
 Prints one JSON line.  `--train` times a training step instead, `--shard` the
 grouped FFN on one GPU's share of the 8-GPU expert/head-parallel layers, and
 `--counters` runs each stage a few times for rocprofv3 counter passes.
@@ -46,6 +49,9 @@ def parse():
                    help="override a workload field, e.g. the routing variants n_groups=8, group_limit=4, "
                         "gate=hash, queue=choice, capacity_factor_eval=1.5, eval=1")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--only", action="store_true",
+                   help="time the headline workload only (by default the other workloads are timed too, "
+                        "with their stages, into the line's \"workloads\" object)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the baseline sample")
     p.add_argument("--stage-reps", type=int, default=10)
     p.add_argument("--train", action="store_true",
@@ -301,39 +307,33 @@ def shard_bench(args):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library implements the "
-              "one-GPU layer, and its expert/head-parallel sharding exists as a design only.", file=sys.stderr)
-        sys.exit(2)
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measure_layer(args, cfg, over, headline):
+    """Times one workload's layer step and its stages; returns a dict.  With
+    headline, also the warm / cache-cold / graph-replay spreads, the roofline
+    object of the dominant kernel and (unless --no-cpu) the CPU baseline."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_45_amd as moe
     from mixture_experts_layer_45_amd import inputs
 
-    if args.shard:
-        return shard_bench(args)
-    name = args.workload or inputs.BENCH_WORKLOAD
-    over = {}
-    for kv in args.set:
-        k, v = kv.split("=", 1)
-        for conv in (int, float):
-            try:
-                v = conv(v)
-                break
-            except ValueError:
-                pass
-        over[k] = v
-    cfg = inputs.variant(name, **over)
     name = cfg["name"]
     T, h, H, E, K, f = cfg["T"], cfg["h"], cfg["H"], cfg["E"], cfg["K"], cfg["f"]
     d = h // H
     Et, A = H * E, T * H * K
     esz = 2 if cfg["dtype"] == "bf16" else 4
     dev = "cuda"
-    torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     log(f"[bench] workload {name}: generating inputs on the device")
     inp = inputs.make_inputs(cfg, dev, seed=0)
@@ -355,24 +355,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
+    log(f"[bench] {name}: timing {args.steps} steps")
+    ms_step = timed(step, args.steps, stream)
     tok_s = T / (ms_step * 1e-3)
 
-    # ---- per-step spread, warm and cache-cold (512 MB written before each step)
-    warm = spread(per_step(step, args.steps, stream), T)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = dict(spread(per_step(step, args.steps, stream, flush), T), flush_bytes=512 << 20)
-    del flush
-    graph = graph_per_step(step, args.steps, stream, T, y)
+    res = {}
+    if headline:
+        # ---- per-step spread, warm and cache-cold (512 MB written before each step)
+        res["warm_per_step"] = spread(per_step(step, args.steps, stream), T)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        res["cold_per_step"] = dict(spread(per_step(step, args.steps, stream, flush), T), flush_bytes=512 << 20)
+        del flush
+        res["graph_per_step"] = graph_per_step(step, args.steps, stream, T, y)
 
     # ---- routing facts of this batch (N, non-empty experts)
     n_kept = int(aux["n_kept"].item())
@@ -461,7 +455,7 @@ def main():
                 fn()
             torch.cuda.synchronize()
         print(json.dumps({"counters_run": name, "copy_bytes": 1 << 30}), flush=True)
-        return
+        return None
     gemm1()
     gemm2()
     if shared_fn:
@@ -534,7 +528,21 @@ def main():
     if cfg.get("n_shared"):
         total_flops += 2.0 * (n_act + 1) * T * h * f
 
-    roofline = {
+    res.update({
+        "ms_per_step": ms_step, "tokens_per_s": tok_s, "tflops": total_flops / (ms_step * 1e-3) / 1e12,
+        "dtype": cfg["dtype"],
+        "config": {"workload": name, "tokens": T, "hidden": h, "heads": H, "experts": E, "top_k": K,
+                   "ffn": f, "act": cfg["act"], "score": cfg["score"], "capacity_factor": cfg["capacity_factor"],
+                   "parallelism": "single GPU", **({"variant": over} if over else {})},
+        "n_kept": n_kept, "n_dropped": A - n_kept, "nonempty_experts": nonempty, "l_aux": l_aux,
+        "stages": stages,
+    })
+    if not headline:
+        del inp, ws, ws_r, ws_p, ws_f, x_perm, h_tmp, y_perm
+        torch.cuda.empty_cache()
+        return res
+
+    res["roofline"] = {
         "kernel": "grouped GEMM1: gate/up projections + SwiGLU" if n_act == 2 else
                   "grouped GEMM1: projection + GELU",
         "bound": "mfma", "achieved": g1_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
@@ -568,20 +576,84 @@ def main():
         log(f"[bench] oracle: {Ts} tokens in {elapsed:.2f} s on {threads} threads")
         cpu = {"value": Ts / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"first {Ts} tokens of the {name} batch as their own batch (capacity for {Ts} "
-                         f"tokens), full weights; fp64 C oracle, {elapsed:.1f} s"}
+                         f"tokens), full weights; fp64 C oracle, {elapsed:.1f} s",
+               "cpu_model": cpu_model()}
+        del host
+        # the tiny fp32 layer (all 256 tokens) on one thread and on all of them
+        tiny = inputs.CONFIGS["tiny_f32"]
+        th = {k: to_np(v) for k, v in inputs.make_inputs(tiny, "cpu", seed=0).items()}
+        for n_thr, key in ((1, "tiny_f32_single_thread"), (threads, "tiny_f32_all_threads")):
+            orc.set_num_threads(n_thr)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                orc.layer_forward(tiny, th, th["x"])
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= 1.0:
+                    break
+            cpu[key] = {"tokens_per_s": reps * tiny["T"] / el, "ms_per_layer": el / reps * 1e3, "threads": n_thr}
+        orc.set_num_threads(threads)
+    res["cpu_baseline"] = cpu
+    return res
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library implements the "
+              "one-GPU layer, and its expert/head-parallel sharding exists as a design only.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_layer_45_amd import inputs
+
+    if args.shard:
+        return shard_bench(args)
+    torch.cuda.set_device(0)
+    name = args.workload or inputs.BENCH_WORKLOAD
+    over = {}
+    for kv in args.set:
+        k, v = kv.split("=", 1)
+        for conv in (int, float):
+            try:
+                v = conv(v)
+                break
+            except ValueError:
+                pass
+        over[k] = v
+    cfg = inputs.variant(name, **over)
+    head = measure_layer(args, cfg, over, headline=True)
+    if head is None or args.train:
+        return
+    others = {}
+    if not args.only and not over and args.workload is None:
+        for wname in inputs.CONFIGS:
+            if wname == cfg["name"]:
+                continue
+            r = measure_layer(args, inputs.variant(wname), {}, headline=False)
+            st = r["stages"]
+            others[wname] = {
+                "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"], "tflops": r["tflops"],
+                "dtype": r["dtype"], "n_kept": r["n_kept"], "nonempty_experts": r["nonempty_experts"],
+                "l_aux": r["l_aux"],
+                "ffn_mfma_frac": st["ffn_mfma_frac"], "ffn_attainable_frac": st["ffn_attainable_frac"],
+                "ffn_bound": st["ffn_bound"], "gemm1_mfma_frac": st["gemm1_mfma_frac"],
+                "gemm2_mfma_frac": st["gemm2_mfma_frac"], "route_hbm_frac": st["route_hbm_frac"],
+                "permute_hbm_frac": st["permute_hbm_frac"], "combine_hbm_frac": st["combine_hbm_frac"],
+                "stages": st,
+            }
     out = {
         "metric": "MoE-layer fwd tokens/sec on 1 GPU (grouped-FFN % MFMA peak; route/permute % HBM BW)",
-        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg["dtype"], "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
-        "config": {"workload": name, "tokens": T, "hidden": h, "heads": H, "experts": E, "top_k": K,
-                   "ffn": f, "act": cfg["act"], "score": cfg["score"], "capacity_factor": cfg["capacity_factor"],
-                   "parallelism": "single GPU", **({"variant": over} if over else {})},
-        "tflops": total_flops / (ms_step * 1e-3) / 1e12,
-        "n_kept": n_kept, "n_dropped": A - n_kept, "nonempty_experts": nonempty, "l_aux": l_aux,
-        "warm_per_step": warm, "cold_per_step": cold, "graph_per_step": graph,
-        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": head["config"], "tflops": head["tflops"],
+        "n_kept": head["n_kept"], "n_dropped": head["n_dropped"], "nonempty_experts": head["nonempty_experts"],
+        "l_aux": head["l_aux"],
+        "warm_per_step": head["warm_per_step"], "cold_per_step": head["cold_per_step"],
+        "graph_per_step": head["graph_per_step"], "stages": head["stages"], "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "workloads": others or None,
     }
     print(json.dumps(out), flush=True)
 

@@ -692,6 +692,16 @@ int orc_layer_forward(const orc_desc *d, const orc_weights *w, const void *x,
     return 0;
 }
 
+/* sets the number of threads the oracle's parallel loops use (n >= 1) */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* number of threads the oracle's parallel loops use */
 int orc_num_threads(void)
 {

@@ -109,6 +109,8 @@ def lib():
                                             C.c_double, C.c_int, C.POINTER(OrcGrads)]
         _lib.orc_num_threads.restype = C.c_int
         _lib.orc_num_threads.argtypes = []
+        _lib.orc_set_num_threads.restype = None
+        _lib.orc_set_num_threads.argtypes = [C.c_int]
     return _lib
 
 
@@ -377,6 +379,10 @@ def layer_backward(cfg, weights, x, dy, c_aux=1.0, magnitude=False):
 
 def num_threads():
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n):
+    lib().orc_set_num_threads(int(n))
 
 
 # ------------------------------------------- expert-parallel load report
