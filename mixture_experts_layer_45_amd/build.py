@@ -61,5 +61,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """The library with its host code (argument validation, workspace layout,
+    launch set-up) built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (clang's runtime; the device code is built as usual): api.hip is compiled
+    again with the sanitizers on the host pass only, the other objects are the
+    ones build() made.  For the CPU sanitizer test."""
+    objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: missing {missing}")
+    obj = out + ".api.o"
+    san = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    cmd = COMMON + san + ["-c", os.path.join(CSRC, "api.hip"), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on api.hip (sanitised):\n{r.stdout}\n{r.stderr}")
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address,undefined",
+           "-shared-libsan", "-o", out, obj] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (sanitised):\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -12,17 +12,22 @@ SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False, out: str = None) -> str:
+    """sanitize: AddressSanitizer + UndefinedBehaviorSanitizer build (load it
+    with gcc's libasan preloaded), written to `out`."""
+    lib = out or LIB
     cmd = [
         "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
         "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wno-unknown-pragmas",
-        SRC, "-o", LIB + ".tmp", "-lm",
     ]
+    if sanitize:
+        cmd += ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+    cmd += [SRC, "-o", lib + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

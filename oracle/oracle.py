@@ -26,7 +26,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# MOE_ORACLE_LIB_PATH names another build of the oracle (the ASan/UBSan build
+# of the CPU sanitizer test); by default the in-tree liboracle.so
+LIB_PATH = os.environ.get("MOE_ORACLE_LIB_PATH") or os.path.join(HERE, "liboracle.so")
 
 
 class OrcDesc(C.Structure):
