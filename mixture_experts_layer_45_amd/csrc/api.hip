@@ -614,12 +614,26 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
     pa.x_perm = nullptr; pa.n_kept = nullptr; pa.hist = L.hist; pa.max_rows = p.max_rows;
     if ((e = launch_permute(pa, st)) != hipSuccess) return dev_fail(e, "permute kernels");
 
+    // One slot per token (K = 1, one head, nothing added after the routed
+    // sum): the gate weight is exactly 1 and a token has at most one row, so
+    // the down GEMM's epilogue stores each expert row straight to its token's
+    // row of y (lesson 10, item 3, the un-permute fused into the expert GEMM),
+    // which is bitwise what the combine would write; tokens whose assignment
+    // was dropped get 0.  The training forward keeps y_perm (the backward
+    // reads it) and so the combine.
+    const bool fused_combine = !sv && p.K == 1 && p.H == 1 && !d->n_shared && !d->has_wo && ((uintptr_t)y & 15) == 0;
+    if (fused_combine && (e = launch_zero_dropped(dest_row, p.T, p.h * p.esz, y, st)) != hipSuccess)
+        return dev_fail(e, "zero-dropped kernel");
+
     FfnArgs fa{};
     fa.G = p.Et; fa.d = p.d; fa.f = p.f; fa.dtype = d->dtype; fa.act = d->act; fa.max_rows = p.max_rows;
     fa.x_perm = x; fa.src_rows = L.src_token; fa.a_nrows = p.T * p.H;
     fa.offsets = L.offsets; fa.w_gate = w->w_gate; fa.w_up = w->w_up;
-    fa.w_down = w->w_down; fa.h_tmp = L.h_tmp; fa.y_perm = L.y_perm; fa.flags = 0; fa.tiles = L.tiles;
+    fa.w_down = w->w_down; fa.h_tmp = L.h_tmp; fa.y_perm = fused_combine ? y : L.y_perm; fa.flags = 0;
+    fa.tiles = L.tiles;
     fa.act_save = sv ? sv->act_grad : nullptr;
+    fa.c_rows = fused_combine ? L.src_token : nullptr;
+    fa.c_nrows = p.T;
     if ((e = launch_ffn(fa, st)) != hipSuccess) return dev_fail(e, "grouped ffn kernels");
 
     if (d->n_shared) {
@@ -632,12 +646,14 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
         if ((e = launch_ffn(sa, st)) != hipSuccess) return dev_fail(e, "shared expert kernels");
     }
 
-    CombineArgs ca{};
-    ca.T = p.T; ca.H = p.H; ca.K = p.K; ca.d = p.d; ca.h = p.h; ca.dtype = d->dtype;
-    ca.dest_row = dest_row; ca.topk_w = topk_w; ca.y_perm = L.y_perm;
-    ca.y_shared = d->n_shared ? L.y_sh : nullptr;
-    ca.y = d->has_wo ? L.y_cat : y;
-    if ((e = launch_combine(ca, st)) != hipSuccess) return dev_fail(e, "combine kernel");
+    if (!fused_combine) {
+        CombineArgs ca{};
+        ca.T = p.T; ca.H = p.H; ca.K = p.K; ca.d = p.d; ca.h = p.h; ca.dtype = d->dtype;
+        ca.dest_row = dest_row; ca.topk_w = topk_w; ca.y_perm = L.y_perm;
+        ca.y_shared = d->n_shared ? L.y_sh : nullptr;
+        ca.y = d->has_wo ? L.y_cat : y;
+        if ((e = launch_combine(ca, st)) != hipSuccess) return dev_fail(e, "combine kernel");
+    }
 
     if (d->has_wo && (e = launch_dense(p.T, p.h, p.h, d->dtype, L.y_cat, w->w_o, y, L.tiles_wo, L.off_wo, st)) != hipSuccess)
         return dev_fail(e, "output projection kernel");

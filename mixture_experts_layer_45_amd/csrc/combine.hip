@@ -109,6 +109,30 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// K = 1, one head: the row of a token whose one assignment was dropped is 0;
+// a kept token's row is left alone (the down GEMM stores it there).  One row
+// per `tpr` threads, 16-byte stores.
+__global__ __launch_bounds__(256) void zero_dropped_kernel(const int32_t* dest_row, int T, int row16, int tpr,
+                                                           uint4* y) {
+    const int rpb = 256 / tpr;
+    const long t = (long)blockIdx.x * rpb + threadIdx.x / tpr;
+    if (t >= T || dest_row[t] >= 0) return;
+    uint4* row = y + t * row16;
+    for (int j = threadIdx.x % tpr; j < row16; j += tpr) row[j] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_dropped(const int32_t* dest_row, int T, int row_bytes, void* y, hipStream_t st) {
+    if (T == 0) return hipSuccess;
+    if (row_bytes % 16 != 0 || ((uintptr_t)y & 15) != 0) return hipErrorInvalidValue;
+    const int row16 = row_bytes / 16;
+    int tpr = 1;
+    while (tpr * 2 <= row16 && tpr < 256) tpr *= 2;
+    const int rpb = 256 / tpr;
+    hipLaunchKernelGGL(zero_dropped_kernel, dim3((T + rpb - 1) / rpb), dim3(256), 0, st, dest_row, T, row16, tpr,
+                       (uint4*)y);
+    return hipGetLastError();
+}
+
 // f_e = counts_e / (T K); P as given; L_aux = mean over heads of alpha E sum_e f_e P_e
 // (fixed-order serial sums; E_tot is small).  One block.
 __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {

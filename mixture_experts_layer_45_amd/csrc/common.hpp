@@ -107,6 +107,8 @@ struct FfnArgs {
     uint32_t flags;
     GemmTile* tiles;  // ws: tile table
     void* act_save;   // training: GEMM1 also stores its pre-activations here [max_rows][n_act*f], or null
+    const int32_t* c_rows;  // null, or row i of GEMM2 is stored to row c_rows[i] of y_perm (clamped to [0, c_nrows))
+    int c_nrows;
 };
 size_t ffn_workspace_bytes(int G, int max_rows, int dtype);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st);
@@ -154,6 +156,9 @@ struct CombineArgs {
     void* y;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+// K = 1, one head: y[t] = 0 for every token whose assignment was dropped (the
+// kept ones are stored by the down GEMM's epilogue)
+hipError_t launch_zero_dropped(const int32_t* dest_row, int T, int row_bytes, void* y, hipStream_t st);
 
 struct StatsArgs {
     int T, H, E, K, A;

@@ -130,6 +130,9 @@ struct GArgs {
     int32_t* claim;     // 8 zeroed tile-claim counters for this launch (persistent kernels)
     float* partial;     // fp32 partial tiles of the split last round (64-wide kernel), or null
     const int32_t* a_rows;  // row map: tile row i reads row a_rows[i] of A (null: row i)
+    const int32_t* c_rows;  // row map of the plain, gated and GELU epilogues: tile row i is stored to row
+                            // c_rows[i] of C, clamped to [0, c_nrows) (null: row i)
+    int c_nrows;
     // 64-wide kernel only:
     void* aux;              // pre-activations: written by the SAVE modes, read by the D modes
     const int2* kspan;      // per group {first 64-wide k stage, k stages}, or null (0, K/64)
@@ -148,6 +151,11 @@ __device__ __forceinline__ int a_row(const GArgs& a, int r, int nrows) {
     if (a.a_mod > 0) return r % a.a_mod;
     if (!a.a_rows) return r;
     return min(max(a.a_rows[r], 0), nrows - 1);
+}
+
+// the C row that tile row r is stored to
+__device__ __forceinline__ int c_row(const int32_t* c_rows, int c_nrows, int r) {
+    return c_rows ? min(max(c_rows[r], 0), c_nrows - 1) : r;
 }
 
 // The last round of an XCD's slice is usually short (r < B tiles for B blocks):
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GArgs a) {
             for (int i = 0; i < 16; ++i) {
                 const int row = row0 + wm * C::WM + tm * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
                 if (row < row_end && col < Nout)
-                    Cp[(size_t)row * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
+                    Cp[(size_t)c_row(a.c_rows, a.c_nrows, row) * Nout + col] = f32_to_bf16(acc[tm * C::TN + tn][i]);
             }
         }
 }
@@ -508,7 +516,8 @@ __device__ __forceinline__ float dgelu_f(float a) {
 
 template <typename C, int MODE>
 __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
-                                                  int wm, int wn, int lane, uint8_t* aux = nullptr) {
+                                                  int wm, int wn, int lane, uint8_t* aux = nullptr,
+                                                  const int32_t* c_rows = nullptr, int c_nrows = 0) {
     if constexpr (MODE == MODE_DSWIGLU || MODE == MODE_DGELU) {
         // acc holds dH; aux the saved pre-activations; C gets da (and du)
         constexpr int NA = MODE == MODE_DSWIGLU ? 2 : 1;
@@ -634,6 +643,7 @@ __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int r
 #pragma clang loop unroll(full)
     for (int tm = 0; tm < C::TM; ++tm) {
         const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+        const int crow = row < row_end ? c_row(c_rows, c_nrows, row) : row;
 #pragma clang loop unroll(full)
         for (int tn = 0; tn < C::TN; ++tn) {
             const floatx16& v = acc[tm * C::TN + tn];
@@ -646,7 +656,7 @@ __device__ __forceinline__ void rowstore_epilogue(floatx16* acc, int row0, int r
                 const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
                 const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
                 const int col = n0 + wn * C::WNM + tn * 32 + 16 * pp + (hi ? 8 : 0);
-                if (row < row_end && col < Nout) *(u32x4*)(Cp + ((size_t)row * Nout + col) * 2) = o;
+                if (row < row_end && col < Nout) *(u32x4*)(Cp + ((size_t)crow * Nout + col) * 2) = o;
             }
         }
     }
@@ -826,7 +836,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
             setup(s_next, nxt);
             prologue(nxt);
         }
-        rowstore_epilogue<C, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane, (uint8_t*)a.aux);
+        rowstore_epilogue<C, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane, (uint8_t*)a.aux,
+                                   a.c_rows, a.c_nrows);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -1225,7 +1236,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             k64_store_partial<BM, MODE>(acc, a.partial, cur.slot, tid);
         else
             rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane,
-                                                      (uint8_t*)a.aux);
+                                                      (uint8_t*)a.aux, a.c_rows, a.c_nrows);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -1270,7 +1281,7 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
             }
     }
     rowstore_epilogue<K64Cfg<BM, MODE>, MODE>(acc, tl.row0, tl.row_end, nt * C::BNM, a.Nout, (uint8_t*)a.C, wave >> 2, wave & 3, lane,
-                                              (uint8_t*)a.aux);
+                                              (uint8_t*)a.aux, a.c_rows, a.c_nrows);
 }
 
 
@@ -1327,7 +1338,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GArgs a) {
             } else {
                 v = acc[0][i][j];
             }
-            Cp[(size_t)row * Nout + col] = v;
+            Cp[(size_t)c_row(a.c_rows, a.c_nrows, row) * Nout + col] = v;
         }
 }
 
@@ -1552,6 +1563,8 @@ hipError_t launch_ffn(const FfnArgs& f, hipStream_t st) {
         g.K = f.f;
         g.Nout = f.d;
         g.a_bytes = (long long)f.max_rows * f.f * (f.dtype == MOE_BF16 ? 2 : 4);
+        g.c_rows = f.c_rows;
+        g.c_nrows = f.c_nrows;
         err = run_gemm(f.dtype, BM, MODE_PLAIN, g, st);
         if (err != hipSuccess) return err;
     }

@@ -510,3 +510,53 @@ def test_empty_batch_leaves_output_untouched():
     moe.moe_layer_forward(d, inp, inp["x"], y, None, None)
     torch.cuda.synchronize()
     assert torch.all(y == 3.0)
+
+
+# ------------------------------------------- one slot per token: fused un-permute
+K1_CASES = {
+    "switch_gelu_drops": ("switch_top1_e64_zipf", dict(T=2000, h=256, f=512, E=16)),
+    "hash_gate": ("switch_top1_e64_zipf", dict(T=1500, h=256, f=320, E=12, gate="hash", logit_bias=None)),
+    "softmax_k1_swiglu": ("top2_e8_h4096", dict(T=900, h=512, f=384, K=1, capacity_factor=0.9)),
+    "sigmoid_k1": ("sigmoid_top8_e256_shared", dict(T=700, h=256, f=192, E=24, K=1, n_shared=0,
+                                                    capacity_factor=1.0)),
+    "fp32_k1": ("tiny_f32", dict(T=300, K=1, capacity_factor=1.0)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(K1_CASES))
+def test_fused_combine_k1_matches_stagewise(case):
+    """With one slot per token the layer stores the down GEMM's rows straight to
+    their tokens' rows of y (and zeros for dropped tokens): bitwise the output of
+    the stage-wise path (route, permute, grouped FFN into y_perm, combine)."""
+    name, over = K1_CASES[case]
+    cfg = inputs.variant(name, **over)
+    T, K, E, h, f = cfg["T"], cfg["K"], cfg["E"], cfg["h"], cfg["f"]
+    G.log(f"[fused combine K=1] {case}")
+    inp = G.dev_inputs(cfg)
+    y_layer, aux = G.run_layer(cfg, inp)
+    assert (aux["dest_row"] < 0).any() or cfg.get("capacity_factor", 0) <= 0 or case == "hash_gate"
+    d = moe.desc_from_cfg(cfg)
+    idx, w = i32((T, K)), f32((T, K))
+    if cfg.get("gate") == "hash":
+        moe.moe_route_hash(d, None, idx, w)
+    else:
+        moe.moe_route(d, inp["x"], inp["w_router"], inp["logit_bias"], inp["select_bias"], None, 0, idx, w, None,
+                      None, moe.workspace(d, moe.MOE_WS_ROUTE))
+    C = orc.capacity(cfg)
+    counts, kept, offsets, dest, src, nk = i32(E), i32(E), i32(E + 1), i32(T), i32(T), i32(1)
+    moe.moe_permute(d, idx, None, moe.INT32_MAX if C is None else C, counts, kept, offsets, dest, src, None, nk,
+                    moe.workspace(d, moe.MOE_WS_PERMUTE))
+    dt = inputs.torch_dtype(cfg)
+    h_tmp = torch.empty((T, f), dtype=dt, device=G.DEV)
+    y_perm = torch.empty((T, h), dtype=dt, device=G.DEV)
+    moe.moe_grouped_ffn_rows(d, inp["x"], src, offsets, T, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
+                             y_perm, 0, moe.workspace(d, moe.MOE_WS_FFN))
+    y_stage = torch.full((T, h), 5.0, dtype=dt, device=G.DEV)
+    moe.moe_combine(d, dest, w, y_perm, None, y_stage)
+    torch.cuda.synchronize()
+    assert torch.equal(dest, aux["dest_row"])
+    iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(y_layer.view(iv), y_stage.view(iv))
+    # and the layer against the oracle
+    ref = orc.layer_forward(cfg, G.np_inputs(inp), to_np(inp["x"]))
+    _compare_layer(cfg, y_layer, aux, ref)
