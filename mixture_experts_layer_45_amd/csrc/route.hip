@@ -40,13 +40,13 @@ constexpr int RT_ROWS = 16;
 constexpr int kMaxParts = 8;  // partial-logit slices of the split-K router GEMM
 constexpr int RT_THREADS = 256;
 
-// tokens per route block: 16, except for bf16 routers with 17..64 experts
+// tokens per route block: 16, except for bf16 routers with 17..64 experts (64)
 static bool route_split_applies(int T, int h, int H, int E, int dtype);
 constexpr int RT_ROWS_SPLIT = 4;  // tokens per selection block behind the split-K router GEMM
 int route_rows(int T, int h, int H, int E, int dtype) {
     if (route_split_applies(T, h, H, E, dtype)) return RT_ROWS_SPLIT;
     if (dtype != MOE_BF16 || E <= 16 || E > 64) return RT_ROWS;
-    return E <= 32 ? 2 * RT_ROWS : 4 * RT_ROWS;
+    return 4 * RT_ROWS;
 }
 int route_blocks(int T, int h, int H, int E, int dtype) {
     const int r = route_rows(T, h, H, E, dtype);
@@ -382,8 +382,10 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 routers with at most 64 experts per head: RS = 16*R tokens of one head
-// per block (R = 1, 2, 4 for E <= 16, 32, 64, so that the router rows a block
-// reads stay small next to its token rows).  Phase 1 as above, the four waves
+// per block (R = 1 for E <= 16, 4 for E <= 64, so that the router rows a block
+// reads stay small next to its token rows; measured on one MI355X, 8 heads of
+// 32 experts over 8192 tokens: R = 4 took the route from 35.3 to 29.2 us, while
+// R = 2 or 4 for 8 experts was no faster than R = 1).  Phase 1 as above, the four waves
 // splitting the reduction over d, with R x NB MFMA tiles per wave and U k steps
 // of loads in flight.  Phase 2 gives each token 256/RS lanes (16, 8 or 4), each
 // holding every LPT-th expert of the token's row of logits in registers: an
@@ -766,7 +768,7 @@ hipError_t launch_route(const RouteArgs& a0, hipStream_t st) {
     }
     if (a.dtype == MOE_BF16 && a.E <= 64) {
         if (a.E <= 16) return launch_small<1, 1>(a, st);
-        if (a.E <= 32) return launch_small<2, 2>(a, st);
+        if (a.E <= 32) return launch_small<2, 4>(a, st);
         return launch_small<4, 4>(a, st);
     }
     if (a.E <= 16) return launch_nb<1>(a, st);
