@@ -15,12 +15,17 @@
 //   1. hist:    per-chunk expert counts (LDS integer atomics; exact):
 //               hist[chunk][e].
 //   2. scan:    per expert, the exclusive prefix over chunks (chunk order), the
-//               totals (counts), kept = min(counts, C) and offsets = exclusive
-//               prefix of kept.  One block; each expert's column of chunk
-//               counts is cut into segments, one thread each (consecutive lanes
-//               take consecutive experts, so every access is coalesced):
-//               segment sums, their prefix, then each segment rewritten in
-//               place.  Integer sums: exact.
+//               totals (counts) and kept = min(counts, C); blocks of 16 or
+//               more experts, each expert's column of chunk counts cut into
+//               segments, one thread each (consecutive lanes take consecutive
+//               experts, so every access is coalesced): segment sums, their
+//               prefix, then each segment rewritten in place.  The offsets
+//               (exclusive prefix of kept) are formed by every rank block.
+//               Integer sums: exact.
+//   When the histogram is small (chunks x experts <= 8192, at most 1024
+//   experts), steps 2 and 3 share one launch: each chunk's rank block reads
+//   the whole histogram and forms its own bases, the totals, kept and the
+//   offsets (the same integer sums, so the same tables).
 //   3. rank:    each chunk walks its ids 64 at a time in order; lanes holding
 //               the same expert find each other with ballots over the bits of
 //               the id, a lane's rank among them is the popcount of the lower
@@ -45,45 +50,56 @@ __device__ __forceinline__ int queue_at(int i, int S, int K, bool choice) {
     return (i - k * S) * K + k;
 }
 
+// the chunk's ids in queue order, position a0 + 64 j + lane in v[j] (-1 past A);
+// all CHUNK/64 loads are issued before any is used
+__device__ __forceinline__ void load_chunk(const int32_t* idx, int a0, int A, int K, bool choice, int32_t* v) {
+    const int S = A / K;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < CHUNK / 64; ++j) {
+        const int i = a0 + 64 * j + lane;
+        v[j] = i < A ? idx[queue_at(i, S, K, choice)] : -1;
+    }
+}
+
 __global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nch,
                                                   int32_t* hist) {
     __shared__ int cnt[MAX_ET];
+    int32_t v[CHUNK / 64];
+    load_chunk(idx, blockIdx.x * CHUNK, A, K, choice, v);
     for (int e = threadIdx.x; e < Et; e += 64) cnt[e] = 0;
     __syncthreads();
-    const int a0 = blockIdx.x * CHUNK;
-    const int a1 = min(a0 + CHUNK, A);
-    const int S = A / K;
-    for (int i = a0 + threadIdx.x; i < a1; i += 64) {
-        const int e = idx[queue_at(i, S, K, choice)];
-        if ((unsigned)e < (unsigned)Et) atomicAdd(&cnt[e], 1);  // out-of-range ids are dropped
-    }
+#pragma unroll
+    for (int j = 0; j < CHUNK / 64; ++j)
+        if ((unsigned)v[j] < (unsigned)Et) atomicAdd(&cnt[v[j]], 1);  // out-of-range ids are dropped
     __syncthreads();
     for (int e = threadIdx.x; e < Et; e += 64) hist[(size_t)blockIdx.x * Et + e] = cnt[e];
 }
 
-// One block of 1024 threads.  hist [nch][Et] is rewritten in place as the
-// per-chunk exclusive base of each expert.  S threads per expert (S a power of
-// two, S * Et <= 1024 when Et <= 1024), each owning a contiguous run of the
-// chunks; larger Et loop over experts with S = 1.
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int Et, int capacity,
-                                                    int32_t* counts, int32_t* kept, int32_t* offsets,
-                                                    int32_t* n_kept) {
+// Experts [blockIdx.x * epb, +epb) per block of 1024 threads.  hist [nch][Et]
+// is rewritten in place as the per-chunk exclusive base of each expert.  S
+// threads per expert (S a power of two, S * epb <= 1024), each owning a
+// contiguous run of the chunks; counts and kept follow from the totals.  The
+// offsets (a prefix over all experts) are left to the rank blocks.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int Et, int epb, int capacity,
+                                                    int32_t* counts, int32_t* kept) {
     __shared__ int32_t seg[1024];
-    __shared__ int32_t part[1024];
     const int tid = threadIdx.x;
+    const int eb = blockIdx.x * epb, ee = min(eb + epb, Et);
     int S = 1;
-    while (S * 2 * Et <= 1024 && S * 2 <= nch) S *= 2;
+    while (S * 2 * epb <= 1024 && S * 2 <= nch) S *= 2;
     const int epp = 1024 / S;              // experts per pass
     const int L = (nch + S - 1) / S;       // chunks per segment
     const int el = tid % epp, sg = tid / epp;  // expert within the pass, segment
-    for (int e0 = 0; e0 < Et; e0 += epp) {
+    for (int e0 = eb; e0 < ee; e0 += epp) {
         const int e = e0 + el;
+        const bool mine = el < epp && e < ee;
         const int c0 = min(sg * L, nch), c1 = min(c0 + L, nch);
         int32_t* col = hist + e;  // chunk c of expert e at col[c * Et]
         // segments are read 16 counts at a time, so 16 loads are in flight
         constexpr int B = 16;
         int32_t sum = 0;
-        if (e < Et)
+        if (mine)
             for (int cb = c0; cb < c1; cb += B) {
                 int32_t v[B];
 #pragma unroll
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int 
         __syncthreads();
         int32_t base = 0;  // chunks of this expert before the segment
         for (int q = 0; q < sg; ++q) base += seg[q * epp + el];
-        if (e < Et) {
+        if (mine) {
             for (int cb = c0; cb < c1; cb += B) {
                 int32_t v[B];
 #pragma unroll
@@ -113,64 +129,66 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* hist, int nch, int 
         }
         __syncthreads();
     }
-    // offsets: exclusive prefix of kept over experts (each thread owns a run)
-    const int per = (Et + 1023) / 1024;
-    int32_t run = 0;
+}
+
+// One wave: off[0..Et) (LDS) holds each expert's kept count and becomes its
+// first row, the exclusive prefix over the experts (lane l owns the run
+// [l*per, (l+1)*per)); with `store`, also written to offsets[0..Et] and n_kept.
+__device__ __forceinline__ void offsets_from_kept(int32_t* off, int Et, bool store, int32_t* offsets,
+                                                  int32_t* n_kept) {
+    const int lane = threadIdx.x & 63;
+    const int per = (Et + 63) / 64;
+    int32_t loc = 0;
     for (int q = 0; q < per; ++q) {
-        const int e = tid * per + q;
-        if (e < Et) run += kept[e];
+        const int e = lane * per + q;
+        if (e < Et) loc += off[e];
     }
-    part[tid] = run;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int32_t v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    int32_t incl = loc;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
     }
-    int32_t b2 = part[tid] - run;
+    int32_t b = incl - loc;
     for (int q = 0; q < per; ++q) {
-        const int e = tid * per + q;
+        const int e = lane * per + q;
         if (e < Et) {
-            offsets[e] = b2;
-            b2 += kept[e];
+            const int32_t k = off[e];
+            off[e] = b;
+            if (store) offsets[e] = b;
+            b += k;
         }
     }
-    if (tid == 1023) {
-        offsets[Et] = part[1023];
-        if (n_kept) *n_kept = part[1023];
+    if (store && lane == 63) {
+        offsets[Et] = incl;
+        if (n_kept) *n_kept = incl;
     }
 }
 
-__global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nbits,
-                                                  int capacity, const int32_t* base,
-                                                  const int32_t* offsets, int32_t* dest_row,
-                                                  int32_t* src_token) {
-    __shared__ int32_t run[MAX_ET];
-    __shared__ int32_t off[MAX_ET];
-    const int lane = threadIdx.x;
-    for (int e = lane; e < Et; e += 64) {
-        run[e] = base[(size_t)blockIdx.x * Et + e];
-        off[e] = offsets[e];
-    }
-    __syncthreads();
+// Step 3 for one chunk whose ids v were preloaded: run[e] enters as the
+// chunk's base for expert e (its earlier queue positions) and is advanced in
+// place; off[e] is the expert's first row.
+__device__ __forceinline__ void rank_chunk(const int32_t* v, int a0, int A, int K, bool choice, int Et, int nbits,
+                                           int capacity, int32_t* run, const int32_t* off, int32_t* dest_row,
+                                           int32_t* src_token) {
+    const int lane = threadIdx.x & 63;
     const uint64_t lt = lanemask_lt();
-    const int a0 = blockIdx.x * CHUNK;
     const int S = A / K;
+#pragma unroll
     for (int step = 0; step < CHUNK / 64; ++step) {
         const int i = a0 + step * 64 + lane;
         if (a0 + step * 64 >= A) break;  // uniform
         const int a = i < A ? queue_at(i, S, K, choice) : A;
-        const int ev = i < A ? idx[a] : -1;
+        const int ev = v[step];
         const bool valid = (unsigned)ev < (unsigned)Et;
         const int e = valid ? ev : 0;
         // lanes with the same (valid, e)
         uint64_t peers = __ballot(valid);
         if (!valid) peers = ~peers;
         for (int bit = 0; bit < nbits; ++bit) {
-            const bool v = (e >> bit) & 1;
-            const uint64_t m = __ballot(v);
-            peers &= v ? m : ~m;
+            const bool b = (e >> bit) & 1;
+            const uint64_t m = __ballot(b);
+            peers &= b ? m : ~m;
         }
         int32_t pos = 0;
         if (valid) pos = run[e] + __popcll(peers & lt);
@@ -189,6 +207,71 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int
             }
         }
     }
+}
+
+// The offsets come from kept (the same prefix in every block; block 0 stores
+// it).  base may be null (no chunks): every base is then 0.
+__global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nbits,
+                                                  int capacity, const int32_t* base, const int32_t* kept,
+                                                  int32_t* offsets, int32_t* n_kept, int32_t* dest_row,
+                                                  int32_t* src_token) {
+    __shared__ int32_t run[MAX_ET];
+    __shared__ int32_t off[MAX_ET];
+    const int a0 = blockIdx.x * CHUNK;
+    int32_t v[CHUNK / 64];
+    load_chunk(idx, a0, A, K, choice, v);
+    for (int e = threadIdx.x; e < Et; e += 64) {
+        run[e] = base ? base[(size_t)blockIdx.x * Et + e] : 0;
+        off[e] = kept[e];
+    }
+    __syncthreads();
+    offsets_from_kept(off, Et, blockIdx.x == 0, offsets, n_kept);
+    __syncthreads();
+    rank_chunk(v, a0, A, K, choice, Et, nbits, capacity, run, off, dest_row, src_token);
+}
+
+// Steps 2 and 3 in one launch when the histogram is small (nch * Et <= kFusedHist,
+// Et <= kFusedEt): every chunk's block reads the whole histogram, forms its own
+// bases (the counts of the earlier chunks, in chunk order), the totals, kept
+// = min(total, C) and the offsets (a wave prefix over the experts, each lane
+// owning a run of Et/64 of them), then ranks its ids.  Block 0 also stores the
+// tables.  Integer sums, so every block derives the same tables as the scan
+// kernel would.
+constexpr int kFusedHist = 8192, kFusedEt = 1024;
+__global__ __launch_bounds__(64) void rank_fused_kernel(const int32_t* idx, int A, int K, bool choice, int Et,
+                                                        int nbits, int capacity, int nch, const int32_t* hist,
+                                                        int32_t* counts, int32_t* kept, int32_t* offsets,
+                                                        int32_t* n_kept, int32_t* dest_row, int32_t* src_token) {
+    __shared__ int32_t run[kFusedEt];
+    __shared__ int32_t off[kFusedEt];
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x, a0 = c * CHUNK;
+    int32_t v[CHUNK / 64];
+    load_chunk(idx, a0, A, K, choice, v);
+    // per expert: base over chunks < c, total over all chunks (16 loads in flight)
+    for (int e = lane; e < Et; e += 64) {
+        int32_t base = 0, tot = 0;
+        for (int q0 = 0; q0 < nch; q0 += 16) {
+            int32_t h[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) h[j] = q0 + j < nch ? hist[(size_t)(q0 + j) * Et + e] : 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                base += q0 + j < c ? h[j] : 0;
+                tot += h[j];
+            }
+        }
+        run[e] = base;
+        off[e] = tot > capacity ? capacity : tot;  // kept, turned into offsets below
+        if (c == 0) {
+            counts[e] = tot;
+            kept[e] = off[e];
+        }
+    }
+    __syncthreads();
+    offsets_from_kept(off, Et, c == 0, offsets, n_kept);
+    __syncthreads();
+    rank_chunk(v, a0, A, K, choice, Et, nbits, capacity, run, off, dest_row, src_token);
 }
 
 // Steps 1-3 in one block of 1024 threads (16 waves) when the assignment list
@@ -340,12 +423,25 @@ static hipError_t launch_tables_chunked(const PermuteArgs& p, int nch, int nbits
                            p.Et, nch, p.hist);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, p.hist, nch, p.Et, p.capacity, p.counts,
-                       p.kept, p.offsets, p.n_kept);
+    if (nch > 0 && (size_t)nch * p.Et <= (size_t)kFusedHist && p.Et <= kFusedEt) {
+        hipLaunchKernelGGL(rank_fused_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K,
+                           p.queue == MOE_QUEUE_CHOICE, p.Et, nbits, p.capacity, nch, p.hist, p.counts, p.kept,
+                           p.offsets, p.n_kept, p.dest_row, p.src_token);
+        return hipGetLastError();
+    }
+    // 16 experts per scan block (measured on one MI355X, 256 chunks x 256
+    // experts: one block for all experts 20 us)
+    const int epb = std::max(16, (p.Et + 63) / 64);
+    hipLaunchKernelGGL(scan_kernel, dim3((p.Et + epb - 1) / epb), dim3(1024), 0, st, p.hist, nch, p.Et, epb,
+                       p.capacity, p.counts, p.kept);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (nch == 0) return hipSuccess;
+    if (nch == 0) {  // no assignments: one block stores the (zero) offsets
+        hipLaunchKernelGGL(rank_kernel, dim3(1), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE,
+                           p.Et, nbits, p.capacity, nullptr, p.kept, p.offsets, p.n_kept, p.dest_row, p.src_token);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE, p.Et, nbits,
-                       p.capacity, p.hist, p.offsets, p.dest_row, p.src_token);
+                       p.capacity, p.hist, p.kept, p.offsets, p.n_kept, p.dest_row, p.src_token);
     return hipGetLastError();
 }
 

@@ -91,17 +91,66 @@ __device__ __forceinline__ bool better(float ka, int ea, float kb, int eb) {
     return ka > kb || (ka == kb && ea < eb);
 }
 
+// Partner value of one step of a butterfly all-reduce over groups of lanes,
+// steps taken in the order OFF = 1, 2, 4, ..., with DPP and lane-swap
+// instructions instead of an LDS permute.  OFF = 1, 2: quad permutes (lane ^
+// OFF); 4: the mirror lane within each group of 8 (lane ^ 7), which holds the
+// value of lane ^ 4 because each quad is uniform after the first two steps;
+// 8: a rotation of each 16-lane row by 8 (lane ^ 8); 16, 32: the row and
+// half-wave swaps (lane ^ 16, lane ^ 32).  Both partners of a step combine
+// the same two values, so every lane of a group ends with the same bits, the
+// ones the plain xor butterfly gives.
+template <int V>
+struct Off {
+    static constexpr int value = V;
+};
+template <int LPT, typename F>
+__device__ __forceinline__ void bfly_steps(F&& f) {
+    if constexpr (LPT > 1) f(Off<1>{});
+    if constexpr (LPT > 2) f(Off<2>{});
+    if constexpr (LPT > 4) f(Off<4>{});
+    if constexpr (LPT > 8) f(Off<8>{});
+    if constexpr (LPT > 16) f(Off<16>{});
+    if constexpr (LPT > 32) f(Off<32>{});
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t bfly_u32(uint32_t v) {
+    if constexpr (OFF == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    if constexpr (OFF == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    if constexpr (OFF == 4) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false); // row_half_mirror
+    if constexpr (OFF == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); // row_ror:8
+    if constexpr (OFF == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & 16) ? p[0] : p[1];
+    }
+    if constexpr (OFF == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? p[0] : p[1];
+    }
+}
+template <int OFF>
+__device__ __forceinline__ float bfly(float v) { return __uint_as_float(bfly_u32<OFF>(__float_as_uint(v))); }
+template <int OFF>
+__device__ __forceinline__ int bfly(int v) { return (int)bfly_u32<OFF>((uint32_t)v); }
+
 __device__ __forceinline__ float wave_sum(float v) {
-    // xor butterfly: partners add the same two values, so every lane ends with
-    // the same, order-fixed sum
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    // partners add the same two values, so every lane ends with the same,
+    // order-fixed sum
+    bfly_steps<64>([&](auto O) __attribute__((always_inline)) { v += bfly<decltype(O)::value>(v); });
     return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    bfly_steps<64>([&](auto O) __attribute__((always_inline)) { v = fmaxf(v, bfly<decltype(O)::value>(v)); });
     return v;
+}
+// arg-max of (key, index) over the wave
+__device__ __forceinline__ void wave_best(float& bk, int& be) {
+    bfly_steps<64>([&](auto O) __attribute__((always_inline)) {
+        constexpr int off = decltype(O)::value;
+        const float ok = bfly<off>(bk);
+        const int oe = bfly<off>(be);
+        if (better(ok, oe, bk, be)) { bk = ok; be = oe; }
+    });
 }
 
 // NB = 16-expert column blocks of the logit tile (E <= 16*NB); EJ = E/64 slots
@@ -269,12 +318,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
                     const int e = lane + 64 * j;
                     if (!used[j] && !gk[j] && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
                 }
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) {
-                    const float ok = __shfl_xor(bk, off);
-                    const int oe = __shfl_xor(be, off);
-                    if (better(ok, oe, bk, be)) { bk = ok; be = oe; }
-                }
+                wave_best(bk, be);
                 const int gb = be / gsz;
 #pragma unroll
                 for (int j = 0; j < EJ; ++j) gk[j] = gk[j] || (lane + 64 * j) / gsz == gb;
@@ -293,12 +337,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
                 const int e = lane + 64 * j;
                 if (!used[j] && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ok = __shfl_xor(bk, off);
-                const int oe = __shfl_xor(be, off);
-                if (better(ok, oe, bk, be)) { bk = ok; be = oe; }
-            }
+            wave_best(bk, be);
             // the owner of `be` marks it used and broadcasts the value the weight needs
             float v = 0.0f;
 #pragma unroll
@@ -308,7 +347,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
                     v = a.score == MOE_SIGMOID ? sg[j] : lp[j];
                 }
             }
-            v = __shfl(v, be & 63);
+            v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), __builtin_amdgcn_readfirstlane(be) & 63));
             if ((k & 63) == lane) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -317,7 +356,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         }
         // gate weights: softmax over the kept biased logits (the first kept is the
         // largest), or kept sigmoids over their sum
-        const float vmax = __shfl(my_v[0], 0);
+        const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v[0]), 0));
         float u[4], loc = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -378,6 +417,144 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
         }
     }
     (void)Et;
+}
+
+// Selection for the RS tokens t0, t0+1, ... of head g (the bf16 kernels for at
+// most 64 experts per head): LPT lanes per token (threads tid < RS*LPT; the
+// others idle), each lane holding experts lq, lq + LPT, ... of the token's row
+// of logits lg [RS][NB*16+1] (LDS); every arg-max round is a lane-local scan
+// then a butterfly over the token's lanes on the (key desc, index asc) order.
+// Writes topk_idx/topk_w, counts the kept experts in hist (LDS) and, when
+// a.prob_part is set, the token's full score distribution to pr (LDS, same
+// layout).
+template <int NB, int RS, int LPT, bool SIG>
+__device__ __forceinline__ void select_tile(const RouteArgs& a, int g, int t0, int tid, const float* lg, float* pr,
+                                            int* hist) {
+    constexpr int EP = NB * 16;
+    constexpr int LDE = EP + 1;
+    constexpr int EPL = EP / LPT;
+    static_assert(EPL >= 1 && LPT <= 64, "a token's lanes lie in one wave and hold one expert or more each");
+    const int T = a.T, H = a.H, E = a.E, K = a.K;
+    const float NEG = -__builtin_inff();
+    const int r = tid / LPT, lq = tid % LPT;
+    const int t = t0 + r;
+    // arg-max of (key, expert, value) over the token's lanes
+    auto group_best = [&](float& bk, int& be, float& bv) __attribute__((always_inline)) {
+        bfly_steps<LPT>([&](auto O) __attribute__((always_inline)) {
+            constexpr int off = decltype(O)::value;
+            const float ok = bfly<off>(bk);
+            const int oe = bfly<off>(be);
+            const float ov = bfly<off>(bv);
+            if (better(ok, oe, bk, be)) { bk = ok; be = oe; bv = ov; }
+        });
+    };
+    auto group_sum = [&](float v) __attribute__((always_inline)) {
+        bfly_steps<LPT>([&](auto O) __attribute__((always_inline)) { v += bfly<decltype(O)::value>(v); });
+        return v;
+    };
+    auto group_max = [&](float v) __attribute__((always_inline)) {
+        bfly_steps<LPT>([&](auto O) __attribute__((always_inline)) { v = fmaxf(v, bfly<decltype(O)::value>(v)); });
+        return v;
+    };
+    if (r < RS && t < T) {  // uniform over a token's lanes
+        const size_t sidx = (size_t)t * H + g;
+        // softmax router: key = biased logit; sigmoid router: key = sigma + bias,
+        // weights from sigma
+        float key[EPL], sg[SIG ? EPL : 1];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lq + LPT * j;
+            const bool valid = e < E;
+            float l = valid ? lg[r * LDE + e] : NEG;
+            if (valid && a.logit_bias) l = l + a.logit_bias[g * E + e];
+            if constexpr (SIG) {
+                sg[j] = valid ? key_sigmoid(l) : 0.0f;
+                key[j] = valid ? (a.select_bias ? sg[j] + a.select_bias[g * E + e] : sg[j]) : NEG;
+            } else {
+                key[j] = l;
+            }
+        }
+        // group limit: experts outside the group_limit best groups are excluded
+        // (the best remaining key lies in the best remaining group)
+        uint32_t excl = 0;  // bit j: expert lq + LPT*j excluded
+        if (a.n_groups > 1) {
+            const int gsz = E / a.n_groups;
+            uint32_t kept = 0;
+            for (int m = 0; m < a.group_limit; ++m) {
+                float bk = NEG, bv = 0.0f;
+                int be = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j) {
+                    const int e = lq + LPT * j;
+                    if (e < E && !((kept >> j) & 1u) && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
+                }
+                group_best(bk, be, bv);
+                const int gb = be / gsz;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j)
+                    if ((lq + LPT * j) / gsz == gb) kept |= 1u << j;
+            }
+            excl = ~kept;
+        }
+        // two passes of K arg-max rounds: the first sums the kept scores, the
+        // second writes the normalised weights (lane k % LPT writes slot k)
+        float den = 0.0f, vmax = 0.0f;
+        for (int pass = 0; pass < 2; ++pass) {
+            uint32_t used = excl;
+            for (int k = 0; k < K; ++k) {
+                float bk = NEG, bv = 0.0f;
+                int be = 0x7fffffff;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j) {
+                    const int e = lq + LPT * j;
+                    if (e < E && !((used >> j) & 1u) && better(key[j], e, bk, be)) {
+                        bk = key[j];
+                        be = e;
+                        if constexpr (SIG) bv = sg[j];
+                        else bv = key[j];
+                    }
+                }
+                group_best(bk, be, bv);
+                if (be % LPT == lq) used |= 1u << (be / LPT);
+                if (k == 0) vmax = bv;  // the first kept has the largest biased logit
+                const float u = SIG ? bv : expf(bv - vmax);
+                if (pass == 0) {
+                    den += u;
+                } else if (k % LPT == lq) {
+                    a.topk_idx[sidx * K + k] = g * E + be;
+                    a.topk_w[sidx * K + k] = u / den;
+                    atomicAdd(&hist[be], 1);
+                }
+            }
+        }
+        // full score distribution of this token, for P
+        if (a.prob_part) {
+            if constexpr (SIG) {
+                float tot = 0.0f;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j) tot += sg[j];
+                tot = group_sum(tot);
+#pragma unroll
+                for (int j = 0; j < EPL; ++j)
+                    if (lq + LPT * j < E) pr[r * LDE + lq + LPT * j] = sg[j] / tot;
+            } else {
+                float m = NEG;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j) m = fmaxf(m, key[j]);
+                m = group_max(m);
+                float ex[EPL], tot = 0.0f;
+#pragma unroll
+                for (int j = 0; j < EPL; ++j) {
+                    ex[j] = lq + LPT * j < E ? expf(key[j] - m) : 0.0f;
+                    tot += ex[j];
+                }
+                tot = group_sum(tot);
+#pragma unroll
+                for (int j = 0; j < EPL; ++j)
+                    if (lq + LPT * j < E) pr[r * LDE + lq + LPT * j] = ex[j] / tot;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -477,133 +654,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
         }
     }
 
-    // ------------------- selection: LPT = 256 / RS lanes per token, each lane
-    // holding experts lq, lq + LPT, ...; every arg-max round is a lane-local scan
-    // then a butterfly over the token's lanes on the (key desc, index asc) order
-    constexpr int LPT = RT_THREADS / RS;
-    constexpr int EPL = EP / LPT;
-    const float NEG = -__builtin_inff();
-    const int r = threadIdx.x / LPT, lq = threadIdx.x % LPT;
-    const int t = t0 + r;
-    // arg-max of (key, expert, value) over the token's lanes
-    auto group_best = [&](float& bk, int& be, float& bv) __attribute__((always_inline)) {
-#pragma unroll
-        for (int off = 1; off < LPT; off <<= 1) {
-            const float ok = __shfl_xor(bk, off);
-            const int oe = __shfl_xor(be, off);
-            const float ov = __shfl_xor(bv, off);
-            if (better(ok, oe, bk, be)) { bk = ok; be = oe; bv = ov; }
-        }
-    };
-    auto group_sum = [&](float v) __attribute__((always_inline)) {
-#pragma unroll
-        for (int off = 1; off < LPT; off <<= 1) v += __shfl_xor(v, off);
-        return v;
-    };
-    auto group_max = [&](float v) __attribute__((always_inline)) {
-#pragma unroll
-        for (int off = 1; off < LPT; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
-        return v;
-    };
-    if (t < T) {  // uniform over a token's lanes
-        const size_t sidx = (size_t)t * H + g;
-        // softmax router: key = biased logit; sigmoid router: key = sigma + bias,
-        // weights from sigma
-        float key[EPL], sg[SIG ? EPL : 1];
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lq + LPT * j;
-            const bool valid = e < E;
-            float l = valid ? part[0][r][e] : NEG;
-            if (valid && a.logit_bias) l = l + a.logit_bias[g * E + e];
-            if constexpr (SIG) {
-                sg[j] = valid ? key_sigmoid(l) : 0.0f;
-                key[j] = valid ? (a.select_bias ? sg[j] + a.select_bias[g * E + e] : sg[j]) : NEG;
-            } else {
-                key[j] = l;
-            }
-        }
-        // group limit: experts outside the group_limit best groups are excluded
-        // (the best remaining key lies in the best remaining group)
-        uint32_t excl = 0;  // bit j: expert lq + LPT*j excluded
-        if (a.n_groups > 1) {
-            const int gsz = E / a.n_groups;
-            uint32_t kept = 0;
-            for (int m = 0; m < a.group_limit; ++m) {
-                float bk = NEG, bv = 0.0f;
-                int be = 0x7fffffff;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) {
-                    const int e = lq + LPT * j;
-                    if (e < E && !((kept >> j) & 1u) && better(key[j], e, bk, be)) { bk = key[j]; be = e; }
-                }
-                group_best(bk, be, bv);
-                const int gb = be / gsz;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j)
-                    if ((lq + LPT * j) / gsz == gb) kept |= 1u << j;
-            }
-            excl = ~kept;
-        }
-        // two passes of K arg-max rounds: the first sums the kept scores, the
-        // second writes the normalised weights (lane k % LPT writes slot k)
-        float den = 0.0f, vmax = 0.0f;
-        for (int pass = 0; pass < 2; ++pass) {
-            uint32_t used = excl;
-            for (int k = 0; k < K; ++k) {
-                float bk = NEG, bv = 0.0f;
-                int be = 0x7fffffff;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) {
-                    const int e = lq + LPT * j;
-                    if (e < E && !((used >> j) & 1u) && better(key[j], e, bk, be)) {
-                        bk = key[j];
-                        be = e;
-                        if constexpr (SIG) bv = sg[j];
-                        else bv = key[j];
-                    }
-                }
-                group_best(bk, be, bv);
-                if (be % LPT == lq) used |= 1u << (be / LPT);
-                if (k == 0) vmax = bv;  // the first kept has the largest biased logit
-                const float u = SIG ? bv : expf(bv - vmax);
-                if (pass == 0) {
-                    den += u;
-                } else if (k % LPT == lq) {
-                    a.topk_idx[sidx * K + k] = g * E + be;
-                    a.topk_w[sidx * K + k] = u / den;
-                    atomicAdd(&hist[be], 1);
-                }
-            }
-        }
-        // full score distribution of this token, for P
-        if (a.prob_part) {
-            if constexpr (SIG) {
-                float tot = 0.0f;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) tot += sg[j];
-                tot = group_sum(tot);
-#pragma unroll
-                for (int j = 0; j < EPL; ++j)
-                    if (lq + LPT * j < E) part[1][r][lq + LPT * j] = sg[j] / tot;
-            } else {
-                float m = NEG;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) m = fmaxf(m, key[j]);
-                m = group_max(m);
-                float ex[EPL], tot = 0.0f;
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) {
-                    ex[j] = lq + LPT * j < E ? expf(key[j] - m) : 0.0f;
-                    tot += ex[j];
-                }
-                tot = group_sum(tot);
-#pragma unroll
-                for (int j = 0; j < EPL; ++j)
-                    if (lq + LPT * j < E) part[1][r][lq + LPT * j] = ex[j] / tot;
-            }
-        }
-    }
+    select_tile<NB, RS, RT_THREADS / RS, SIG>(a, g, t0, threadIdx.x, &part[0][0][0], &part[1][0][0], hist);
     __syncthreads();
     const int rows = min(RS, T - t0);
     for (int e = threadIdx.x; e < E; e += RT_THREADS) {

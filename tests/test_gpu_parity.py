@@ -83,6 +83,9 @@ ROUTE_VARIANTS = {
     "softmax_e20_k3": ("top2_e8_h4096", dict(E=20, K=3, T=1001)),
     "heads2_e24_k5": ("multihead_h8_e32_top4", dict(H=2, E=24, K=5, T=777)),
     "zipf_e40_k2": ("switch_top1_e64_zipf", dict(E=40, K=2, T=1234)),
+    # sigmoid scoring on the kernel for at most 64 experts, longer head slices
+    "sigmoid_e16_k4_d2048": ("sigmoid_top8_e256_shared", dict(E=16, K=4, T=1500, h=2048)),
+    "sigmoid_e64_k8_d1024": ("sigmoid_top8_e256_shared", dict(E=64, K=8, T=2100, h=1024)),
 }
 ROUTE_CASES = WORKLOADS + sorted(ROUTE_VARIANTS)
 
@@ -129,6 +132,42 @@ def test_route_logits_gemm(name):
     assert np.abs(g["topk_w"][ok] - r["topk_w"][ok]).max() <= 1e-4
 
 
+# Router GEMMs on larger batches with ragged last token blocks, several heads,
+# sigmoid scoring, and a batch smaller than one block
+WALK_CASES = {
+    "top2_T8500": ("top2_e8_h4096", dict(T=8500)),
+    "switch_T4200": ("switch_top1_e64_zipf", dict(T=4200)),
+    "heads2_e24_T5000": ("multihead_h8_e32_top4", dict(H=2, E=24, K=5, T=5000)),
+    "sigmoid_e32_T3000_d1024": ("sigmoid_top8_e256_shared", dict(E=32, K=4, T=3000, h=1024)),
+    "switch_T5": ("switch_top1_e64_zipf", dict(T=5)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(WALK_CASES))
+def test_route_logits_gemm_larger_batches(case):
+    base, over = WALK_CASES[case]
+    cfg = inputs.variant(base, **over)
+    G.log(f"[route batches] {case} T={cfg['T']} h={cfg['h']} H={cfg.get('H', 1)} E={cfg['E']}")
+    inp = inputs.make_inputs(dict(cfg, f=8), "cpu")
+    dv = {k: (None if v is None else v.to(G.DEV)) for k, v in inp.items()}
+    g = route_gpu(cfg, x=dv["x"], w_router=dv["w_router"], biases=dv, want_logits=True)
+    ref_lg = orc.logits(cfg, to_np(inp["x"]), to_np(inp["w_router"]))
+    assert np.abs(g["logits"] - ref_lg).max() <= 5e-5
+    r = orc.select(cfg, ref_lg, to_np(inp["logit_bias"]), to_np(inp["select_bias"]))
+    ok = r["margin"] >= G.MARGIN
+    assert ok.mean() > 0.5
+    assert np.array_equal(g["topk_idx"][ok], r["topk_idx"][ok])
+    assert np.abs(g["topk_w"][ok] - r["topk_w"][ok]).max() <= 1e-4
+    # on the GPU's own logits the selection is exact everywhere, P agrees with
+    # the oracle's distributions and the counts with the indices
+    r_g = orc.select(cfg, g["logits"], to_np(inp["logit_bias"]), to_np(inp["select_bias"]))
+    assert np.array_equal(g["topk_idx"], r_g["topk_idx"])
+    assert np.abs(g["topk_w"] - r_g["topk_w"]).max() <= 2e-6
+    assert np.allclose(g["P"], r_g["psum"] / cfg["T"], rtol=1e-4, atol=1e-7)
+    Et = cfg.get("H", 1) * cfg["E"]
+    assert np.array_equal(g["counts"], np.bincount(g["topk_idx"].ravel(), minlength=Et))
+
+
 # ------------------------------------------------------------------ permutation
 @pytest.mark.parametrize("name,skew,cap", [
     ("tiny_f32", 0.0, "cfg"), ("top2_e8_h4096", 0.0, "cfg"), ("top2_e8_h4096", 1.5, "cfg"),
@@ -165,6 +204,57 @@ def test_permute_bit_exact(name, skew, cap):
                        xs[srcs].view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32))
     if C == 0:
         assert n == 0 and (dest.cpu().numpy() == -1).all()
+
+
+# Routing tables on assignment lists with a ragged last chunk (1024 queue
+# positions per chunk), on both table paths: the fused rank kernel (chunks x
+# experts <= 8192) and histogram -> scan -> rank (larger histograms); with a
+# capacity, and with out-of-range expert ids (which are dropped)
+RAGGED_PERMUTE = {
+    "top2_A6002_cap": ("top2_e8_h4096", dict(T=3001, h=64), 0.5, "cfg"),
+    "sigmoid_A8200": ("sigmoid_top8_e256_shared", dict(T=1025, h=64), 0.3, "cfg"),
+    "multihead_A9600_cap": ("multihead_h8_e32_top4", dict(T=300, h=64, capacity_factor=1.0), 0.8, "cfg"),
+    "sigmoid_A40000_cap": ("sigmoid_top8_e256_shared", dict(T=5000, h=64, capacity_factor=1.1), 0.6, "cfg"),
+    "switch_A5000_badids": ("switch_top1_e64_zipf", dict(T=5000, h=64), 1.0, "cfg"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RAGGED_PERMUTE))
+def test_permute_tables_ragged_chunks(case):
+    base, over, skew, cap = RAGGED_PERMUTE[case]
+    cfg = inputs.variant(base, **over)
+    T, H, K, E = cfg["T"], cfg.get("H", 1), cfg["K"], cfg["E"]
+    A, Et = T * H * K, H * E
+    G.log(f"[permute ragged] {case} A={A} Et={Et} chunks={(A + 1023) // 1024}")
+    idx = inputs.make_routing(cfg, "cpu", skew=skew)
+    if case.endswith("badids"):
+        idx.view(-1)[::97] = Et + 3
+        idx.view(-1)[5::101] = -2
+    C = orc.capacity(cfg) if cap == "cfg" else cap
+    Cg = moe.INT32_MAX if C is None else C
+    d = moe.desc_from_cfg(cfg)
+    counts, kept, offsets, dest, src, nk = i32(Et), i32(Et), i32(Et + 1), i32(A), i32(A), i32(1)
+    ws = moe.workspace(d, moe.MOE_WS_PERMUTE)
+    moe.moe_permute(d, idx.to(G.DEV), None, Cg, counts, kept, offsets, dest, src, None, nk, ws)
+    torch.cuda.synchronize()
+    if case.endswith("badids"):
+        # the kernels drop ids outside [0, Et): the oracle sees them as one extra
+        # expert after the real ones, whose rows (and count) come last
+        bad = (idx < 0) | (idx >= Et)
+        ids = np.where(bad.numpy(), Et, idx.numpy()).astype(np.int32)
+        r = orc.permute(dict(cfg, E=E + 1), ids, C)
+        r = dict(counts=r["counts"][:Et], kept=r["kept"][:Et], offsets=r["offsets"][:Et + 1],
+                 dest_row=np.where(bad.numpy().ravel(), -1, r["dest_row"]), n_kept=int(r["offsets"][Et]),
+                 src_sub=r["src_sub"][:int(r["offsets"][Et])])
+    else:
+        r = orc.permute(cfg, idx.numpy(), C)
+    n = r["n_kept"]
+    assert int(nk.item()) == n
+    assert np.array_equal(counts.cpu().numpy(), r["counts"])
+    assert np.array_equal(kept.cpu().numpy(), r["kept"])
+    assert np.array_equal(offsets.cpu().numpy(), r["offsets"])
+    assert np.array_equal(dest.cpu().numpy(), r["dest_row"])
+    assert np.array_equal(src.cpu().numpy()[:n], r["src_sub"])
 
 
 # ------------------------------------------------------------------ grouped FFN
