@@ -125,6 +125,10 @@ Plan plan_of(const moe_desc* d) {
     return p;
 }
 
+// route partials of P up to this size are summed by the stats kernel (one
+// block) rather than by their own launch
+constexpr size_t kFoldPartials = 65536;
+
 struct RouteWs { float* prob_part; void* split; };
 RouteWs carve_route(Carver& c, const Plan& p, int dtype) {
     RouteWs w;
@@ -584,6 +588,8 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
     int32_t* dest_row = aux && aux->dest_row && !sv ? aux->dest_row : L.dest_row;
     int32_t* counts = aux && aux->counts && !sv ? aux->counts : L.counts;
     const bool want_stats = aux && (aux->f || aux->P || aux->l_aux || aux->kept || aux->n_kept || aux->n_dropped);
+    // small partial tables: the stats kernel sums P itself (one launch fewer)
+    const bool fold_p = d->gate == MOE_GATE_TOPK && (size_t)p.route_nbx * p.Et <= kFoldPartials;
     hipError_t e;
 
     if (d->gate == MOE_GATE_HASH) {
@@ -602,7 +608,7 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
         ra.prob_part = want_stats ? L.prob_part : nullptr;
         ra.split_ws = L.route_split;
         if ((e = launch_route(ra, st)) != hipSuccess) return dev_fail(e, "route kernel");
-        if (want_stats && (e = launch_prob_mean(L.prob_part, p.route_nbx, p.H, p.E, p.T, L.prob_mean, st)) != hipSuccess)
+        if (want_stats && !fold_p && (e = launch_prob_mean(L.prob_part, p.route_nbx, p.H, p.E, p.T, L.prob_mean, st)) != hipSuccess)
             return dev_fail(e, "prob_mean kernel");
     }
 
@@ -661,7 +667,10 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
     if (want_stats) {
         StatsArgs sa{};
         sa.T = p.T; sa.H = p.H; sa.E = p.E; sa.K = p.K; sa.A = p.A; sa.alpha = d->aux_alpha;
-        sa.counts = counts; sa.kept_in = L.kept; sa.offsets = L.offsets; sa.prob_mean = L.prob_mean;
+        sa.counts = counts; sa.kept_in = L.kept; sa.offsets = L.offsets;
+        sa.prob_mean = fold_p ? nullptr : L.prob_mean;
+        sa.prob_part = fold_p ? L.prob_part : nullptr;
+        sa.nbx = p.route_nbx;
         sa.f = aux->f; sa.P = aux->P; sa.l_aux = aux->l_aux; sa.n_kept = aux->n_kept;
         sa.n_dropped = aux->n_dropped; sa.kept_out = aux->kept;
         if ((e = launch_stats(sa, st)) != hipSuccess) return dev_fail(e, "stats kernel");

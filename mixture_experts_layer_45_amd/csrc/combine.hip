@@ -133,27 +133,43 @@ hipError_t launch_zero_dropped(const int32_t* dest_row, int T, int row_bytes, vo
     return hipGetLastError();
 }
 
-// f_e = counts_e / (T K); P as given; L_aux = mean over heads of alpha E sum_e f_e P_e
-// (fixed-order serial sums; E_tot is small).  One block.
-__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+// f_e = counts_e / (T K); P as given, or summed here from the route kernels'
+// partials (the same order as prob_mean_kernel, so the same bits); L_aux =
+// mean over heads of alpha E sum_e f_e P_e (fixed-order serial sums; E is at
+// most 256).  One block.
+constexpr int kStatsMaxEt = 4096;
+__global__ __launch_bounds__(1024) void stats_kernel(StatsArgs a) {
     const int Et = a.H * a.E;
+    const int tid = threadIdx.x;
+    __shared__ float Pl[kStatsMaxEt];
+    __shared__ float fl[kStatsMaxEt];
     __shared__ float headsum[256];
-    for (int i = threadIdx.x; i < Et; i += 256) {
+    if (a.prob_part) {
+        for (int e0 = 0; e0 < Et; e0 += 1024 / kPLanes) {
+            const int ge = e0 + tid / kPLanes, j = tid % kPLanes;
+            const bool valid = ge < Et;
+            const float v = prob_mean_of(a.prob_part, a.nbx, a.E, a.T, ge, valid, j);
+            if (valid && j == 0) Pl[ge] = v;
+        }
+    } else {
+        for (int i = tid; i < Et; i += 1024) Pl[i] = a.prob_mean[i];
+    }
+    for (int i = tid; i < Et; i += 1024) {
         const float fe = (float)a.counts[i] / ((float)a.T * (float)a.K);
+        fl[i] = fe;
         if (a.f) a.f[i] = fe;
-        if (a.P) a.P[i] = a.prob_mean[i];
         if (a.kept_out) a.kept_out[i] = a.kept_in[i];
     }
-    for (int g = threadIdx.x; g < a.H; g += 256) {
+    __syncthreads();
+    for (int i = tid; i < Et; i += 1024)
+        if (a.P) a.P[i] = Pl[i];
+    for (int g = tid; g < a.H; g += 1024) {
         float s = 0.0f;
-        for (int e = 0; e < a.E; ++e) {
-            const float fe = (float)a.counts[g * a.E + e] / ((float)a.T * (float)a.K);
-            s += fe * a.prob_mean[g * a.E + e];
-        }
+        for (int e = 0; e < a.E; ++e) s += fl[g * a.E + e] * Pl[g * a.E + e];
         headsum[g] = a.alpha * (float)a.E * s;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         if (a.l_aux) {
             float s = 0.0f;
             for (int g = 0; g < a.H; ++g) s += headsum[g];
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
 }
 
 hipError_t launch_stats(const StatsArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, st, a);
     return hipGetLastError();
 }
 

@@ -36,6 +36,67 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
+// Partner value of one step of a butterfly all-reduce over groups of lanes,
+// steps taken in the order OFF = 1, 2, 4, ..., with DPP and lane-swap
+// instructions instead of an LDS permute.  OFF = 1, 2: quad permutes (lane ^
+// OFF); 4: the mirror lane within each group of 8 (lane ^ 7), which holds the
+// value of lane ^ 4 because each quad is uniform after the first two steps;
+// 8: a rotation of each 16-lane row by 8 (lane ^ 8); 16, 32: the row and
+// half-wave swaps (lane ^ 16, lane ^ 32).  Both partners of a step combine
+// the same two values, so every lane of a group ends with the same bits, the
+// ones the plain xor butterfly gives.
+template <int V>
+struct Off {
+    static constexpr int value = V;
+};
+template <int LPT, typename F>
+__device__ __forceinline__ void bfly_steps(F&& f) {
+    if constexpr (LPT > 1) f(Off<1>{});
+    if constexpr (LPT > 2) f(Off<2>{});
+    if constexpr (LPT > 4) f(Off<4>{});
+    if constexpr (LPT > 8) f(Off<8>{});
+    if constexpr (LPT > 16) f(Off<16>{});
+    if constexpr (LPT > 32) f(Off<32>{});
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t bfly_u32(uint32_t v) {
+    if constexpr (OFF == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    if constexpr (OFF == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    if constexpr (OFF == 4) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false); // row_half_mirror
+    if constexpr (OFF == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); // row_ror:8
+    if constexpr (OFF == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & 16) ? p[0] : p[1];
+    }
+    if constexpr (OFF == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? p[0] : p[1];
+    }
+}
+template <int OFF>
+__device__ __forceinline__ float bfly(float v) { return __uint_as_float(bfly_u32<OFF>(__float_as_uint(v))); }
+template <int OFF>
+__device__ __forceinline__ int bfly(int v) { return (int)bfly_u32<OFF>((uint32_t)v); }
+
+// P from the route kernels' partials part[(g*nbx + b)*E + e] (block b's sum of
+// head g's score distributions over its tokens): P_e = (sum over b) / T in one
+// fixed order, 16 consecutive lanes per expert ge = g*E + e, lane j adding
+// b = j, j+16, ... in turn, then the butterfly over the 16 lanes.  All 16
+// lanes of the group must call it (valid false: no loads, any value); each
+// returns the same bits.
+constexpr int kPLanes = 16;
+__device__ __forceinline__ float prob_mean_of(const float* part, int nbx, int E, int T, int ge, bool valid, int j) {
+    float s = 0.0f;
+    if (valid) {
+        const int g = ge / E, e = ge - g * E;
+        const float* p = part + (size_t)g * nbx * E + e;
+#pragma unroll 8
+        for (int b = j; b < nbx; b += kPLanes) s += p[(size_t)b * E];
+    }
+    bfly_steps<kPLanes>([&](auto O) __attribute__((always_inline)) { s += bfly<decltype(O)::value>(s); });
+    return T > 0 ? s / (float)T : 0.0f;
+}
+
 // ------------------------------------------------------- internal launchers
 // Every launcher enqueues on `st` and returns hipGetLastError() of the launch.
 struct RouteArgs {
@@ -166,7 +227,9 @@ struct StatsArgs {
     const int32_t* counts;
     const int32_t* kept_in;
     const int32_t* offsets;
-    const float* prob_mean;
+    const float* prob_mean;   // P as computed, or null with prob_part
+    const float* prob_part;   // the route kernels' partials (prob_mean_of), nbx blocks per head
+    int nbx;
     float* f;
     float* P;
     float* l_aux;

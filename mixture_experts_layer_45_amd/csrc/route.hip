@@ -91,48 +91,6 @@ __device__ __forceinline__ bool better(float ka, int ea, float kb, int eb) {
     return ka > kb || (ka == kb && ea < eb);
 }
 
-// Partner value of one step of a butterfly all-reduce over groups of lanes,
-// steps taken in the order OFF = 1, 2, 4, ..., with DPP and lane-swap
-// instructions instead of an LDS permute.  OFF = 1, 2: quad permutes (lane ^
-// OFF); 4: the mirror lane within each group of 8 (lane ^ 7), which holds the
-// value of lane ^ 4 because each quad is uniform after the first two steps;
-// 8: a rotation of each 16-lane row by 8 (lane ^ 8); 16, 32: the row and
-// half-wave swaps (lane ^ 16, lane ^ 32).  Both partners of a step combine
-// the same two values, so every lane of a group ends with the same bits, the
-// ones the plain xor butterfly gives.
-template <int V>
-struct Off {
-    static constexpr int value = V;
-};
-template <int LPT, typename F>
-__device__ __forceinline__ void bfly_steps(F&& f) {
-    if constexpr (LPT > 1) f(Off<1>{});
-    if constexpr (LPT > 2) f(Off<2>{});
-    if constexpr (LPT > 4) f(Off<4>{});
-    if constexpr (LPT > 8) f(Off<8>{});
-    if constexpr (LPT > 16) f(Off<16>{});
-    if constexpr (LPT > 32) f(Off<32>{});
-}
-template <int OFF>
-__device__ __forceinline__ uint32_t bfly_u32(uint32_t v) {
-    if constexpr (OFF == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-    if constexpr (OFF == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-    if constexpr (OFF == 4) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false); // row_half_mirror
-    if constexpr (OFF == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); // row_ror:8
-    if constexpr (OFF == 16) {
-        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-        return (threadIdx.x & 16) ? p[0] : p[1];
-    }
-    if constexpr (OFF == 32) {
-        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-        return (threadIdx.x & 32) ? p[0] : p[1];
-    }
-}
-template <int OFF>
-__device__ __forceinline__ float bfly(float v) { return __uint_as_float(bfly_u32<OFF>(__float_as_uint(v))); }
-template <int OFF>
-__device__ __forceinline__ int bfly(int v) { return (int)bfly_u32<OFF>((uint32_t)v); }
-
 __device__ __forceinline__ float wave_sum(float v) {
     // partners add the same two values, so every lane ends with the same,
     // order-fixed sum
@@ -667,22 +625,12 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
     }
 }
 
-// P_e = (sum over the head's block partials) / T.  One block per expert: thread
-// i sums partials i, i+256, ... in order, then a fixed LDS tree; the order
-// depends only on the sizes, so P is reproducible.
+// P_e for 16 experts per block of 256 threads (prob_mean_of's lane layout)
 __global__ __launch_bounds__(256) void prob_mean_kernel(const float* part, int nbx, int H, int E, int T, float* out) {
-    __shared__ float red[256];
-    const int i = blockIdx.x;  // global expert g*E + e
-    const int g = i / E, e = i - g * E;
-    float s = 0.0f;
-    for (int b = threadIdx.x; b < nbx; b += 256) s += part[((size_t)g * nbx + b) * E + e];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) out[i] = T > 0 ? red[0] / (float)T : 0.0f;
+    const int ge = blockIdx.x * 16 + (int)(threadIdx.x / kPLanes), j = threadIdx.x % kPLanes;
+    const bool valid = ge < H * E;
+    const float v = prob_mean_of(part, nbx, E, T, ge, valid, j);
+    if (valid && j == 0) out[ge] = v;
 }
 
 __device__ __forceinline__ uint32_t fmix32(uint32_t h) {
@@ -831,7 +779,7 @@ hipError_t launch_route(const RouteArgs& a0, hipStream_t st) {
 
 hipError_t launch_prob_mean(const float* part, int nbx, int H, int E, int T, float* out, hipStream_t st) {
     const int n = H * E;
-    hipLaunchKernelGGL(prob_mean_kernel, dim3(n), dim3(256), 0, st, part, nbx, H, E, T, out);
+    hipLaunchKernelGGL(prob_mean_kernel, dim3((n + 15) / 16), dim3(256), 0, st, part, nbx, H, E, T, out);
     return hipGetLastError();
 }
 

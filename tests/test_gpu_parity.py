@@ -561,6 +561,23 @@ def test_layer_deterministic():
             assert torch.equal(a1[k], a2[k]), k
 
 
+@pytest.mark.parametrize("name,over", [
+    ("top2_e8_h4096", dict(T=3000, h=256, f=64)),           # P summed by the stats kernel
+    ("multihead_h8_e32_top4", dict(T=2000, h=512, f=64)),   # the same, several heads
+    ("sigmoid_top8_e256_shared", dict(T=2500, f=64)),       # P summed by its own kernel
+])
+def test_layer_P_equals_route_P(name, over):
+    """The layer's aux P (whichever kernel sums the route partials) is bit for
+    bit moe_route's P on the same inputs."""
+    cfg = inputs.variant(name, **over)
+    G.log(f"[P layer vs route] {cfg['name']}")
+    inp = G.dev_inputs(cfg)
+    _, aux = G.run_layer(cfg, inp)
+    g = route_gpu(cfg, x=inp["x"], w_router=inp["w_router"], biases=inp)
+    assert np.array_equal(aux["P"].cpu().numpy().view(np.uint32), g["P"].view(np.uint32))
+    assert np.array_equal(aux["topk_idx"].cpu().numpy(), g["topk_idx"])
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("case", [
     dict(name="tiny_f32", T=1),
