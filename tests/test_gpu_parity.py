@@ -282,6 +282,11 @@ SPLIT_CASES = {
     "tail_only_swiglu": ("top2_e8_h4096", dict(E=2, K=1, h=1024, f=1024), [310, 290]),
     "tail_only_gelu": ("switch_top1_e64_zipf", dict(E=2, K=1, h=1024, f=1024), [301, 299]),
     "whole_and_tail_swiglu": ("top2_e8_h4096", dict(E=4, K=1, h=1024, f=2048), [1300, 1250, 1290, 1280]),
+    # k stages per tile that the pieces do not divide evenly (17 and 10), and
+    # eleven ~100-row experts with 64-stage down-GEMM tiles
+    "crossing_chunks_swiglu": ("top2_e8_h4096", dict(E=2, K=1, h=1088, f=640), [300, 290]),
+    "crossing_chunks_gelu_11": ("switch_top1_e64_zipf", dict(E=11, K=1, h=1024, f=4096),
+                                [101, 97, 120, 88, 100, 100, 64, 130, 99, 105, 96]),
 }
 
 
