@@ -26,11 +26,13 @@
 //   experts), steps 2 and 3 share one launch: each chunk's rank block reads
 //   the whole histogram and forms its own bases, the totals, kept and the
 //   offsets (the same integer sums, so the same tables).
-//   3. rank:    each chunk walks its ids 64 at a time in order; lanes holding
-//               the same expert find each other with ballots over the bits of
-//               the id, a lane's rank among them is the popcount of the lower
-//               lanes, and a per-expert running count in LDS carries the queue
-//               position across steps.  pos < C keeps the row at offsets[e]+pos.
+//   3. rank:    lanes holding the same expert find each other with ballots
+//               over the bits of the id and a lane's rank among them is the
+//               popcount of the lower lanes; with at most 1024 experts the 16
+//               waves of a chunk's block take 64 positions each and add
+//               per-wave bases scanned in LDS, otherwise one wave walks the
+//               chunk 64 positions at a time with a per-expert running count.
+//               pos < C keeps the row at offsets[e]+pos.
 //   4. gather:  token-major: the slice of each sub-token is read once and
 //               copied to each of its kept rows (16-byte copies).
 // No step depends on the order in which blocks run, so the result is unique.
@@ -230,38 +232,116 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* idx, int A, int
     rank_chunk(v, a0, A, K, choice, Et, nbits, capacity, run, off, dest_row, src_token);
 }
 
-// Steps 2 and 3 in one launch when the histogram is small (nch * Et <= kFusedHist,
-// Et <= kFusedEt): every chunk's block reads the whole histogram, forms its own
-// bases (the counts of the earlier chunks, in chunk order), the totals, kept
-// = min(total, C) and the offsets (a wave prefix over the experts, each lane
-// owning a run of Et/64 of them), then ranks its ids.  Block 0 also stores the
-// tables.  Integer sums, so every block derives the same tables as the scan
-// kernel would.
-constexpr int kFusedHist = 8192, kFusedEt = 1024;
-__global__ __launch_bounds__(64) void rank_fused_kernel(const int32_t* idx, int A, int K, bool choice, int Et,
-                                                        int nbits, int capacity, int nch, const int32_t* hist,
-                                                        int32_t* counts, int32_t* kept, int32_t* offsets,
-                                                        int32_t* n_kept, int32_t* dest_row, int32_t* src_token) {
-    __shared__ int32_t run[kFusedEt];
-    __shared__ int32_t off[kFusedEt];
-    const int lane = threadIdx.x;
+// Step 3 over one chunk with 16 waves (Et <= kWideEt): wave w owns queue
+// positions a0 + 64 w + lane and finds, with the ballots of rank_chunk, the
+// lanes holding the same expert.  The highest lane of each group stores the
+// group's size to cnt[w][e] (LDS, zeroed beforehand); the block then turns
+// cnt into each wave's base per expert (chunk base, then the waves in order)
+// and every lane's position is its wave's base plus the popcount of its lower
+// peers.  The same positions as rank_chunk's 16 sequential steps.
+constexpr int kWideEt = 1024;
+__device__ __forceinline__ void rank_chunk_wide(int32_t ev, int a0, int A, int K, bool choice, int Et, int nbits,
+                                                int capacity, int32_t (*cnt)[kWideEt], const int32_t* chunk_base,
+                                                const int32_t* off, int32_t* dest_row, int32_t* src_token) {
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int i = a0 + 64 * w + lane;
+    const int S = A / K;
+    const int a = i < A ? queue_at(i, S, K, choice) : A;
+    const bool valid = (unsigned)ev < (unsigned)Et;
+    const int e = valid ? ev : 0;
+    uint64_t peers = __ballot(valid);
+    if (!valid) peers = ~peers;
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool b = (e >> bit) & 1;
+        const uint64_t m = __ballot(b);
+        peers &= b ? m : ~m;
+    }
+    if (valid && (peers >> lane) == 1ull) cnt[w][e] = __popcll(peers);
+    __syncthreads();
+    for (int x = tid; x < Et; x += 1024) {
+        int32_t run = chunk_base[x];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int32_t c = cnt[q][x];
+            cnt[q][x] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (a < A && !valid) dest_row[a] = -1;
+    if (valid) {
+        const int32_t pos = cnt[w][e] + __popcll(peers & lanemask_lt());
+        if (pos < capacity) {
+            const int32_t row = off[e] + pos;
+            dest_row[a] = row;
+            src_token[row] = a / K;
+        } else {
+            dest_row[a] = -1;
+        }
+    }
+}
+
+// Step 3 after the scan kernel, 16 waves per chunk (Et <= kWideEt): the bases
+// come from hist as the scan rewrote it, the offsets from kept (the same prefix
+// in every block; block 0 stores it).  base may be null (no chunks).
+__global__ __launch_bounds__(1024) void rank_wide_kernel(const int32_t* idx, int A, int K, bool choice, int Et,
+                                                         int nbits, int capacity, const int32_t* base,
+                                                         const int32_t* kept, int32_t* offsets, int32_t* n_kept,
+                                                         int32_t* dest_row, int32_t* src_token) {
+    __shared__ int32_t cnt[16][kWideEt];
+    __shared__ int32_t cb[kWideEt];
+    __shared__ int32_t off[kWideEt];
+    const int tid = threadIdx.x;
     const int c = blockIdx.x, a0 = c * CHUNK;
-    int32_t v[CHUNK / 64];
-    load_chunk(idx, a0, A, K, choice, v);
+    const int S = A / K;
+    const int i = a0 + tid;
+    const int32_t ev = i < A ? idx[queue_at(i, S, K, choice)] : -1;
+    for (int x = tid; x < 16 * Et; x += 1024) cnt[x / Et][x % Et] = 0;
+    for (int e = tid; e < Et; e += 1024) {
+        cb[e] = base ? base[(size_t)c * Et + e] : 0;
+        off[e] = kept[e];
+    }
+    __syncthreads();
+    if (tid < 64) offsets_from_kept(off, Et, c == 0, offsets, n_kept);
+    rank_chunk_wide(ev, a0, A, K, choice, Et, nbits, capacity, cnt, cb, off, dest_row, src_token);
+}
+
+// Steps 2 and 3 in one launch when the histogram is small (nch * Et <= kFusedHist,
+// Et <= kWideEt): every chunk's block (16 waves) reads the whole histogram,
+// forms its own bases (the counts of the earlier chunks, in chunk order), the
+// totals, kept = min(total, C) and the offsets (a wave prefix over the experts,
+// each lane owning a run of Et/64 of them), then ranks its ids
+// (rank_chunk_wide).  Block 0 also stores the tables.  Integer sums, so every
+// block derives the same tables as the scan kernel would.
+constexpr int kFusedHist = 8192;
+__global__ __launch_bounds__(1024) void rank_fused_kernel(const int32_t* idx, int A, int K, bool choice, int Et,
+                                                          int nbits, int capacity, int nch, const int32_t* hist,
+                                                          int32_t* counts, int32_t* kept, int32_t* offsets,
+                                                          int32_t* n_kept, int32_t* dest_row, int32_t* src_token) {
+    __shared__ int32_t cnt[16][kWideEt];
+    __shared__ int32_t base[kWideEt];
+    __shared__ int32_t off[kWideEt];
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x, a0 = c * CHUNK;
+    // this thread's id (queue position a0 + tid), loaded first
+    const int S = A / K;
+    const int i = a0 + tid;
+    const int32_t ev = i < A ? idx[queue_at(i, S, K, choice)] : -1;
+    for (int x = tid; x < 16 * Et; x += 1024) cnt[x / Et][x % Et] = 0;
     // per expert: base over chunks < c, total over all chunks (16 loads in flight)
-    for (int e = lane; e < Et; e += 64) {
-        int32_t base = 0, tot = 0;
+    for (int e = tid; e < Et; e += 1024) {
+        int32_t b = 0, tot = 0;
         for (int q0 = 0; q0 < nch; q0 += 16) {
             int32_t h[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) h[j] = q0 + j < nch ? hist[(size_t)(q0 + j) * Et + e] : 0;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                base += q0 + j < c ? h[j] : 0;
+                b += q0 + j < c ? h[j] : 0;
                 tot += h[j];
             }
         }
-        run[e] = base;
+        base[e] = b;
         off[e] = tot > capacity ? capacity : tot;  // kept, turned into offsets below
         if (c == 0) {
             counts[e] = tot;
@@ -269,9 +349,9 @@ __global__ __launch_bounds__(64) void rank_fused_kernel(const int32_t* idx, int 
         }
     }
     __syncthreads();
-    offsets_from_kept(off, Et, c == 0, offsets, n_kept);
-    __syncthreads();
-    rank_chunk(v, a0, A, K, choice, Et, nbits, capacity, run, off, dest_row, src_token);
+    if (tid < 64) offsets_from_kept(off, Et, c == 0, offsets, n_kept);
+    // (rank_chunk_wide's first barrier orders the offsets before their use)
+    rank_chunk_wide(ev, a0, A, K, choice, Et, nbits, capacity, cnt, base, off, dest_row, src_token);
 }
 
 // Steps 1-3 in one block of 1024 threads (16 waves) when the assignment list
@@ -423,8 +503,8 @@ static hipError_t launch_tables_chunked(const PermuteArgs& p, int nch, int nbits
                            p.Et, nch, p.hist);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (nch > 0 && (size_t)nch * p.Et <= (size_t)kFusedHist && p.Et <= kFusedEt) {
-        hipLaunchKernelGGL(rank_fused_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K,
+    if (nch > 0 && (size_t)nch * p.Et <= (size_t)kFusedHist && p.Et <= kWideEt) {
+        hipLaunchKernelGGL(rank_fused_kernel, dim3(nch), dim3(1024), 0, st, p.topk_idx, p.A, p.K,
                            p.queue == MOE_QUEUE_CHOICE, p.Et, nbits, p.capacity, nch, p.hist, p.counts, p.kept,
                            p.offsets, p.n_kept, p.dest_row, p.src_token);
         return hipGetLastError();
@@ -435,13 +515,16 @@ static hipError_t launch_tables_chunked(const PermuteArgs& p, int nch, int nbits
     hipLaunchKernelGGL(scan_kernel, dim3((p.Et + epb - 1) / epb), dim3(1024), 0, st, p.hist, nch, p.Et, epb,
                        p.capacity, p.counts, p.kept);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (nch == 0) {  // no assignments: one block stores the (zero) offsets
-        hipLaunchKernelGGL(rank_kernel, dim3(1), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE,
-                           p.Et, nbits, p.capacity, nullptr, p.kept, p.offsets, p.n_kept, p.dest_row, p.src_token);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE, p.Et, nbits,
-                       p.capacity, p.hist, p.kept, p.offsets, p.n_kept, p.dest_row, p.src_token);
+    // no assignments: one block stores the (zero) offsets
+    const int nb = nch > 0 ? nch : 1;
+    const int32_t* base = nch > 0 ? p.hist : nullptr;
+    if (p.Et <= kWideEt)
+        hipLaunchKernelGGL(rank_wide_kernel, dim3(nb), dim3(1024), 0, st, p.topk_idx, p.A, p.K,
+                           p.queue == MOE_QUEUE_CHOICE, p.Et, nbits, p.capacity, base, p.kept, p.offsets, p.n_kept,
+                           p.dest_row, p.src_token);
+    else
+        hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE,
+                           p.Et, nbits, p.capacity, base, p.kept, p.offsets, p.n_kept, p.dest_row, p.src_token);
     return hipGetLastError();
 }
 
