@@ -64,18 +64,19 @@ __device__ __forceinline__ void load_chunk(const int32_t* idx, int a0, int A, in
     }
 }
 
-__global__ __launch_bounds__(64) void hist_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nch,
-                                                  int32_t* hist) {
+// one thread per queue position of the chunk
+static_assert(CHUNK == 1024, "hist_kernel and the 16-wave rank kernels take one thread per queue position");
+__global__ __launch_bounds__(1024) void hist_kernel(const int32_t* idx, int A, int K, bool choice, int Et, int nch,
+                                                    int32_t* hist) {
     __shared__ int cnt[MAX_ET];
-    int32_t v[CHUNK / 64];
-    load_chunk(idx, blockIdx.x * CHUNK, A, K, choice, v);
-    for (int e = threadIdx.x; e < Et; e += 64) cnt[e] = 0;
+    const int tid = threadIdx.x;
+    const int i = blockIdx.x * CHUNK + tid;
+    const int32_t e = i < A ? idx[queue_at(i, A / K, K, choice)] : -1;
+    for (int x = tid; x < Et; x += 1024) cnt[x] = 0;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < CHUNK / 64; ++j)
-        if ((unsigned)v[j] < (unsigned)Et) atomicAdd(&cnt[v[j]], 1);  // out-of-range ids are dropped
+    if ((unsigned)e < (unsigned)Et) atomicAdd(&cnt[e], 1);  // out-of-range ids are dropped
     __syncthreads();
-    for (int e = threadIdx.x; e < Et; e += 64) hist[(size_t)blockIdx.x * Et + e] = cnt[e];
+    for (int x = tid; x < Et; x += 1024) hist[(size_t)blockIdx.x * Et + x] = cnt[x];
 }
 
 // Experts [blockIdx.x * epb, +epb) per block of 1024 threads.  hist [nch][Et]
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const void* x, int H, int r
 static hipError_t launch_tables_chunked(const PermuteArgs& p, int nch, int nbits, hipStream_t st) {
     hipError_t err;
     if (nch > 0) {
-        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(64), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE,
+        hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(1024), 0, st, p.topk_idx, p.A, p.K, p.queue == MOE_QUEUE_CHOICE,
                            p.Et, nch, p.hist);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
