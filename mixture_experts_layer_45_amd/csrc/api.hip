@@ -588,8 +588,11 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
     int32_t* dest_row = aux && aux->dest_row && !sv ? aux->dest_row : L.dest_row;
     int32_t* counts = aux && aux->counts && !sv ? aux->counts : L.counts;
     const bool want_stats = aux && (aux->f || aux->P || aux->l_aux || aux->kept || aux->n_kept || aux->n_dropped);
-    // small partial tables: the stats kernel sums P itself (one launch fewer)
-    const bool fold_p = d->gate == MOE_GATE_TOPK && (size_t)p.route_nbx * p.Et <= kFoldPartials;
+    // few experts and small partial tables: the stats kernel sums P itself (one
+    // launch fewer; measured on one MI355X: top-2 layer 10.5 -> 7.5 us, Zipf
+    // top-1 12.9 -> 10.6 us; with 256 experts its one block is slower than the
+    // P kernel's many)
+    const bool fold_p = d->gate == MOE_GATE_TOPK && p.Et <= 64 && (size_t)p.route_nbx * p.Et <= kFoldPartials;
     hipError_t e;
 
     if (d->gate == MOE_GATE_HASH) {

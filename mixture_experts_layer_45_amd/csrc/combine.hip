@@ -133,8 +133,9 @@ hipError_t launch_zero_dropped(const int32_t* dest_row, int T, int row_bytes, vo
     return hipGetLastError();
 }
 
-// f_e = counts_e / (T K); P as given, or summed here from the route kernels'
-// partials (the same order as prob_mean_kernel, so the same bits); L_aux =
+// f_e = counts_e / (T K); P as given, or (at most 64 experts in all) summed
+// here from the route kernels' partials (the same order as prob_mean_kernel, so
+// the same bits); L_aux =
 // mean over heads of alpha E sum_e f_e P_e (fixed-order serial sums; E is at
 // most 256).  One block.
 constexpr int kStatsMaxEt = 4096;
@@ -144,13 +145,11 @@ __global__ __launch_bounds__(1024) void stats_kernel(StatsArgs a) {
     __shared__ float Pl[kStatsMaxEt];
     __shared__ float fl[kStatsMaxEt];
     __shared__ float headsum[256];
-    if (a.prob_part) {
-        for (int e0 = 0; e0 < Et; e0 += 1024 / kPLanes) {
-            const int ge = e0 + tid / kPLanes, j = tid % kPLanes;
-            const bool valid = ge < Et;
-            const float v = prob_mean_of(a.prob_part, a.nbx, a.E, a.T, ge, valid, j);
-            if (valid && j == 0) Pl[ge] = v;
-        }
+    if (a.prob_part) {  // at most 64 experts in all (p_lanes = 16): one pass
+        const int ge = tid / 16, j = tid % 16;
+        const bool valid = ge < Et;
+        const float v = prob_mean_of<16>(a.prob_part, a.nbx, a.E, a.T, ge, valid, j);
+        if (valid && j == 0) Pl[ge] = v;
     } else {
         for (int i = tid; i < Et; i += 1024) Pl[i] = a.prob_mean[i];
     }

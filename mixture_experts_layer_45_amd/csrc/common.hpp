@@ -80,20 +80,21 @@ __device__ __forceinline__ int bfly(int v) { return (int)bfly_u32<OFF>((uint32_t
 
 // P from the route kernels' partials part[(g*nbx + b)*E + e] (block b's sum of
 // head g's score distributions over its tokens): P_e = (sum over b) / T in one
-// fixed order, 16 consecutive lanes per expert ge = g*E + e, lane j adding
-// b = j, j+16, ... in turn, then the butterfly over the 16 lanes.  All 16
-// lanes of the group must call it (valid false: no loads, any value); each
-// returns the same bits.
-constexpr int kPLanes = 16;
+// fixed order, LANES consecutive lanes per expert ge = g*E + e (16 for at most
+// 64 experts in all, else 64: p_lanes), lane j adding b = j, j+LANES, ... in
+// turn, then the butterfly over the LANES lanes.  All LANES lanes of the group
+// must call it (valid false: no loads, any value); each returns the same bits.
+constexpr int p_lanes(int Et) { return Et <= 64 ? 16 : 64; }
+template <int LANES>
 __device__ __forceinline__ float prob_mean_of(const float* part, int nbx, int E, int T, int ge, bool valid, int j) {
     float s = 0.0f;
     if (valid) {
         const int g = ge / E, e = ge - g * E;
         const float* p = part + (size_t)g * nbx * E + e;
 #pragma unroll 8
-        for (int b = j; b < nbx; b += kPLanes) s += p[(size_t)b * E];
+        for (int b = j; b < nbx; b += LANES) s += p[(size_t)b * E];
     }
-    bfly_steps<kPLanes>([&](auto O) __attribute__((always_inline)) { s += bfly<decltype(O)::value>(s); });
+    bfly_steps<LANES>([&](auto O) __attribute__((always_inline)) { s += bfly<decltype(O)::value>(s); });
     return T > 0 ? s / (float)T : 0.0f;
 }
 

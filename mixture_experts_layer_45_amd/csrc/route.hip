@@ -625,11 +625,12 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(RouteArgs a) {
     }
 }
 
-// P_e for 16 experts per block of 256 threads (prob_mean_of's lane layout)
+// P_e for 256/LANES experts per block of 256 threads (prob_mean_of's lane layout)
+template <int LANES>
 __global__ __launch_bounds__(256) void prob_mean_kernel(const float* part, int nbx, int H, int E, int T, float* out) {
-    const int ge = blockIdx.x * 16 + (int)(threadIdx.x / kPLanes), j = threadIdx.x % kPLanes;
+    const int ge = blockIdx.x * (256 / LANES) + (int)(threadIdx.x / LANES), j = threadIdx.x % LANES;
     const bool valid = ge < H * E;
-    const float v = prob_mean_of(part, nbx, E, T, ge, valid, j);
+    const float v = prob_mean_of<LANES>(part, nbx, E, T, ge, valid, j);
     if (valid && j == 0) out[ge] = v;
 }
 
@@ -779,7 +780,10 @@ hipError_t launch_route(const RouteArgs& a0, hipStream_t st) {
 
 hipError_t launch_prob_mean(const float* part, int nbx, int H, int E, int T, float* out, hipStream_t st) {
     const int n = H * E;
-    hipLaunchKernelGGL(prob_mean_kernel, dim3((n + 15) / 16), dim3(256), 0, st, part, nbx, H, E, T, out);
+    if (p_lanes(n) == 16)
+        hipLaunchKernelGGL(prob_mean_kernel<16>, dim3((n + 15) / 16), dim3(256), 0, st, part, nbx, H, E, T, out);
+    else
+        hipLaunchKernelGGL(prob_mean_kernel<64>, dim3((n + 3) / 4), dim3(256), 0, st, part, nbx, H, E, T, out);
     return hipGetLastError();
 }
 

@@ -567,9 +567,10 @@ def test_layer_deterministic():
 
 
 @pytest.mark.parametrize("name,over", [
-    ("top2_e8_h4096", dict(T=3000, h=256, f=64)),           # P summed by the stats kernel
-    ("multihead_h8_e32_top4", dict(T=2000, h=512, f=64)),   # the same, several heads
-    ("sigmoid_top8_e256_shared", dict(T=2500, f=64)),       # P summed by its own kernel
+    ("top2_e8_h4096", dict(T=3000, h=256, f=64)),                      # P summed by the stats kernel
+    ("multihead_h8_e32_top4", dict(T=2000, H=2, E=24, h=512, f=64)),   # the same, two heads
+    ("multihead_h8_e32_top4", dict(T=2000, h=512, f=64)),              # P summed by its own kernel
+    ("sigmoid_top8_e256_shared", dict(T=2500, f=64)),                  # the same, one head
 ])
 def test_layer_P_equals_route_P(name, over):
     """The layer's aux P (whichever kernel sums the route partials) is bit for
