@@ -145,11 +145,13 @@ __global__ __launch_bounds__(1024) void stats_kernel(StatsArgs a) {
     __shared__ float Pl[kStatsMaxEt];
     __shared__ float fl[kStatsMaxEt];
     __shared__ float headsum[256];
-    if (a.prob_part) {  // at most 64 experts in all (p_lanes = 16): one pass
-        const int ge = tid / 16, j = tid % 16;
-        const bool valid = ge < Et;
-        const float v = prob_mean_of<16>(a.prob_part, a.nbx, a.E, a.T, ge, valid, j);
-        if (valid && j == 0) Pl[ge] = v;
+    if (a.prob_part) {  // the layer folds P here for at most 64 experts in all (one pass)
+        for (int e0 = 0; e0 < Et; e0 += 1024 / 16) {
+            const int ge = e0 + tid / 16, j = tid % 16;
+            const bool valid = ge < Et;
+            const float v = prob_mean_of<16>(a.prob_part, a.nbx, a.E, a.T, ge, valid, j);
+            if (valid && j == 0) Pl[ge] = v;
+        }
     } else {
         for (int i = tid; i < Et; i += 1024) Pl[i] = a.prob_mean[i];
     }
