@@ -216,6 +216,11 @@ RAGGED_PERMUTE = {
     "multihead_A9600_cap": ("multihead_h8_e32_top4", dict(T=300, h=64, capacity_factor=1.0), 0.8, "cfg"),
     "sigmoid_A40000_cap": ("sigmoid_top8_e256_shared", dict(T=5000, h=64, capacity_factor=1.1), 0.6, "cfg"),
     "switch_A5000_badids": ("switch_top1_e64_zipf", dict(T=5000, h=64), 1.0, "cfg"),
+    # 1024 experts in all (the largest the 16-wave rank kernels take) and 1280
+    # (the one-wave rank kernel after the scan)
+    "heads4_e256_Et1024": ("multihead_h8_e32_top4", dict(T=600, H=4, E=256, K=2, h=256), 0.4, "cfg"),
+    "heads5_e256_Et1280_cap": ("multihead_h8_e32_top4", dict(T=700, H=5, E=256, K=3, h=320, capacity_factor=1.2),
+                               0.7, "cfg"),
 }
 
 
