@@ -377,8 +377,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(RouteArgs a) {
     (void)Et;
 }
 
-// Selection for the RS tokens t0, t0+1, ... of head g (the bf16 kernels for at
-// most 64 experts per head): LPT lanes per token (threads tid < RS*LPT; the
+// Selection for the RS tokens t0, t0+1, ... of head g (phase 2 of
+// route_small_kernel): LPT lanes per token (threads tid < RS*LPT; the
 // others idle), each lane holding experts lq, lq + LPT, ... of the token's row
 // of logits lg [RS][NB*16+1] (LDS); every arg-max round is a lane-local scan
 // then a butterfly over the token's lanes on the (key desc, index asc) order.
