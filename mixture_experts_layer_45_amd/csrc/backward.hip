@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint16_t* dcat, 
         u32x4 o;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            o[q] = (uint32_t)f32_to_bf16(oe[2 * q]) | ((uint32_t)f32_to_bf16(oe[2 * q + 1]) << 16);
+            o[q] = pack_bf16x2(oe[2 * q], oe[2 * q + 1]);
         *(u32x4*)(orow + j) = o;
     }
     acc = wsum(acc);
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void dx_kernel(const uint16_t* dXp, const int3
     if (dxs) add(*(const u32x4*)(dxs + (size_t)t * h + col));
     u32x4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
     *(u32x4*)(dx + (size_t)t * h + col) = o;
 }
 

@@ -78,10 +78,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int tpr) {
                 }
             }
             uint4 out;
-            out.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-            out.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-            out.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
-            out.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+            out.x = pack_bf16x2(acc[0], acc[1]);
+            out.y = pack_bf16x2(acc[2], acc[3]);
+            out.z = pack_bf16x2(acc[4], acc[5]);
+            out.w = pack_bf16x2(acc[6], acc[7]);
             *(uint4*)((uint16_t*)a.y + o) = out;
         } else {
             float* yo = (float*)a.y + o;

@@ -15,12 +15,15 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even, on gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32; for every non-NaN fp32 value it gives the bits of the
+// integer formula u += 0x7fff + ((u >> 16) & 1), u >> 16, checked over all 2^32
+// inputs; NaN stays NaN).  Two at a time where possible (pack_bf16x2).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const bf16x2v v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -474,10 +474,6 @@ struct LdsRun<0> {
     static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t, lds_void_ptr, const uint32_t*, int) {}
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
-
 // Epilogue of the persistent kernels (weight fragment as the MFMA's first
 // operand): activation in fp32, one rounding to bf16, then (lane l holding row
 // l%32 and, per group q of four, columns 8q + 4*(l/32) + 0..3) one
