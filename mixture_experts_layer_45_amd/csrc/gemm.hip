@@ -10,14 +10,18 @@
 // first writes a table of the real M-tiles (group, first row, end row); the
 // GEMM blocks read their tile from it and surplus blocks exit.
 //
-// Three bf16 kernels for gfx950 share the tile table, the XCD-aware schedule
+// Four bf16 kernels for gfx950 share the tile table, the XCD-aware schedule
 // and the fused epilogue (activation in fp32, one rounding to bf16):
-//   * gemm_bf16_k64_kernel  -- when K is a multiple of 64: persistent, 8 waves,
-//     BM x 256 tiles, 64-wide k stages of whole 128-byte rows, 16-byte row
-//     stores;
-//   * gemm_bf16_ring8_kernel -- gated products on 256-row tiles with K >= 4096
-//     (where it measured a few percent ahead) and any K % 32 == 0 otherwise:
-//     persistent, 8 waves, a deeper ring of 32-wide k stages;
+//   * gemm_bf16_w4_kernel -- 256-row tiles with K a multiple of 64 and at least
+//     2048 (the top-2 layer's GEMMs, the shared expert, W_o): persistent, one
+//     wave per SIMD holding a 128 x 128 quarter of the 256 x 256 tile, with a
+//     hand-laid instruction schedule;
+//   * gemm_bf16_k64_kernel  -- other shapes with K a multiple of 64: persistent,
+//     8 waves, BM x 256 tiles, 64-wide k stages of whole 128-byte rows, 16-byte
+//     row stores;
+//   * gemm_bf16_ring8_kernel -- K % 64 == 32, and the training forward's gated
+//     product on 256-row tiles with K >= 4096: persistent, 8 waves, a deeper
+//     ring of 32-wide k stages;
 //   * gemm_bf16_kernel -- any K (zero-filled tail), 4 waves, one tile per block.
 // Measured on one MI355X: the 64-wide kernel is 10-25 % faster on 128-row tiles
 // (256 experts x ~128 rows, d = 7168) and on short K (d = 512, f = 1024).
@@ -25,6 +29,7 @@
 // they lie through the LDS transposing load: the forward weights for the input
 // gradients (KM = 1) and the activations for the weight gradients (KM = 2).
 #include <algorithm>
+#include <utility>
 
 #include "common.hpp"
 
@@ -1281,6 +1286,356 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
 }
 
 
+// ------------------------------------ bf16 MFMA, 4 waves of 128 x 128, 256-row tiles
+// One wave per SIMD (256 threads) on the 256 x 256 block tile of the 64-wide
+// kernel (same LDS stages, swizzle, loads, tile schedule and split tail), each
+// wave owning a 128 x 128 quarter: 16 accumulator tiles (256 registers, all in
+// AGPRs) and, per 16-wide k sub-step, 4 activation and 4 weight fragments for
+// 16 MFMAs -- a third fewer LDS reads per MFMA than the 8-wave kernel's
+// 128 x 64 waves.  With no second wave on the SIMD to cover for it, the wave's
+// instruction stream is laid out by hand (scheduling barriers fix the order):
+// every sub-step reads the next one's 8 fragments behind its first 8 MFMAs;
+// the next stage's 16 buffer-to-LDS loads ride on the first 32 MFMAs, one per
+// two; the stage's wait and block barrier sit before the last 8 MFMAs, which
+// then cover the reads of the next stage's first fragments.  Measured on the
+// top-2 layer's gate/up GEMM: 3.45 -> 3.29-3.34 ms against the ring kernel,
+// with the clock 1.58 -> 1.70 GHz (fewer LDS operations) at the same MFMA count.
+template <int MODE>
+struct W4Cfg {
+    static constexpr int NMAT = gated_mode(MODE) ? 2 : 1;
+    static constexpr int BNM = gated_mode(MODE) ? 128 : 256;  // output columns per matrix
+    static constexpr int WM = 128;
+    static constexpr int WNM = BNM / 2;
+    static constexpr int TM = WM / 32;
+    static constexpr int TN = WNM / 32;
+    static constexpr int NB = NMAT * TN;    // weight fragments per sub-step
+    static constexpr int NACC = TM * NB;    // 32 x 32 accumulator tiles per wave
+    static constexpr int NRD = TM + NB;     // fragment reads per sub-step
+    static constexpr int A_BYTES = 256 * 128;
+    static constexpr int STAGE = A_BYTES + 256 * 128;
+    static constexpr int LPW = 16;          // loads per wave per stage (8 activation, 8 weight rows x 8)
+    static_assert(NACC == 16 && NRD == 8, "the hand-laid schedule assumes 16 MFMAs and 8 reads per sub-step");
+};
+
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(IntC<Is>{}), ...);
+}
+// f(IntC<0>{}), ..., f(IntC<N-1>{}) in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One 32 x 32 output tile of the 4-wave kernel: activation in fp32, one
+// rounding, one lane swap per register pair, 16-byte row stores (the layout
+// of rowstore_epilogue).  g (and u, the up product of SwiGLU) are in VGPRs.
+template <int MODE>
+__device__ __forceinline__ void w4_store_tile(floatx16 g, const floatx16& u, int row, int row_end, int crow, int col0,
+                                              int Nout, uint8_t* Cp, bool hi) {
+    if constexpr (gated_mode(MODE)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) g[i] = act_silu(g[i]) * u[i];
+    } else if constexpr (MODE == MODE_GELU) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) g[i] = act_gelu(g[i]);
+    }
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        // groups 2pp (columns 16pp + 0..7) and 2pp+1 (16pp + 8..15)
+        const uint32_t x0 = pack_bf16x2(g[8 * pp + 0], g[8 * pp + 1]), x1 = pack_bf16x2(g[8 * pp + 2], g[8 * pp + 3]);
+        const uint32_t y0 = pack_bf16x2(g[8 * pp + 4], g[8 * pp + 5]), y1 = pack_bf16x2(g[8 * pp + 6], g[8 * pp + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const u32x4 o = {s0[0], s1[0], s0[1], s1[1]};
+        const int col = col0 + 16 * pp + (hi ? 8 : 0);
+        if (row < row_end && col < Nout) *(u32x4*)(Cp + ((size_t)crow * Nout + col) * 2) = o;
+    }
+}
+
+// The wave's tiles one at a time.  Each accumulator tile is pinned to AGPRs
+// (an empty asm with an "a" operand) right before it is copied out: otherwise
+// the compiler copies all 256 accumulators to VGPRs at the end of the k loop
+// and spills.
+template <int MODE>
+__device__ __forceinline__ void w4_epilogue(const floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
+                                            int wm, int wn, int lane, const int32_t* c_rows, int c_nrows) {
+    using C = W4Cfg<MODE>;
+    const bool hi = lane >= 32;
+#pragma clang loop unroll(full)
+    for (int tm = 0; tm < C::TM; ++tm) {
+        const int row = row0 + wm * C::WM + tm * 32 + (lane & 31);
+        const int crow = row < row_end ? c_row(c_rows, c_nrows, row) : row;
+#pragma clang loop unroll(full)
+        for (int tn = 0; tn < C::TN; ++tn) {
+            floatx16 g = acc[tm * C::TN + tn], u;
+            asm volatile("" : "+a"(g));
+            if constexpr (gated_mode(MODE)) {
+                u = acc[C::TM * C::TN + tm * C::TN + tn];
+                asm volatile("" : "+a"(u));
+            }
+            w4_store_tile<MODE>(g, u, row, row_end, crow, n0 + wn * C::WNM + tn * 32, Nout, Cp, hi);
+        }
+    }
+}
+
+// fp32 partial tile of one piece: accumulator (ai, 4q..4q+3) of thread tid at
+// float4 index (ai*4 + q)*256 + tid of the slot
+template <int MODE>
+__device__ __forceinline__ void w4_store_partial(const floatx16* acc, float* partial, int slot, int tid) {
+    using C = W4Cfg<MODE>;
+    floatx4* P = (floatx4*)partial + (size_t)slot * (C::NACC * 4 * 256);
+#pragma clang loop unroll(full)
+    for (int ai = 0; ai < C::NACC; ++ai) {
+        floatx16 v = acc[ai];
+        asm volatile("" : "+a"(v));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) P[(ai * 4 + q) * 256 + tid] = floatx4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
+    // device pass only (LDS address-space casts, buffer-to-LDS loads)
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = W4Cfg<MODE>;
+    constexpr int TM = C::TM, NB = C::NB, NRD = C::NRD;
+    // two stages, then the word for the tile claimed for after the current one
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE + 16];
+    int32_t& next_tile = *(int32_t*)(smem + 2 * C::STAGE);
+
+    const int K = a.K, Nout = a.Nout;
+    const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int nk = K / 64;
+    const int n_m = a.tiles[a.m_tiles].group;  // real row tiles (header of the table)
+    const int total = n_m * a.n_tiles;
+    const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
+    const int q = (total + 7) / 8;
+    const int tx0 = xcd * q;  // this XCD's slice of the schedule
+    const int Tx = max(0, min(q, total - tx0));
+    int r_tail, S;
+    tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
+    const int n_whole = S > 1 ? Tx - r_tail : Tx;  // items: whole tiles, then S pieces of each tail tile
+    const int s_end = n_whole + (S > 1 ? r_tail * S : 0);
+    int s = blockIdx.x >> 3;  // first item static, later ones claimed
+    if (s >= s_end) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const bool upper = (wu * 64) / C::BNM != 0;  // this wave's weight rows come from B1 (SwiGLU up)
+    const int a_dst = wu * 64 * 128;
+    const int b_dst = C::A_BYTES + wu * 64 * 128;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, (short)0, (int)a.a_bytes, kBufWord3);
+    const int a_nrows = (int)(a.a_bytes / rowbytes);
+
+    struct Tile {
+        int row0, row_end, n0;
+        int kb, nkl, slot;  // first k stage, k stages, partial slot (-1: a whole tile)
+        __amdgpu_buffer_rsrc_t rB;
+        uint32_t va[8], vb[8];
+    };
+    // lane l of load i fills LDS chunk l%8 of row 8i + l/8 of the wave's 64-row
+    // run, so it fetches the logical chunk stored there; loads come in groups
+    // of four on one LDS base with immediate offsets 1024*(i%4), taken off here
+    auto setup = [&](int item, Tile& t) __attribute__((always_inline)) {
+        int si = tx0 + item;
+        t.kb = 0;
+        t.nkl = nk;
+        t.slot = -1;
+        if (item >= n_whole) {  // piece p of tail tile jt
+            const int j = item - n_whole, jt = j / S, p = j - jt * S;
+            si = tx0 + n_whole + jt;
+            t.kb = p * nk / S;
+            t.nkl = (p + 1) * nk / S - t.kb;
+            t.slot = xcd * kTailSlots + j;
+        }
+        int mt, nt;
+        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, 256, mt, nt);
+        t.row0 = tl.row0;
+        t.row_end = tl.row_end;
+        t.n0 = nt * C::BNM;
+        const size_t bgo = a.b_shared ? 0 : (size_t)tl.group * Nout * rowbytes;
+        const uint8_t* B0 = (const uint8_t*)a.B0 + bgo;
+        const uint8_t* B1 = gated_mode(MODE) ? (const uint8_t*)a.B1 + bgo : B0;
+        t.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(upper ? B1 : B0), (short)0, (int)((size_t)Nout * rowbytes), kBufWord3);
+        const int lr = lane >> 3, pc = lane & 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = wu * 64 + 8 * i + lr;
+            const int c = pc ^ ((r >> 1) & 7);
+            const int gr = a_row(a, min(t.row0 + r, t.row_end - 1), a_nrows);
+            t.va[i] = (uint32_t)gr * rowbytes + (uint32_t)(c * 16) - 1024u * (i % 4);
+            const int mat = r / C::BNM;
+            const int col = min(t.n0 + r - mat * C::BNM, Nout - 1);
+            t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * (i % 4);
+        }
+    };
+    // load j of stage ks of the tile into slot st: activation rows for j < 8, then weight rows
+    auto ld1 = [&](const Tile& t, int ks, int st, auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        constexpr int i = j % 8;
+        uint8_t* dst = smem + st * C::STAGE + (j < 8 ? a_dst : b_dst) + 4096 * (i / 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 8 ? rA : t.rB, (lds_void_ptr)dst, 16, j < 8 ? t.va[i] : t.vb[i],
+                                                 (t.kb + ks) * 128, 1024 * (i % 4), 0);
+    };
+    // fragment addresses: every row a lane reads is (lane % 32) plus a multiple
+    // of 32, so its swizzle term ((row / 2) % 8) is lane-constant
+    const int xsw = ((lane & 31) >> 1) & 7;
+    const uint32_t a_lane = (uint32_t)((wm * C::WM + (lane & 31)) * 128);
+    const uint32_t b_lane = (uint32_t)(C::A_BYTES + (wn * C::WNM + (lane & 31)) * 128);
+    uint32_t chofs[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) chofs[kk] = (uint32_t)(((kk * 2 + (lane >> 5)) ^ xsw) << 4);
+    // read j of sub-step kk, in the order the MFMAs below use them: activation
+    // block 0, the NB weight fragments, activation blocks 1..TM-1 (blocks past
+    // the tile's rows, tm >= nv, are skipped)
+    auto rd1 = [&](int st, int kk, bf16x8* fr, auto J, auto NV) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value, nv = decltype(NV)::value;
+        const uint32_t base = (uint32_t)(st * C::STAGE) + chofs[kk];
+        if constexpr (j == 0) {
+            if constexpr (nv > 0) fr[0] = *(const bf16x8*)(smem + (base + a_lane));
+        } else if constexpr (j <= NB) {
+            constexpr int bi = j - 1, m = bi / C::TN, tn = bi % C::TN;
+            fr[TM + bi] = *(const bf16x8*)(smem + (base + b_lane + (m * C::BNM + tn * 32) * 128));
+        } else {
+            constexpr int tm = j - NB;
+            if constexpr (tm < nv) fr[tm] = *(const bf16x8*)(smem + (base + a_lane + tm * 32 * 128));
+        }
+    };
+    floatx16 acc[C::NACC];
+    // MFMA i of a sub-step: activation block tm = i / NB, weight fragment i % NB
+    auto mf1 = [&](const bf16x8* fr, auto I, auto NV) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value, nv = decltype(NV)::value;
+        constexpr int tm = i / NB, bi = i % NB, m = bi / C::TN, tn = bi % C::TN;
+        constexpr int ai = (m * TM + tm) * C::TN + tn;
+        if constexpr (tm < nv) acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[TM + bi], fr[tm], acc[ai], 0, 0, 0);
+    };
+
+    Tile cur;
+    setup(s, cur);
+    static_for<C::LPW>([&](auto J) { ld1(cur, 0, 0, J); });
+    bf16x8 fa[NRD], fb[NRD];
+    int32_t claim = 0;  // lane 0 of wave 0: the claim counter's answer for the current tile
+    while (true) {
+#pragma unroll
+        for (int i = 0; i < C::NACC; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+        // claim the block's next item now; the answer is needed only after the k loop
+        if (tid == 0) claim = __hip_atomic_fetch_add(a.claim + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_vmcnt<0>();  // stage 0 landed (and the last tile's stores)
+        __builtin_amdgcn_s_barrier();
+        auto kloop = [&](auto NV) __attribute__((always_inline)) {
+            static_for<NRD>([&](auto J) { rd1(0, 0, fa, J, NV); });
+            // stage kt in MFMA slots p = 16 kk + i: sub-steps on fa, fb, fa, fb
+            auto stage = [&](int kt, auto HN) __attribute__((always_inline)) {
+                constexpr bool hn = decltype(HN)::value;  // a next stage follows
+                const int slot = kt & 1, nslot = slot ^ 1;
+                static_for<64>([&](auto P) {
+                    constexpr int p = decltype(P)::value, kk = p / 16, i = p % 16;
+                    if constexpr (p == 56) {
+                        if constexpr (hn) {
+                            // this wave's reads of the slot have returned and its loads
+                            // of the next stage have landed
+                            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                            wait_vmcnt<0>();
+                        } else {  // last stage: publish the claimed item
+                            if (tid == 0) next_tile = per + claim;
+                            __builtin_amdgcn_s_waitcnt(0xC07F);
+                        }
+                        __builtin_amdgcn_s_barrier();
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    mf1(kk % 2 == 0 ? fa : fb, IntC<i>{}, NV);
+                    if constexpr (kk < 3) {
+                        if constexpr (i < NRD) rd1(slot, kk + 1, kk % 2 == 0 ? fb : fa, IntC<i>{}, NV);
+                    } else if constexpr (hn && p >= 56) {
+                        rd1(nslot, 0, fa, IntC<p - 56>{}, NV);
+                    }
+                    if constexpr (hn && p < 32 && p % 2 == 0) ld1(cur, kt + 1, nslot, IntC<p / 2>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+            const int nk1 = cur.nkl - 1;
+            for (int kt = 0; kt < nk1; ++kt) stage(kt, IntC<1>{});
+            stage(nk1, IntC<0>{});
+        };
+        // a ragged last row tile of a group leaves some waves' row blocks empty
+        const int nvb = __builtin_amdgcn_readfirstlane(min(max((cur.row_end - cur.row0 - wm * C::WM + 31) / 32, 0), TM));
+        if (nvb == TM) kloop(IntC<TM>{});
+        else if (nvb == 0) kloop(IntC<0>{});
+        else if (nvb == 1) kloop(IntC<1>{});
+        else if (nvb == 2) kloop(IntC<2>{});
+        else kloop(IntC<3>{});
+        // every slot is free: start the next item's first stage, then store this one
+        const int s_next = __builtin_amdgcn_readfirstlane(next_tile);
+        const bool more = s_next < s_end;
+        Tile nxt;
+        if (more) {
+            setup(s_next, nxt);
+            static_for<C::LPW>([&](auto J) { ld1(nxt, 0, 0, J); });
+        }
+        if (cur.slot >= 0)
+            w4_store_partial<MODE>(acc, a.partial, cur.slot, tid);
+        else
+            w4_epilogue<MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane, a.c_rows, a.c_nrows);
+        if (!more) break;
+        cur = nxt;
+        s = s_next;
+    }
+    wait_vmcnt<0>();
+#endif
+}
+
+// The split tail tiles of the 4-wave kernel (ungated products: the gated one
+// is never split): each (XCD, tail tile) block sums the tile's pieces in piece
+// order, one 32 x 32 output tile at a time, and runs the epilogue (the thread
+// layout of the 4-wave kernel).
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm_w4_tail_kernel(GArgs a, int per) {
+    using C = W4Cfg<MODE>;
+    static_assert(!gated_mode(MODE), "the gated product keeps whole tiles");
+    const int xcd = blockIdx.x / kTailSlots, jt = blockIdx.x % kTailSlots;
+    const int nk = a.K / 64;
+    const int n_m = a.tiles[a.m_tiles].group;
+    const int total = n_m * a.n_tiles;
+    const int q = (total + 7) / 8;
+    const int tx0 = xcd * q;
+    const int Tx = max(0, min(q, total - tx0));
+    int r_tail, S;
+    tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
+    if (S < 2 || jt >= r_tail) return;
+    int mt, nt;
+    const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, 256, mt, nt);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool hi = lane >= 32;
+    const floatx4* P0 = (const floatx4*)a.partial + (size_t)(xcd * kTailSlots + jt * S) * (C::NACC * 4 * 256);
+    auto sum_tile = [&](int ai) {
+        floatx16 v;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = 0.0f;
+        for (int p = 0; p < S; ++p) {
+            const floatx4* P = P0 + (size_t)p * (C::NACC * 4 * 256);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const floatx4 x = P[(ai * 4 + q4) * 256 + tid];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[4 * q4 + i] += x[i];
+            }
+        }
+        return v;
+    };
+    for (int tm = 0; tm < C::TM; ++tm) {
+        const int row = tl.row0 + wm * C::WM + tm * 32 + (lane & 31);
+        const int crow = row < tl.row_end ? c_row(a.c_rows, a.c_nrows, row) : row;
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const floatx16 g = sum_tile(tm * C::TN + tn);
+            w4_store_tile<MODE>(g, g, row, tl.row_end, crow, nt * C::BNM + wn * C::WNM + tn * 32, a.Nout, (uint8_t*)a.C, hi);
+        }
+    }
+}
+
 // ------------------------------------------------------------- fp32 VALU
 // 64 x 64 output tile per matrix, BK = 16, 256 threads each computing 4x4.
 constexpr int FBM = 64, FBN = 64, FBK = 16;
@@ -1378,6 +1733,31 @@ static int persistent_blocks() {
     return cached[dev];
 }
 
+// the 4-wave kernel (and its split-tail sums): 256-row tiles, K a multiple of
+// 64.  The gated product keeps whole tiles: the training forward runs it on the
+// ring kernel with a saving epilogue, and both then sum every output in the
+// same k order, so the two forwards agree bit for bit.
+template <int MODE>
+static hipError_t run_w4(GArgs g, hipStream_t st) {
+    using R = W4Cfg<MODE>;
+    g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+    if constexpr (gated_mode(MODE)) g.partial = nullptr;
+    const int pb = persistent_blocks();
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<MODE>), dim3(pb), dim3(256), 0, st, g);
+    hipError_t err = hipGetLastError();
+    if constexpr (!gated_mode(MODE)) {
+        if (err == hipSuccess && g.partial) {
+            hipLaunchKernelGGL((gemm_w4_tail_kernel<MODE>), dim3(8 * kTailSlots), dim3(256), 0, st, g, pb / 8);
+            err = hipGetLastError();
+        }
+    }
+    return err;
+}
+// shortest K for the 4-wave kernel: with one wave per SIMD nothing covers a
+// tile's first stage and epilogue, which short-K tiles repeat often (the
+// multi-head layer's K = 512 gate/up GEMM: 0.75 -> 0.80 ms on it)
+constexpr int kW4MinK = 2048;
+
 template <int BM, int MODE>
 static hipError_t run_bf16(GArgs g, hipStream_t st) {
     using C = TileCfg<BM, MODE>;
@@ -1392,6 +1772,10 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     // rows 16-byte aligned), except for a gated product on 256-row tiles with a
     // long K, where the ring kernel measured ahead (for the plain long-K products
     // it measured behind: top-2 down 1.72 -> 1.90 ms, W_o 0.23 -> 0.25 ms)
+    if constexpr (BM == 256) {
+        if (offsets_fit && g.K % 64 == 0 && g.K >= kW4MinK && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0 && !g.kspan)
+            return run_w4<MODE>(g, st);
+    }
     const bool ring_first = MODE != MODE_PLAIN && BM == 256 && g.K >= 4096;
     if (!ring_first && offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
         using R = K64Cfg<BM, MODE>;

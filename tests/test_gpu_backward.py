@@ -157,11 +157,12 @@ def test_training_forward_matches_forward():
 
 
 def test_training_forward_long_k_saves_activation_derivatives():
-    """The shape where the gate/up GEMM runs on the ring kernel (256-row tiles,
-    K = 4096): the training forward's output equals the inference forward's bit
-    for bit (same kernel and k order), and the saved dh/da, dh/du of sampled
-    rows match an fp64 recomputation from x and the expert weights within one
-    bf16 rounding."""
+    """The shape where the gate/up GEMM runs on 256-row tiles with K = 4096 (the
+    inference forward on the 4-wave kernel, the training forward on the ring
+    kernel with its saving epilogue): the training forward's output equals the
+    inference forward's bit for bit (the same k order), and the saved dh/da,
+    dh/du of sampled rows match an fp64 recomputation from x and the expert
+    weights within one bf16 rounding."""
     cfg = inputs.variant("top2_e8_h4096", T=2048, f=256)
     inp = G.dev_inputs(cfg)
     y0, aux = G.run_layer(cfg, inp)

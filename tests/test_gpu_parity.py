@@ -292,6 +292,14 @@ SPLIT_CASES = {
     "crossing_chunks_swiglu": ("top2_e8_h4096", dict(E=2, K=1, h=1088, f=640), [300, 290]),
     "crossing_chunks_gelu_11": ("switch_top1_e64_zipf", dict(E=11, K=1, h=1024, f=4096),
                                 [101, 97, 120, 88, 100, 100, 64, 130, 99, 105, 96]),
+    # the 4-wave kernel (256-row tiles, K >= 2048), ragged row tiles: plain and
+    # GELU products whose tiles are all tail tiles, split into 8 pieces; gated
+    # products (never split: whole tiles only) before a split plain down GEMM,
+    # whose whole tiles come before a tail of 2-piece tiles (K = 4096)
+    "w4_tail_only_swiglu": ("top2_e8_h4096", dict(E=2, K=1, h=2048, f=1024), [600, 700]),
+    "w4_tail_only_plain": ("top2_e8_h4096", dict(E=2, K=1, h=1024, f=2048), [600, 700]),
+    "w4_tail_only_gelu": ("switch_top1_e64_zipf", dict(E=2, K=1, h=2048, f=1024), [700, 600]),
+    "w4_whole_and_tail_swiglu": ("top2_e8_h4096", dict(E=2, K=1, h=2048, f=4096), [1100, 1300]),
 }
 
 
@@ -638,6 +646,9 @@ K1_CASES = {
     "sigmoid_k1": ("sigmoid_top8_e256_shared", dict(T=700, h=256, f=192, E=24, K=1, n_shared=0,
                                                     capacity_factor=1.0)),
     "fp32_k1": ("tiny_f32", dict(T=300, K=1, capacity_factor=1.0)),
+    # 256-row tiles and K = 2048: the 4-wave down GEMM, its tail split into 8
+    # pieces, whose sums are stored to the tokens' rows
+    "switch_k1_w4_tail": ("switch_top1_e64_zipf", dict(T=3000, h=256, f=2048, E=4, capacity_factor=1.0)),
 }
 
 
