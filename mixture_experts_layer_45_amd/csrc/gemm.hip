@@ -1368,13 +1368,15 @@ __device__ __forceinline__ void w4_epilogue(const floatx16* acc, int row0, int r
         const int crow = row < row_end ? c_row(c_rows, c_nrows, row) : row;
 #pragma clang loop unroll(full)
         for (int tn = 0; tn < C::TN; ++tn) {
-            floatx16 g = acc[tm * C::TN + tn], u;
+            floatx16 g = acc[tm * C::TN + tn];
             asm volatile("" : "+a"(g));
             if constexpr (gated_mode(MODE)) {
-                u = acc[C::TM * C::TN + tm * C::TN + tn];
+                floatx16 u = acc[C::TM * C::TN + tm * C::TN + tn];
                 asm volatile("" : "+a"(u));
+                w4_store_tile<MODE>(g, u, row, row_end, crow, n0 + wn * C::WNM + tn * 32, Nout, Cp, hi);
+            } else {
+                w4_store_tile<MODE>(g, g, row, row_end, crow, n0 + wn * C::WNM + tn * 32, Nout, Cp, hi);
             }
-            w4_store_tile<MODE>(g, u, row, row_end, crow, n0 + wn * C::WNM + tn * 32, Nout, Cp, hi);
         }
     }
 }
@@ -1589,12 +1591,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
 
 // The split tail tiles of the 4-wave kernel (ungated products: the gated one
 // is never split): each (XCD, tail tile) block sums the tile's pieces in piece
-// order, one 32 x 32 output tile at a time, and runs the epilogue (the thread
-// layout of the 4-wave kernel).
+// order and runs the epilogue.  1024 threads: thread t takes the accumulators
+// of the 4-wave kernel's thread t % 256 in its activation row block t / 256.
 template <int MODE>
-__global__ __launch_bounds__(256) void gemm_w4_tail_kernel(GArgs a, int per) {
+__global__ __launch_bounds__(1024) void gemm_w4_tail_kernel(GArgs a, int per) {
     using C = W4Cfg<MODE>;
     static_assert(!gated_mode(MODE), "the gated product keeps whole tiles");
+    static_assert(C::TM * 256 == 1024, "one activation row block per 256 threads");
     const int xcd = blockIdx.x / kTailSlots, jt = blockIdx.x % kTailSlots;
     const int nk = a.K / 64;
     const int n_m = a.tiles[a.m_tiles].group;
@@ -1607,7 +1610,7 @@ __global__ __launch_bounds__(256) void gemm_w4_tail_kernel(GArgs a, int per) {
     if (S < 2 || jt >= r_tail) return;
     int mt, nt;
     const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, 256, mt, nt);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x & 255, tm = threadIdx.x >> 8, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const bool hi = lane >= 32;
     const floatx4* P0 = (const floatx4*)a.partial + (size_t)(xcd * kTailSlots + jt * S) * (C::NACC * 4 * 256);
@@ -1615,6 +1618,7 @@ __global__ __launch_bounds__(256) void gemm_w4_tail_kernel(GArgs a, int per) {
         floatx16 v;
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = 0.0f;
+#pragma unroll 2
         for (int p = 0; p < S; ++p) {
             const floatx4* P = P0 + (size_t)p * (C::NACC * 4 * 256);
 #pragma unroll
@@ -1626,13 +1630,12 @@ __global__ __launch_bounds__(256) void gemm_w4_tail_kernel(GArgs a, int per) {
         }
         return v;
     };
-    for (int tm = 0; tm < C::TM; ++tm) {
-        const int row = tl.row0 + wm * C::WM + tm * 32 + (lane & 31);
-        const int crow = row < tl.row_end ? c_row(a.c_rows, a.c_nrows, row) : row;
-        for (int tn = 0; tn < C::TN; ++tn) {
-            const floatx16 g = sum_tile(tm * C::TN + tn);
-            w4_store_tile<MODE>(g, g, row, tl.row_end, crow, nt * C::BNM + wn * C::WNM + tn * 32, a.Nout, (uint8_t*)a.C, hi);
-        }
+    const int row = tl.row0 + wm * C::WM + tm * 32 + (lane & 31);
+    const int crow = row < tl.row_end ? c_row(a.c_rows, a.c_nrows, row) : row;
+#pragma unroll
+    for (int tn = 0; tn < C::TN; ++tn) {
+        const floatx16 g = sum_tile(tm * C::TN + tn);
+        w4_store_tile<MODE>(g, g, row, tl.row_end, crow, nt * C::BNM + wn * C::WNM + tn * 32, a.Nout, (uint8_t*)a.C, hi);
     }
 }
 
@@ -1747,7 +1750,7 @@ static hipError_t run_w4(GArgs g, hipStream_t st) {
     hipError_t err = hipGetLastError();
     if constexpr (!gated_mode(MODE)) {
         if (err == hipSuccess && g.partial) {
-            hipLaunchKernelGGL((gemm_w4_tail_kernel<MODE>), dim3(8 * kTailSlots), dim3(256), 0, st, g, pb / 8);
+            hipLaunchKernelGGL((gemm_w4_tail_kernel<MODE>), dim3(8 * kTailSlots), dim3(1024), 0, st, g, pb / 8);
             err = hipGetLastError();
         }
     }
