@@ -1771,14 +1771,16 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     if (blocks == 0) return hipSuccess;
     const long long b_bytes = (long long)g.Nout * g.K * 2;
     const bool offsets_fit = g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
-    // the 64-wide-stage kernel whenever K allows it (K a multiple of 64, output
-    // rows 16-byte aligned), except for a gated product on 256-row tiles with a
-    // long K, where the ring kernel measured ahead (for the plain long-K products
-    // it measured behind: top-2 down 1.72 -> 1.90 ms, W_o 0.23 -> 0.25 ms)
+    // 256-row tiles with a long K (a multiple of 64): the 4-wave kernel
     if constexpr (BM == 256) {
         if (offsets_fit && g.K % 64 == 0 && g.K >= kW4MinK && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0 && !g.kspan)
             return run_w4<MODE>(g, st);
     }
+    // otherwise the 64-wide-stage kernel whenever K allows it (K a multiple of
+    // 64, output rows 16-byte aligned), except for a gated product on 256-row
+    // tiles with K >= 4096 that the 4-wave kernel does not take, where the ring
+    // kernel measured ahead of it; for the plain long-K products it measured
+    // behind (top-2 down 1.72 -> 1.90 ms, W_o 0.23 -> 0.25 ms)
     const bool ring_first = MODE != MODE_PLAIN && BM == 256 && g.K >= 4096;
     if (!ring_first && offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
         using R = K64Cfg<BM, MODE>;
