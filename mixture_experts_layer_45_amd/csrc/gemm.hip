@@ -15,7 +15,8 @@
 //   * gemm_bf16_w4_kernel -- 256-row tiles with K a multiple of 64 and at least
 //     2048 (the top-2 layer's GEMMs, the shared expert, W_o): persistent, one
 //     wave per SIMD holding a 128 x 128 quarter of the 256 x 256 tile, with a
-//     hand-laid instruction schedule;
+//     hand-laid instruction schedule and the activations loaded two stages
+//     ahead;
 //   * gemm_bf16_k64_kernel  -- other shapes with K a multiple of 64: persistent,
 //     8 waves, BM x 256 tiles, 64-wide k stages of whole 128-byte rows, 16-byte
 //     row stores;
@@ -1287,19 +1288,24 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
 
 
 // ------------------------------------ bf16 MFMA, 4 waves of 128 x 128, 256-row tiles
-// One wave per SIMD (256 threads) on the 256 x 256 block tile of the 64-wide
-// kernel (same LDS stages, swizzle, loads, tile schedule and split tail), each
+// One wave per SIMD (256 threads) on a 256 x 256 block tile (the 64-wide
+// kernel's stage layout, swizzle, loads, schedule order and split tail), each
 // wave owning a 128 x 128 quarter: 16 accumulator tiles (256 registers, all in
 // AGPRs) and, per 16-wide k sub-step, 4 activation and 4 weight fragments for
 // 16 MFMAs -- a third fewer LDS reads per MFMA than the 8-wave kernel's
 // 128 x 64 waves.  With no second wave on the SIMD to cover for it, the wave's
 // instruction stream is laid out by hand (scheduling barriers fix the order):
 // every sub-step reads the next one's 8 fragments behind its first 8 MFMAs;
-// the next stage's 16 buffer-to-LDS loads ride on the first 32 MFMAs, one per
-// two; the stage's wait and block barrier sit before the last 8 MFMAs, which
-// then cover the reads of the next stage's first fragments.  Measured on the
-// top-2 layer's gate/up GEMM: 3.45 -> 3.29-3.34 ms against the ring kernel,
-// with the clock 1.58 -> 1.70 GHz (fewer LDS operations) at the same MFMA count.
+// the loads ride on the stage's first 32 MFMAs, one per two; the stage's wait
+// and block barrier sit before the last 8 MFMAs, which then cover the reads of
+// the next stage's first fragments.  All of LDS holds three stages of
+// activation rows and two of weight rows, so the activations load two stages
+// ahead; with no room left for a claim word, each block takes every 32nd item
+// of its XCD's slice.  Measured on the top-2 layer (gate/up, down): 3.45, 1.72
+// ms on the ring and 64-wide kernels; 3.26-3.32, 1.70-1.76 ms here with two
+// stages of each operand; 3.18-3.24, 1.59-1.61 ms with the activation ring.
+// The clock under the gate/up GEMM rose from 1.58 to 1.70 GHz with the
+// 4-wave layout (fewer LDS operations) at the same MFMA count.
 template <int MODE>
 struct W4Cfg {
     static constexpr int NMAT = gated_mode(MODE) ? 2 : 1;
@@ -1311,8 +1317,8 @@ struct W4Cfg {
     static constexpr int NB = NMAT * TN;    // weight fragments per sub-step
     static constexpr int NACC = TM * NB;    // 32 x 32 accumulator tiles per wave
     static constexpr int NRD = TM + NB;     // fragment reads per sub-step
-    static constexpr int A_BYTES = 256 * 128;
-    static constexpr int STAGE = A_BYTES + 256 * 128;
+    static constexpr int A_BYTES = 256 * 128;  // one stage of activation rows (64 k values each)
+    static constexpr int B_BYTES = 256 * 128;  // one stage of weight rows
     static constexpr int LPW = 16;          // loads per wave per stage (8 activation, 8 weight rows x 8)
     static_assert(NACC == 16 && NRD == 8, "the hand-laid schedule assumes 16 MFMAs and 8 reads per sub-step");
 };
@@ -1402,9 +1408,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = W4Cfg<MODE>;
     constexpr int TM = C::TM, NB = C::NB, NRD = C::NRD;
-    // two stages, then the word for the tile claimed for after the current one
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE + 16];
-    int32_t& next_tile = *(int32_t*)(smem + 2 * C::STAGE);
+    // all of LDS: the activation rows of three stages, then the weight rows of two
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * C::A_BYTES + 2 * C::B_BYTES];
+    constexpr int B_OFF = 3 * C::A_BYTES;
 
     const int K = a.K, Nout = a.Nout;
     const uint32_t rowbytes = (uint32_t)K * 2u;
@@ -1419,14 +1425,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
     tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
     const int n_whole = S > 1 ? Tx - r_tail : Tx;  // items: whole tiles, then S pieces of each tail tile
     const int s_end = n_whole + (S > 1 ? r_tail * S : 0);
-    int s = blockIdx.x >> 3;  // first item static, later ones claimed
+    int s = blockIdx.x >> 3;  // items s, s + per, s + 2 per, ... of the XCD's slice
     if (s >= s_end) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const bool upper = (wu * 64) / C::BNM != 0;  // this wave's weight rows come from B1 (SwiGLU up)
-    const int a_dst = wu * 64 * 128;
-    const int b_dst = C::A_BYTES + wu * 64 * 128;
+    const int a_dst = wu * 64 * 128;  // this wave's 64 rows of a slot
+    const int b_dst = B_OFF + wu * 64 * 128;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, (short)0, (int)a.a_bytes, kBufWord3);
     const int a_nrows = (int)(a.a_bytes / rowbytes);
 
@@ -1472,11 +1478,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
             t.vb[i] = (uint32_t)col * rowbytes + (uint32_t)(c * 16) - 1024u * (i % 4);
         }
     };
-    // load j of stage ks of the tile into slot st: activation rows for j < 8, then weight rows
-    auto ld1 = [&](const Tile& t, int ks, int st, auto J) __attribute__((always_inline)) {
+    // load j of stage ks of the tile: activation rows for j < 8 (into slot
+    // ks % 3), weight rows for j >= 8 (slot ks % 2)
+    auto ld1 = [&](const Tile& t, int ks, auto J) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         constexpr int i = j % 8;
-        uint8_t* dst = smem + st * C::STAGE + (j < 8 ? a_dst : b_dst) + 4096 * (i / 4);
+        uint8_t* dst = smem + (j < 8 ? (ks % 3) * C::A_BYTES + a_dst : (ks % 2) * C::B_BYTES + b_dst) + 4096 * (i / 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 8 ? rA : t.rB, (lds_void_ptr)dst, 16, j < 8 ? t.va[i] : t.vb[i],
                                                  (t.kb + ks) * 128, 1024 * (i % 4), 0);
     };
@@ -1484,24 +1491,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
     // of 32, so its swizzle term ((row / 2) % 8) is lane-constant
     const int xsw = ((lane & 31) >> 1) & 7;
     const uint32_t a_lane = (uint32_t)((wm * C::WM + (lane & 31)) * 128);
-    const uint32_t b_lane = (uint32_t)(C::A_BYTES + (wn * C::WNM + (lane & 31)) * 128);
+    const uint32_t b_lane = (uint32_t)(B_OFF + (wn * C::WNM + (lane & 31)) * 128);
     uint32_t chofs[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) chofs[kk] = (uint32_t)(((kk * 2 + (lane >> 5)) ^ xsw) << 4);
     // read j of sub-step kk, in the order the MFMAs below use them: activation
     // block 0, the NB weight fragments, activation blocks 1..TM-1 (blocks past
     // the tile's rows, tm >= nv, are skipped)
-    auto rd1 = [&](int st, int kk, bf16x8* fr, auto J, auto NV) __attribute__((always_inline)) {
+    // (ks: the k stage, whose activations sit in slot ks % 3 and weights in ks % 2)
+    auto rd1 = [&](int ks, int kk, bf16x8* fr, auto J, auto NV) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value, nv = decltype(NV)::value;
-        const uint32_t base = (uint32_t)(st * C::STAGE) + chofs[kk];
+        const uint32_t abase = (uint32_t)((ks % 3) * C::A_BYTES) + chofs[kk];
+        const uint32_t bbase = (uint32_t)((ks % 2) * C::B_BYTES) + chofs[kk];
         if constexpr (j == 0) {
-            if constexpr (nv > 0) fr[0] = *(const bf16x8*)(smem + (base + a_lane));
+            if constexpr (nv > 0) fr[0] = *(const bf16x8*)(smem + (abase + a_lane));
         } else if constexpr (j <= NB) {
             constexpr int bi = j - 1, m = bi / C::TN, tn = bi % C::TN;
-            fr[TM + bi] = *(const bf16x8*)(smem + (base + b_lane + (m * C::BNM + tn * 32) * 128));
+            fr[TM + bi] = *(const bf16x8*)(smem + (bbase + b_lane + (m * C::BNM + tn * 32) * 128));
         } else {
             constexpr int tm = j - NB;
-            if constexpr (tm < nv) fr[tm] = *(const bf16x8*)(smem + (base + a_lane + tm * 32 * 128));
+            if constexpr (tm < nv) fr[tm] = *(const bf16x8*)(smem + (abase + a_lane + tm * 32 * 128));
         }
     };
     floatx16 acc[C::NACC];
@@ -1513,54 +1522,59 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
         if constexpr (tm < nv) acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[TM + bi], fr[tm], acc[ai], 0, 0, 0);
     };
 
+    // an item's first loads: stage 0's activations and weights, then stage 1's activations
+    auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
+        static_for<C::LPW>([&](auto J) { ld1(t, 0, J); });
+        if (t.nkl > 1) static_for<8>([&](auto J) { ld1(t, 1, J); });
+    };
     Tile cur;
     setup(s, cur);
-    static_for<C::LPW>([&](auto J) { ld1(cur, 0, 0, J); });
+    prologue(cur);
     bf16x8 fa[NRD], fb[NRD];
-    int32_t claim = 0;  // lane 0 of wave 0: the claim counter's answer for the current tile
     while (true) {
 #pragma unroll
         for (int i = 0; i < C::NACC; ++i)
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
-        // claim the block's next item now; the answer is needed only after the k loop
-        if (tid == 0) claim = __hip_atomic_fetch_add(a.claim + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait_vmcnt<0>();  // stage 0 landed (and the last tile's stores)
+        // stage 0 landed (and the last item's stores); stage 1's activations may be in flight
+        if (cur.nkl > 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         auto kloop = [&](auto NV) __attribute__((always_inline)) {
             static_for<NRD>([&](auto J) { rd1(0, 0, fa, J, NV); });
-            // stage kt in MFMA slots p = 16 kk + i: sub-steps on fa, fb, fa, fb
-            auto stage = [&](int kt, auto HN) __attribute__((always_inline)) {
-                constexpr bool hn = decltype(HN)::value;  // a next stage follows
-                const int slot = kt & 1, nslot = slot ^ 1;
+            // stage kt in MFMA slots p = 16 kk + i: sub-steps on fa, fb, fa, fb.
+            // It loads stage kt+1's weights (the slot of stage kt-1, freed by the
+            // last barrier) and then stage kt+2's activations, so that waiting
+            // for stage kt+1 leaves those last 8 loads in flight.
+            auto stage = [&](int kt, auto HN, auto HA) __attribute__((always_inline)) {
+                constexpr bool hn = decltype(HN)::value;  // stage kt+1 exists
+                constexpr bool ha = decltype(HA)::value;  // stage kt+2 exists
                 static_for<64>([&](auto P) {
                     constexpr int p = decltype(P)::value, kk = p / 16, i = p % 16;
                     if constexpr (p == 56) {
-                        if constexpr (hn) {
-                            // this wave's reads of the slot have returned and its loads
-                            // of the next stage have landed
-                            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                            wait_vmcnt<0>();
-                        } else {  // last stage: publish the claimed item
-                            if (tid == 0) next_tile = per + claim;
-                            __builtin_amdgcn_s_waitcnt(0xC07F);
-                        }
+                        // this wave's reads of the stage have returned and its loads of
+                        // stage kt+1 have landed
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                        if constexpr (ha) wait_vmcnt<8>();
+                        else wait_vmcnt<0>();
                         __builtin_amdgcn_s_barrier();
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     mf1(kk % 2 == 0 ? fa : fb, IntC<i>{}, NV);
                     if constexpr (kk < 3) {
-                        if constexpr (i < NRD) rd1(slot, kk + 1, kk % 2 == 0 ? fb : fa, IntC<i>{}, NV);
+                        if constexpr (i < NRD) rd1(kt, kk + 1, kk % 2 == 0 ? fb : fa, IntC<i>{}, NV);
                     } else if constexpr (hn && p >= 56) {
-                        rd1(nslot, 0, fa, IntC<p - 56>{}, NV);
+                        rd1(kt + 1, 0, fa, IntC<p - 56>{}, NV);
                     }
-                    if constexpr (hn && p < 32 && p % 2 == 0) ld1(cur, kt + 1, nslot, IntC<p / 2>{});
+                    if constexpr (hn && p < 16 && p % 2 == 0) ld1(cur, kt + 1, IntC<8 + p / 2>{});
+                    if constexpr (ha && p >= 16 && p < 32 && p % 2 == 0) ld1(cur, kt + 2, IntC<(p - 16) / 2>{});
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
-            const int nk1 = cur.nkl - 1;
-            for (int kt = 0; kt < nk1; ++kt) stage(kt, IntC<1>{});
-            stage(nk1, IntC<0>{});
+            const int nkl = cur.nkl;
+            for (int kt = 0; kt < nkl - 2; ++kt) stage(kt, IntC<1>{}, IntC<1>{});
+            if (nkl >= 2) stage(nkl - 2, IntC<1>{}, IntC<0>{});
+            stage(nkl - 1, IntC<0>{}, IntC<0>{});
         };
         // a ragged last row tile of a group leaves some waves' row blocks empty
         const int nvb = __builtin_amdgcn_readfirstlane(min(max((cur.row_end - cur.row0 - wm * C::WM + 31) / 32, 0), TM));
@@ -1569,13 +1583,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
         else if (nvb == 1) kloop(IntC<1>{});
         else if (nvb == 2) kloop(IntC<2>{});
         else kloop(IntC<3>{});
-        // every slot is free: start the next item's first stage, then store this one
-        const int s_next = __builtin_amdgcn_readfirstlane(next_tile);
+        // every slot is free: start the next item's first stages, then store this one
+        const int s_next = s + per;
         const bool more = s_next < s_end;
         Tile nxt;
         if (more) {
             setup(s_next, nxt);
-            static_for<C::LPW>([&](auto J) { ld1(nxt, 0, 0, J); });
+            prologue(nxt);
         }
         if (cur.slot >= 0)
             w4_store_partial<MODE>(acc, a.partial, cur.slot, tid);
