@@ -123,7 +123,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
     if (tid < 4 * kClaimSets) ((int32_t*)(tiles + max_tiles + 1))[tid] = 0;
 }
 
-constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together
+constexpr int NGROUP = 4;  // consecutive N-tiles that walk the M-tiles together (default width)
 
 struct GArgs {
     const void* A;   // [rows][K]
@@ -150,6 +150,7 @@ struct GArgs {
     const int32_t* krows;
     int lda, ldb;           // row strides in elements (k-major B alone: ldb 0 = Nout)
     long long b_bytes;      // bytes of B the loads may address
+    int ngroup;             // column tiles per schedule group of the persistent kernels (0: NGROUP)
 };
 
 // the A row behind tile row r, clamped to the nrows rows of A
@@ -180,7 +181,7 @@ __device__ __forceinline__ void tail_split(int Tx, int B, int nk, bool enabled, 
     }
 }
 // schedule index -> (row tile, column tile) and the row tile's table entry:
-// groups of NGROUP column tiles, each sweeping every real row tile.  Within a
+// groups of ng column tiles, each sweeping every real row tile.  Within a
 // column group the items of one group's (expert's) ne row tiles are
 // consecutive.  Groups of at most kPairedRows rows run column tile by column
 // tile, so the row tiles that read one weight tile run back to back (measured:
@@ -189,13 +190,19 @@ __device__ __forceinline__ void tail_split(int Tx, int B, int nk, bool enabled, 
 // of the multi-head layer's ~1000-row groups in the other order: 0.73 -> 0.74 ms).
 // tiles[m].pad is the row tile's index within its group, so the group's first
 // tile and tile count follow from any one of its tiles.
+// The group width ng is NGROUP (4) for 256-row tiles.  128-row tiles take all
+// column tiles in one group: each row tile's activations are then fetched by
+// one XCD instead of one per group of 4 column tiles, and the weight tile
+// still reaches its row tiles back to back (the 256-expert layer's down GEMM,
+// 28 column tiles: 1.86 -> 1.75 ms; for 256-row tiles a wider group measured
+// slower: top-2 gate/up 3.18 -> 3.46 ms at 16).
 constexpr int kPairedRows = 512;
 __device__ __forceinline__ GemmTile sched_decode(int si, int n_m, int n_tiles, const GemmTile* tiles, int BM, int& mt,
-                                                 int& nt) {
-    const int gsz = n_m * NGROUP;
+                                                 int& nt, int ng) {
+    const int gsz = n_m * ng;
     const int nb = si / gsz;
     const int rem = si - nb * gsz;
-    const int width = min(NGROUP, n_tiles - nb * NGROUP);
+    const int width = min(ng, n_tiles - nb * ng);
     const int m0 = rem / width;
     const GemmTile t0 = tiles[m0];
     const int f = m0 - t0.pad;  // the group's first row tile
@@ -203,13 +210,14 @@ __device__ __forceinline__ GemmTile sched_decode(int si, int n_m, int n_tiles, c
     if (ne > 1 && ne * BM <= kPairedRows) {
         const int local = rem - width * f;
         mt = f + local % ne;
-        nt = nb * NGROUP + local / ne;
+        nt = nb * ng + local / ne;
         return mt == m0 ? t0 : tiles[mt];
     }
     mt = m0;
-    nt = nb * NGROUP + (rem - m0 * width);
+    nt = nb * ng + (rem - m0 * width);
     return t0;
 }
+__device__ __forceinline__ int sched_width(const GArgs& a) { return a.ngroup > 0 ? a.ngroup : NGROUP; }
 
 
 // block -> (m tile, n tile): blocks are dealt to the 8 XCDs round-robin, so block
@@ -718,7 +726,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_ring8_kernel(GArgs a) {
     // immediate offset 1024*i, so the offset here is reduced by that amount
     auto setup = [&](int si, Tile& t) __attribute__((always_inline)) {
         int mt, nt;
-        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, BM, mt, nt);
+        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, BM, mt, nt, sched_width(a));
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
@@ -987,7 +995,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             t.slot = xcd * kTailSlots + j;
         }
         int mt, nt;
-        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, BM, mt, nt);
+        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, BM, mt, nt, sched_width(a));
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
@@ -1264,7 +1272,7 @@ __global__ __launch_bounds__(512) void gemm_k64_tail_kernel(GArgs a, int per) {
     tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
     if (S < 2 || jt >= r_tail) return;
     int mt, nt;
-    const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, BM, mt, nt);
+    const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, BM, mt, nt, sched_width(a));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     floatx16 acc[C::NACC];
 #pragma unroll
@@ -1458,7 +1466,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
             t.slot = xcd * kTailSlots + j;
         }
         int mt, nt;
-        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, 256, mt, nt);
+        const GemmTile tl = sched_decode(si, n_m, a.n_tiles, a.tiles, 256, mt, nt, sched_width(a));
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
@@ -1623,7 +1631,7 @@ __global__ __launch_bounds__(1024) void gemm_w4_tail_kernel(GArgs a, int per) {
     tail_split(Tx, per, nk, a.partial != nullptr, r_tail, S);
     if (S < 2 || jt >= r_tail) return;
     int mt, nt;
-    const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, 256, mt, nt);
+    const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, 256, mt, nt, sched_width(a));
     const int tid = threadIdx.x & 255, tm = threadIdx.x >> 8, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const bool hi = lane >= 32;
@@ -1799,6 +1807,7 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     if (!ring_first && offsets_fit && g.K % 64 == 0 && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
         using R = K64Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+        if (BM == 128) g.ngroup = g.n_tiles;  // one schedule group per row tile sweep
         const int pb = persistent_blocks();
         hipLaunchKernelGGL((gemm_bf16_k64_kernel<BM, MODE, 0>), dim3(pb), dim3(512), 0, st, g);
         hipError_t err = hipGetLastError();
@@ -1809,6 +1818,7 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     if (g.K % 32 == 0 && offsets_fit && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0) {
         using R = Ring8Cfg<BM, MODE>;
         g.n_tiles = (g.Nout + R::BNM - 1) / R::BNM;
+        if (BM == 128) g.ngroup = g.n_tiles;
         hipLaunchKernelGGL((gemm_bf16_ring8_kernel<BM, MODE>), dim3(persistent_blocks()), dim3(512), 0, st, g);
     } else
         hipLaunchKernelGGL((gemm_bf16_kernel<BM, MODE>), dim3(blocks), dim3(256), 0, st, g);
