@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--shard", action="store_true",
                    help="time the grouped FFN on one GPU's share of the expert/head-parallel layers at their "
                         "real shapes (8 GPUs): prints one line")
+    p.add_argument("--row-major", action="store_true",
+                   help="time the expert weights in their row-major layout (by default the bf16 workloads' "
+                        "expert weights are put in fragment order once, before any timing, with moe_pack_weights)")
     p.add_argument("--counters", action="store_true",
                    help="for rocprofv3 --pmc runs: a 1 GiB device copy (counter calibration), then each "
                         "stage (route, gather permute, GEMM1, GEMM2, combine) three times; prints one line")
@@ -337,6 +340,17 @@ def measure_layer(args, cfg, over, headline):
     stream = torch.cuda.current_stream()
     log(f"[bench] workload {name}: generating inputs on the device")
     inp = inputs.make_inputs(cfg, dev, seed=0)
+    # the expert weights in fragment order (a one-time layout change made when
+    # the weights are loaded, outside every timed region); the training step
+    # reads row-major weights
+    inp_rm = desc_rm = None
+    packed = cfg["dtype"] == "bf16" and not args.row_major and not args.train
+    if packed:
+        if headline:
+            inp_rm, desc_rm = inp, moe.desc_from_cfg(cfg)
+        inp = moe.pack_weights(inp)
+        torch.cuda.synchronize()
+        cfg = dict(cfg, packed=1)
     desc = moe.desc_from_cfg(cfg)
     ws = moe.workspace(desc)
     y = torch.empty((T, h), dtype=inputs.torch_dtype(cfg), device=dev)
@@ -359,7 +373,16 @@ def measure_layer(args, cfg, over, headline):
     ms_step = timed(step, args.steps, stream)
     tok_s = T / (ms_step * 1e-3)
 
-    res = {}
+    res = {"weights": "fragment order (moe_pack_weights)" if packed else "row-major"}
+    if inp_rm is not None:
+        # the same step on the row-major weights, for reference
+        def step_rm():
+            moe.moe_layer_forward(desc_rm, inp_rm, inp_rm["x"], y, aux, ws)
+
+        step_rm()
+        torch.cuda.synchronize()
+        res["row_major_ms_per_step"] = timed(step_rm, args.steps, stream)
+        del inp_rm
     if headline:
         # ---- per-step spread, warm and cache-cold (512 MB written before each step)
         res["warm_per_step"] = spread(per_step(step, args.steps, stream), T)
@@ -406,7 +429,7 @@ def measure_layer(args, cfg, over, headline):
         moe.moe_grouped_ffn_rows(desc, inp["x"], src, offsets, max_rows, inp["w_gate"], inp["w_up"],
                                  inp["w_down"], h_tmp, y_perm, moe.MOE_FFN_GEMM1, ws_f)
 
-    def gemm1_packed():  # the stage-wise path: the same GEMM on the gathered x_perm
+    def gemm1_gathered():  # the stage-wise path: the same GEMM on the gathered x_perm
         moe.moe_grouped_ffn(desc, x_perm, offsets, max_rows, inp["w_gate"], inp["w_up"], inp["w_down"], h_tmp,
                             y_perm, moe.MOE_FFN_GEMM1, ws_f)
 
@@ -463,8 +486,8 @@ def measure_layer(args, cfg, over, headline):
     t_route = timed(route, R, stream)
     t_perm = timed(permute, R, stream)
     t_tables = timed(permute_tables, R, stream)
-    permute()  # leave x_perm and the tables in place for the packed GEMM
-    t_g1_packed = timed(gemm1_packed, R, stream)
+    permute()  # leave x_perm and the tables in place for the gathered-row GEMM
+    t_g1_gathered = timed(gemm1_gathered, R, stream)
     t_g1 = timed(gemm1, R, stream)
     t_g2 = timed(gemm2, R, stream)
     t_comb = timed(combine, R, stream)
@@ -493,7 +516,7 @@ def measure_layer(args, cfg, over, headline):
         "permute_ms": t_perm, "permute_hbm_frac": frac(permute_bytes / (t_perm * 1e-3) / 1e9, HBM_PEAK_GBS),
         "permute_tables_ms": t_tables,
         "gemm1_ms": t_g1, "gemm1_tflops": g1_tfs, "gemm1_mfma_frac": g1_tfs / MFMA_BF16_PEAK_TFS,
-        "gemm1_packed_ms": t_g1_packed,
+        "gemm1_gathered_ms": t_g1_gathered,
         "gemm2_ms": t_g2, "gemm2_tflops": g2_tfs, "gemm2_mfma_frac": g2_tfs / MFMA_BF16_PEAK_TFS,
         "combine_ms": t_comb,
         "combine_hbm_frac": combine_bytes / (t_comb * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -634,7 +657,8 @@ def main():
             st = r["stages"]
             others[wname] = {
                 "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"], "tflops": r["tflops"],
-                "dtype": r["dtype"], "n_kept": r["n_kept"], "nonempty_experts": r["nonempty_experts"],
+                "dtype": r["dtype"], "weights": r["weights"], "n_kept": r["n_kept"],
+                "nonempty_experts": r["nonempty_experts"],
                 "l_aux": r["l_aux"],
                 "ffn_mfma_frac": st["ffn_mfma_frac"], "ffn_attainable_frac": st["ffn_attainable_frac"],
                 "ffn_bound": st["ffn_bound"], "gemm1_mfma_frac": st["gemm1_mfma_frac"],
@@ -648,6 +672,7 @@ def main():
         "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": head["dtype"], "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": head["config"], "tflops": head["tflops"],
+        "weights": head["weights"], "row_major_ms_per_step": head.get("row_major_ms_per_step"),
         "n_kept": head["n_kept"], "n_dropped": head["n_dropped"], "nonempty_experts": head["nonempty_experts"],
         "l_aux": head["l_aux"],
         "warm_per_step": head["warm_per_step"], "cold_per_step": head["cold_per_step"],

@@ -91,6 +91,12 @@ typedef enum { MOE_QUEUE_TOKEN = 0, MOE_QUEUE_CHOICE = 1 } moe_queue;
  *   queue        moe_queue order of each expert's capacity queue
  *   capacity_factor_eval, eval   "HAI-LLM MoE" (train, val) capacity factors:
  *                with eval = 1 the capacity uses capacity_factor_eval.
+ *   packed       1: the expert weights (w_gate, w_up, w_down, the shared
+ *                expert's and w_o) are in the fragment order that
+ *                moe_pack_weights writes; forward entry points only (training
+ *                and the backward pass read row-major weights).  Needs
+ *                MOE_BF16, d and f multiples of 64 and every GEMM operand
+ *                under 2 GB, else MOE_ERR_UNSUPPORTED.
  * Limits: 1 <= K <= E <= 256; h % H == 0; for MOE_BF16, d = h/H and f are
  * multiples of 8 (16-byte rows). */
 typedef struct moe_desc {
@@ -107,6 +113,7 @@ typedef struct moe_desc {
     int32_t queue;       /* moe_queue */
     float capacity_factor_eval;
     int32_t eval;        /* 0: capacity_factor, 1: capacity_factor_eval */
+    int32_t packed;      /* 0: row-major expert weights, 1: fragment order */
 } moe_desc;
 
 /* Flags of moe_route. */
@@ -246,6 +253,23 @@ moe_status moe_grouped_ffn_rows(const moe_desc *desc, const void *x, const int32
                                 const int32_t *offsets, int32_t max_rows, const void *w_gate,
                                 const void *w_up, const void *w_down, void *h_tmp, void *y_perm,
                                 uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert weights in fragment order, for the forward kernels (lesson 10, item
+ * 3: the local experts run as one grouped GEMM; this is the weight layout that
+ * GEMM reads fastest on gfx950).  w holds n_mat bf16 matrices [n_out][k]
+ * (row-major, one after the other, as the expert weights are given);
+ * w_packed receives the same n_mat * n_out * k values, matrix by matrix in
+ * the same order and size, each reordered so that the 8 values one lane
+ * passes to a 32x32x16 MFMA are contiguous: 16-byte piece
+ *   ((nb * k/16 + s) * 64 + l)  of a matrix  =  W[32 nb + l % 32][16 s + 8 (l / 32) + 0..7]
+ * for row block nb < n_out/32, 16-k step s < k/16 and lane l < 64.  Pack
+ * w_gate, w_up and w_down (and sh_*, w_o) once, then pass the packed buffers
+ * with desc->packed = 1.  Both buffers are device memory owned by the caller;
+ * they must be 16-byte aligned and must not overlap.  n_out must be a
+ * positive multiple of 32 and k of 16, else MOE_ERR_INVALID_ARG and nothing
+ * is launched; n_mat = 0 is a no-op.  Asynchronous on `stream`. */
+moe_status moe_pack_weights(const void *w, void *w_packed, int64_t n_mat, int32_t n_out, int32_t k,
+                            void *stream);
 
 /* Gate-weighted unpermute and combine (lesson 10, item 1 output formula and
  * item 3 weighted sum): y[t][g*d + j] = sum over k with dest_row >= 0, in slot

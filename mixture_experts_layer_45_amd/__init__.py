@@ -53,6 +53,7 @@ def desc_from_cfg(cfg, T=None):
         n_groups=int(cfg.get("n_groups", 0)), group_limit=int(cfg.get("group_limit", 0)),
         queue=MOE_QUEUE_CHOICE if cfg.get("queue", "token") == "choice" else MOE_QUEUE_TOKEN,
         capacity_factor_eval=float(cfg.get("capacity_factor_eval", 0.0)), eval=int(cfg.get("eval", 0)),
+        packed=int(cfg.get("packed", 0)),
     )
 
 
@@ -149,6 +150,33 @@ def moe_grouped_ffn_rows(desc, x, src_token, offsets, max_rows, w_gate, w_up, w_
 def moe_combine(desc, dest_row, topk_w, y_perm, y_shared, y, stream=None):
     _check(lib().moe_combine(C.byref(desc), _ptr(dest_row), _ptr(topk_w), _ptr(y_perm), _ptr(y_shared),
                              _ptr(y), _stream(stream)))
+
+
+def moe_pack_weights(w, w_packed, stream=None):
+    """w: bf16 device tensor [..., n_out, k] (a stack of row-major matrices);
+    w_packed: a tensor of the same shape and dtype that receives them in
+    fragment order."""
+    if w.dim() < 2 or w.shape != w_packed.shape or w.dtype != w_packed.dtype:
+        raise ValueError("w and w_packed must have one shape [..., n_out, k] and one dtype")
+    n_out, k = int(w.shape[-2]), int(w.shape[-1])
+    n_mat = w.numel() // (n_out * k) if n_out * k else 0
+    _check(lib().moe_pack_weights(_ptr(w), _ptr(w_packed), int(n_mat), n_out, k, _stream(stream)))
+
+
+# the weights that desc.packed = 1 refers to
+PACKED_KEYS = ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down", "w_o")
+
+
+def pack_weights(weights, stream=None):
+    """A copy of a weights dict with every expert weight of PACKED_KEYS in
+    fragment order (new tensors; the rest shared)."""
+    out = dict(weights)
+    for key in PACKED_KEYS:
+        w = weights.get(key)
+        if w is not None:
+            out[key] = w.new_empty(w.shape)
+            moe_pack_weights(w, out[key], stream)
+    return out
 
 
 _WEIGHT_KEYS = ("w_router", "logit_bias", "select_bias", "w_gate", "w_up", "w_down", "sh_gate",

@@ -30,7 +30,7 @@ class MoeDesc(C.Structure):
         ("dtype", C.c_int32), ("score", C.c_int32), ("act", C.c_int32),
         ("capacity_factor", C.c_float), ("aux_alpha", C.c_float),
         ("gate", C.c_int32), ("n_groups", C.c_int32), ("group_limit", C.c_int32), ("queue", C.c_int32),
-        ("capacity_factor_eval", C.c_float), ("eval", C.c_int32),
+        ("capacity_factor_eval", C.c_float), ("eval", C.c_int32), ("packed", C.c_int32),
     ]
 
 
@@ -79,6 +79,7 @@ SIGNATURES = {
     "moe_grouped_ffn_rows": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, C.c_int32, _VP, _VP, _VP, _VP, _VP,
                                        C.c_uint32, _VP, C.c_size_t, _VP]),
     "moe_combine": (C.c_int, [C.POINTER(MoeDesc), _VP, _VP, _VP, _VP, _VP, _VP]),
+    "moe_pack_weights": (C.c_int, [_VP, _VP, C.c_int64, C.c_int32, C.c_int32, _VP]),
     "moe_layer_forward": (C.c_int, [C.POINTER(MoeDesc), C.POINTER(MoeWeights), _VP, _VP,
                                     C.POINTER(MoeAux), _VP, C.c_size_t, _VP]),
     "moe_max_rows": (C.c_int32, [C.POINTER(MoeDesc)]),

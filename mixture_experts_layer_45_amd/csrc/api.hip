@@ -84,6 +84,20 @@ moe_status check_desc(const moe_desc* d) {
         if ((long)d->group_limit * (d->E / d->n_groups) < d->K)
             return fail(MOE_ERR_INVALID_ARG, "K = %d > group_limit * E / n_groups", d->K);
     }
+    if (d->packed != 0 && d->packed != 1) return fail(MOE_ERR_INVALID_ARG, "packed must be 0 or 1");
+    if (d->packed) {
+        // fragment-ordered weights are read by the 4-wave and 64-wide kernels
+        // alone: bf16, contraction lengths and output widths multiples of 64,
+        // every operand under 2 GB (32-bit buffer offsets)
+        if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights need MOE_BF16");
+        if (dd % 64 || d->f % 64)
+            return fail(MOE_ERR_UNSUPPORTED, "packed weights need d = %d and f = %d to be multiples of 64", dd, d->f);
+        const long long lim = 1ll << 31;
+        const long long f = d->f, h = d->h;
+        if ((long long)d->T * h * 2 >= lim || (long long)d->T * d->H * d->K * f * 2 >= lim || f * dd * 2 >= lim ||
+            (d->n_shared && (f * h * 2 >= lim || (long long)d->T * f * 2 >= lim)) || (d->has_wo && h * h * 2 >= lim))
+            return fail(MOE_ERR_UNSUPPORTED, "packed weights need every GEMM operand under 2 GB");
+    }
     return MOE_OK;
 }
 
@@ -499,6 +513,8 @@ static moe_status grouped_ffn(const moe_desc* d, const void* x_perm, const int32
     if ((fl & MOE_FFN_GEMM1) && (!x_perm || !w_gate || (d->act == MOE_SWIGLU && !w_up)))
         return fail(MOE_ERR_INVALID_ARG, "x_perm, w_gate or w_up is NULL");
     if ((fl & MOE_FFN_GEMM2) && (!w_down || !y_perm)) return fail(MOE_ERR_INVALID_ARG, "w_down or y_perm is NULL");
+    if (d->packed && ((((fl & MOE_FFN_GEMM1) ? (uintptr_t)h_tmp : 0) | ((fl & MOE_FFN_GEMM2) ? (uintptr_t)y_perm : 0)) & 15))
+        return fail(MOE_ERR_INVALID_ARG, "packed weights need h_tmp and y_perm 16-byte aligned");
     Plan q = p;
     q.max_rows = max_rows;
     Carver cm(nullptr);
@@ -509,7 +525,7 @@ static moe_status grouped_ffn(const moe_desc* d, const void* x_perm, const int32
     a.G = p.Et; a.d = p.d; a.f = p.f; a.dtype = d->dtype; a.act = d->act; a.max_rows = max_rows;
     a.x_perm = x_perm; a.offsets = offsets; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
     a.h_tmp = h_tmp; a.y_perm = y_perm; a.flags = fl; a.tiles = carve_ffn(c, q, d->dtype);
-    a.src_rows = src_rows; a.a_nrows = p.T * p.H;
+    a.src_rows = src_rows; a.a_nrows = p.T * p.H; a.packed = d->packed;
     hipError_t e = launch_ffn(a, (hipStream_t)stream);
     if (e != hipSuccess) return dev_fail(e, "grouped ffn kernels");
     return MOE_OK;
@@ -564,6 +580,8 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
     if (d->n_shared && (!w->sh_gate || !w->sh_down || (d->act == MOE_SWIGLU && !w->sh_up)))
         return fail(MOE_ERR_INVALID_ARG, "a shared-expert weight is NULL");
     if (d->has_wo && !w->w_o) return fail(MOE_ERR_INVALID_ARG, "w_o is NULL");
+    if (d->packed && d->has_wo && ((uintptr_t)y & 15))
+        return fail(MOE_ERR_INVALID_ARG, "packed weights with W_o need y 16-byte aligned");
     const size_t need = ws_bytes_of(d, MOE_WS_LAYER);
     if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
 
@@ -643,6 +661,7 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
     fa.act_save = sv ? sv->act_grad : nullptr;
     fa.c_rows = fused_combine ? L.src_token : nullptr;
     fa.c_nrows = p.T;
+    fa.packed = d->packed;
     if ((e = launch_ffn(fa, st)) != hipSuccess) return dev_fail(e, "grouped ffn kernels");
 
     if (d->n_shared) {
@@ -652,6 +671,7 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
         sa.x_perm = x; sa.offsets = L.off_sh; sa.w_gate = w->sh_gate; sa.w_up = w->sh_up;
         sa.w_down = w->sh_down; sa.h_tmp = L.h_sh; sa.y_perm = L.y_sh; sa.flags = 0; sa.tiles = L.tiles_sh;
         sa.act_save = sv ? sv->sh_act_grad : nullptr;
+        sa.packed = d->packed;
         if ((e = launch_ffn(sa, st)) != hipSuccess) return dev_fail(e, "shared expert kernels");
     }
 
@@ -664,7 +684,7 @@ static moe_status layer_forward(const moe_desc* d, const moe_weights* w, const v
         if ((e = launch_combine(ca, st)) != hipSuccess) return dev_fail(e, "combine kernel");
     }
 
-    if (d->has_wo && (e = launch_dense(p.T, p.h, p.h, d->dtype, L.y_cat, w->w_o, y, L.tiles_wo, L.off_wo, st)) != hipSuccess)
+    if (d->has_wo && (e = launch_dense(p.T, p.h, p.h, d->dtype, L.y_cat, w->w_o, y, L.tiles_wo, L.off_wo, st, d->packed)) != hipSuccess)
         return dev_fail(e, "output projection kernel");
 
     if (want_stats) {
@@ -687,6 +707,23 @@ moe_status moe_layer_forward(const moe_desc* d, const moe_weights* w, const void
     return layer_forward(d, w, x, y, aux, nullptr, ws, ws_bytes, stream);
 }
 
+moe_status moe_pack_weights(const void* w, void* w_packed, int64_t n_mat, int32_t n_out, int32_t k, void* stream) {
+    g_err[0] = 0;
+    if (n_mat < 0) return fail(MOE_ERR_INVALID_ARG, "n_mat = %lld < 0", (long long)n_mat);
+    if (n_out <= 0 || n_out % 32 || k <= 0 || k % 16)
+        return fail(MOE_ERR_INVALID_ARG, "n_out = %d must be a positive multiple of 32 and k = %d of 16", n_out, k);
+    if (n_mat == 0) return MOE_OK;
+    if (n_mat > (1ll << 62) / ((long long)n_out * k)) return fail(MOE_ERR_INVALID_ARG, "the matrices are too large");
+    if (!w || !w_packed) return fail(MOE_ERR_INVALID_ARG, "w or w_packed is NULL");
+    const uintptr_t bytes = (uintptr_t)(n_mat * n_out * (long long)k * 2);
+    const uintptr_t a = (uintptr_t)w, b = (uintptr_t)w_packed;
+    if (a < b + bytes && b < a + bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
+    if ((a | b) & 15) return fail(MOE_ERR_INVALID_ARG, "w and w_packed must be 16-byte aligned");
+    hipError_t e = launch_pack_weights(w, w_packed, n_mat, n_out, k, (hipStream_t)stream);
+    if (e != hipSuccess) return dev_fail(e, "pack kernel");
+    return MOE_OK;
+}
+
 int32_t moe_max_rows(const moe_desc* d) {
     if (check_desc(d) != MOE_OK) return -1;
     return plan_of(d).max_rows;
@@ -698,6 +735,7 @@ static moe_status check_training(const moe_desc* d) {
     moe_status s = check_desc(d);
     if (s != MOE_OK) return s;
     if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "training needs MOE_BF16");
+    if (d->packed) return fail(MOE_ERR_UNSUPPORTED, "training reads row-major weights (packed = 0)");
     const int dd = d->h / d->H;
     if (dd % 64 || d->f % 64 || d->h % 64)
         return fail(MOE_ERR_UNSUPPORTED, "training needs d = %d, f = %d and h = %d to be multiples of 64", dd, d->f, d->h);

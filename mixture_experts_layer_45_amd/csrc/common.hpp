@@ -174,6 +174,7 @@ struct FfnArgs {
     void* act_save;   // training: GEMM1 also stores its pre-activations here [max_rows][n_act*f], or null
     const int32_t* c_rows;  // null, or row i of GEMM2 is stored to row c_rows[i] of y_perm (clamped to [0, c_nrows))
     int c_nrows;
+    int packed;             // 1: w_gate, w_up, w_down in the fragment order of moe_pack_weights
 };
 size_t ffn_workspace_bytes(int G, int max_rows, int dtype);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t st);
@@ -210,7 +211,9 @@ hipError_t launch_grouped_gemm(int mode, const GemmSpec& s, const int32_t* offse
                                GemmTile* tiles, hipStream_t st, int bm = 0);
 // Dense GEMM y[rows][n] = x[rows][k] W^T with W [n][k] (one group; used for W_o).
 hipError_t launch_dense(int rows, int k, int n, int dtype, const void* x, const void* w, void* y,
-                        GemmTile* tiles, int32_t* offsets2, hipStream_t st);
+                        GemmTile* tiles, int32_t* offsets2, hipStream_t st, int packed = 0);
+// n_mat bf16 matrices [n_out][k] (n_out % 32 == 0, k % 16 == 0) into fragment order
+hipError_t launch_pack_weights(const void* w, void* out, long long n_mat, int n_out, int k, hipStream_t st);
 
 struct CombineArgs {
     int T, H, K, d, h, dtype;

@@ -96,6 +96,10 @@ def _desc(**over):
     (dict(gate="hash", K=1, n_groups=2, group_limit=1), _ffi.MOE_ERR_INVALID_ARG),
     (dict(eval=2), _ffi.MOE_ERR_INVALID_ARG),
     (dict(capacity_factor_eval=float("nan")), _ffi.MOE_ERR_INVALID_ARG),
+    (dict(packed=2), _ffi.MOE_ERR_INVALID_ARG),
+    (dict(packed=1), _ffi.MOE_ERR_UNSUPPORTED),                        # fp32
+    (dict(packed=1, dtype="bf16", f=96), _ffi.MOE_ERR_UNSUPPORTED),    # f % 64
+    (dict(packed=1, dtype="bf16", H=2, h=64), _ffi.MOE_ERR_UNSUPPORTED),  # d = 32
 ])
 def test_bad_descriptors_are_rejected(over, status):
     d = _desc(**over)
@@ -130,6 +134,30 @@ def test_stage_calls_validate_before_launch():
     one = C.c_void_p(4096)
     assert L.moe_permute(C.byref(d), one, None, 4, one, one, one, one, one, None, None, fake, 8, None) == 3
     assert L.moe_permute(C.byref(d), one, None, 4, one, one, one, one, one, None, None, None, 0, None) == 3
+
+
+def test_pack_weights_validates_before_launch():
+    L = _ffi.lib()
+    a, b = C.c_void_p(1 << 20), C.c_void_p(1 << 30)
+    assert L.moe_pack_weights(a, b, 2, 48, 64, None) == 1  # n_out % 32
+    assert L.moe_pack_weights(a, b, 2, 64, 24, None) == 1  # k % 16
+    assert L.moe_pack_weights(a, b, -1, 64, 64, None) == 1
+    assert L.moe_pack_weights(None, b, 2, 64, 64, None) == 1
+    assert L.moe_pack_weights(a, C.c_void_p((1 << 20) + 4096), 2, 64, 64, None) == 1  # 16 KB each: overlap
+    assert "overlap" in L.moe_last_error().decode()
+    assert L.moe_pack_weights(C.c_void_p((1 << 20) + 8), b, 2, 64, 64, None) == 1
+    assert "aligned" in L.moe_last_error().decode()
+    assert L.moe_pack_weights(None, None, 0, 64, 64, None) == 0  # nothing to pack
+    # packed weights are for the forward entry points; training refuses them
+    d = _desc(packed=1, dtype="bf16")
+    assert moe.moe_capacity(d) > 0
+    W = _ffi.MoeWeights()
+    assert L.moe_layer_forward_train(C.byref(d), C.byref(W), None, None, None, None, None, 0, None) == 2
+    assert "row-major" in L.moe_last_error().decode()
+    # the packed GEMM epilogues store 16-byte rows: misaligned outputs are refused
+    one, odd = C.c_void_p(4096), C.c_void_p(4096 + 4)
+    assert L.moe_grouped_ffn(C.byref(d), one, one, 16, one, one, one, odd, one, 0, None, 0, None) == 1
+    assert "aligned" in L.moe_last_error().decode()
 
 
 def test_permute_noalloc_validates_before_launch():
