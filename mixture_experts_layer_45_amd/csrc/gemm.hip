@@ -1656,18 +1656,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
 // weight fragment a wave multiplies is 1 KB of consecutive bytes, so the waves
 // load their weight fragments straight into registers, three sub-steps (48
 // MFMAs) ahead in a ring of four, and LDS holds the activation rows alone
-// (three stages, loaded two stages ahead as in the kernel above).  Each weight
-// fragment is then read by the two waves that share its columns (from L2)
-// instead of once into LDS, and LDS traffic per stage drops from 192 to 96
-// KB.  The MFMAs see the same operands in the same order as on row-major
-// weights, so both kernels give the same bits.  Measured on the top-2 layer:
-// gate/up 3.17 -> 3.13 ms, down 1.62 -> 1.59 ms.
+// (four stages, loaded three stages ahead).  Each weight fragment is then
+// read by the two waves that share its columns (from L2) instead of once into
+// LDS, and LDS traffic per stage drops from 192 to 96 KB.  The MFMAs see the
+// same operands in the same order as on row-major weights, so both kernels
+// give the same bits.  Measured on the top-2 layer: gate/up 3.17 -> 3.07 ms,
+// down 1.62 -> 1.56 ms.
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = W4Cfg<MODE>;
     constexpr int TM = C::TM, NB = C::NB;
-    constexpr int NAS = 3;  // activation stages in LDS
+    // activation stages in LDS, loaded NAS - 1 stages ahead (top-2 layer, one
+    // box: 3 stages 4.78 ms, 4 stages 4.72 ms, 5 stages 4.84 ms)
+    constexpr int NAS = 4;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NAS * C::A_BYTES];
 
     const int K = a.K, Nout = a.Nout;
@@ -1773,11 +1775,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
             acc[ai] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bcur[bi]), fr[tm], acc[ai], 0, 0, 0);
     };
     // an item's first loads: stage 0's activations, the weights of its first
-    // three sub-steps, stage 1's activations
+    // three sub-steps, the activations of stages 1 .. NAS - 2
     auto prologue = [&](const Tile& t) __attribute__((always_inline)) {
         static_for<8>([&](auto J) { lda1(t, 0, J); });
         static_for<3>([&](auto G) { static_for<NB>([&](auto B) { ldb1(t, decltype(G)::value, bR[decltype(G)::value], B); }); });
-        if (t.nkl > 1) static_for<8>([&](auto J) { lda1(t, 1, J); });
+        static_for<NAS - 2>([&](auto S) {
+            constexpr int st = decltype(S)::value + 1;
+            if (st < t.nkl) static_for<8>([&](auto J) { lda1(t, st, J); });
+        });
     };
     Tile cur;
     setup(s, cur);
@@ -1789,10 +1794,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
         // stage 0's activations landed (the weights of its first three sub-steps
-        // and stage 1's activations may still be in flight; the compiler waits
-        // for each weight register before its first MFMA)
-        if (cur.nkl > 1) wait_vmcnt<20>();
-        else wait_vmcnt<12>();
+        // and the later stages' activations may still be in flight; the compiler
+        // waits for each weight register before its first MFMA)
+        static_assert(NAS == 4, "the waits below count 12 weight and 8 activation loads per stage");
+        {
+            const int ahead = min(NAS - 2, cur.nkl - 1);  // activation stages loaded after stage 0's weights
+            if (ahead >= 2) wait_vmcnt<28>();
+            else if (ahead == 1) wait_vmcnt<20>();
+            else wait_vmcnt<12>();
+        }
         __builtin_amdgcn_s_barrier();
         auto kloop = [&](auto NV) __attribute__((always_inline)) {
             static_for<TM>([&](auto J) { rda(0, 0, fa, J, NV); });
@@ -1804,7 +1814,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
                     if constexpr (p == 56) {
                         // own LDS reads done; stage kt+1's activations landed (they were
                         // issued before this stage's last weight loads, which this
-                        // stage has already waited for)
+                        // stage has already waited for); ha: stage kt + NAS - 1 exists
                         __builtin_amdgcn_s_waitcnt(0xC07F);
                         wait_vmcnt<(ha ? 8 : 0) + (hn ? 8 : 0)>();
                         __builtin_amdgcn_s_barrier();
@@ -1816,7 +1826,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
                     } else if constexpr (hn && p >= 56 && p < 56 + TM) {
                         rda(kt + 1, 0, fa, IntC<p - 56>{}, NV);
                     }
-                    if constexpr (ha && p >= 16 && p < 32 && p % 2 == 0) lda1(cur, kt + 2, IntC<(p - 16) / 2>{});
+                    if constexpr (ha && p >= 16 && p < 32 && p % 2 == 0) lda1(cur, kt + NAS - 1, IntC<(p - 16) / 2>{});
                     // sub-step kk loads the weights of sub-step kk + 3
                     if constexpr (i >= 8 && i % 2 == 0 && (kk == 0 || hn))
                         ldb1(cur, 4 * kt + kk + 3, bR[(kk + 3) % 4], IntC<(i - 8) / 2>{});
@@ -1824,8 +1834,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
                 });
             };
             const int nkl = cur.nkl;
-            for (int kt = 0; kt < nkl - 2; ++kt) stage(kt, IntC<1>{}, IntC<1>{});
-            if (nkl >= 2) stage(nkl - 2, IntC<1>{}, IntC<0>{});
+            int kt = 0;
+            for (; kt < nkl - (NAS - 1); ++kt) stage(kt, IntC<1>{}, IntC<1>{});
+            for (; kt < nkl - 1; ++kt) stage(kt, IntC<1>{}, IntC<0>{});
             stage(nkl - 1, IntC<0>{}, IntC<0>{});
         };
         const int nvb = __builtin_amdgcn_readfirstlane(min(max((cur.row_end - cur.row0 - wm * C::WM + 31) / 32, 0), TM));
