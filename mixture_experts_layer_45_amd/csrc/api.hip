@@ -713,11 +713,11 @@ moe_status moe_pack_weights(const void* w, void* w_packed, int64_t n_mat, int32_
     if (n_out <= 0 || n_out % 32 || k <= 0 || k % 16)
         return fail(MOE_ERR_INVALID_ARG, "n_out = %d must be a positive multiple of 32 and k = %d of 16", n_out, k);
     if (n_mat == 0) return MOE_OK;
-    if (n_mat > (1ll << 62) / ((long long)n_out * k)) return fail(MOE_ERR_INVALID_ARG, "the matrices are too large");
+    if (n_mat > (1ll << 60) / ((long long)n_out * k)) return fail(MOE_ERR_INVALID_ARG, "the matrices are too large");
     if (!w || !w_packed) return fail(MOE_ERR_INVALID_ARG, "w or w_packed is NULL");
-    const uintptr_t bytes = (uintptr_t)(n_mat * n_out * (long long)k * 2);
+    const uintptr_t bytes = (uintptr_t)n_mat * (uintptr_t)n_out * (uintptr_t)k * 2u;
     const uintptr_t a = (uintptr_t)w, b = (uintptr_t)w_packed;
-    if (a < b + bytes && b < a + bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
+    if ((a < b ? b - a : a - b) < bytes) return fail(MOE_ERR_INVALID_ARG, "w and w_packed overlap");
     if ((a | b) & 15) return fail(MOE_ERR_INVALID_ARG, "w and w_packed must be 16-byte aligned");
     hipError_t e = launch_pack_weights(w, w_packed, n_mat, n_out, k, (hipStream_t)stream);
     if (e != hipSuccess) return dev_fail(e, "pack kernel");
