@@ -116,3 +116,22 @@ def test_packed_layer_forward_is_bitwise_row_major(case):
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     for k in ("topk_idx", "dest_row", "counts", "kept", "n_kept"):
         assert torch.equal(aux0[k], aux1[k]), k
+
+
+@pytest.mark.parametrize("name", ["top2_e8_h4096", "sigmoid_top8_e256_shared", "switch_top1_e64_zipf",
+                                  "multihead_h8_e32_top4"])
+def test_packed_layer_full_size_is_bitwise_row_major(name):
+    """The bf16 workloads at their full sizes, on the weights bench.py times
+    (fragment order), against the same layer on row-major weights, which
+    test_layer_full_size_sampled holds to the oracle."""
+    cfg = inputs.CONFIGS[name]
+    G.log(f"[packed layer full] {name}: generating inputs on the device")
+    inp = inputs.make_inputs(cfg, G.DEV)
+    y0, aux0 = G.run_layer(cfg, inp)
+    packed = moe.pack_weights(inp)
+    y1, aux1 = G.run_layer(dict(cfg, packed=1), packed)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    for k in ("topk_idx", "dest_row", "counts", "kept", "n_kept"):
+        assert torch.equal(aux0[k], aux1[k]), k
+    del inp, packed
+    torch.cuda.empty_cache()
