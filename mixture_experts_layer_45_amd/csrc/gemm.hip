@@ -477,8 +477,11 @@ constexpr int kBufWord3 = 0x00020000;
 // N buffer loads into consecutive 1 KB LDS runs sharing one M0 value: load i
 // carries immediate offset 1024*i (a compile-time constant, as the instruction
 // requires), which moves both its global and its LDS address.
+// N loads on one LDS base, load i with immediate offset 1024 i (the offset
+// field holds 12 bits, so at most four)
 template <int N>
 struct LdsRun {
+    static_assert(N <= 4, "immediate offsets above 4095 do not encode");
     static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t r, lds_void_ptr lds, const uint32_t* v, int soff) {
         LdsRun<N - 1>::go(r, lds, v, soff);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, v[N - 1], soff, (N - 1) * 1024, 0);
