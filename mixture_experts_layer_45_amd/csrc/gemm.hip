@@ -1223,8 +1223,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
     // dependent global loads) during stage 1 of the current one, so that its
     // first loads go out as soon as the k loop ends (the multi-head layer's
     // K = 512 gate/up GEMM: 0.68 -> 0.66 ms); 128-row tiles do it after the k
-    // loop (early: the 256-expert gate/up GEMM 3.17 -> 3.19 ms)
-    constexpr bool kEarly = BM == 256;
+    // loop (early: the 256-expert gate/up GEMM 3.17 -> 3.19 ms), and so do the
+    // training and backward modes, whose 256-row variants would then spill
+    constexpr bool kEarly = BM == 256 && KM == 0 && MODE <= MODE_PLAIN;
     Tile nxt;
     int s_next = s_end;
     bool more = false;
