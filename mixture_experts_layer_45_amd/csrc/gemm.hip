@@ -478,17 +478,19 @@ constexpr int kBufWord3 = 0x00020000;
 // carries immediate offset 1024*i (a compile-time constant, as the instruction
 // requires), which moves both its global and its LDS address.
 // N loads on one LDS base, load i with immediate offset 1024 i (the offset
-// field holds 12 bits, so at most four)
-template <int N>
+// field holds 12 bits, so at most four); AUX: the loads' cache-policy bits
+// (kCpolNT: non-temporal)
+constexpr int kCpolNT = 2;
+template <int N, int AUX = 0>
 struct LdsRun {
     static_assert(N <= 4, "immediate offsets above 4095 do not encode");
     static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t r, lds_void_ptr lds, const uint32_t* v, int soff) {
-        LdsRun<N - 1>::go(r, lds, v, soff);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, v[N - 1], soff, (N - 1) * 1024, 0);
+        LdsRun<N - 1, AUX>::go(r, lds, v, soff);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, v[N - 1], soff, (N - 1) * 1024, AUX);
     }
 };
-template <>
-struct LdsRun<0> {
+template <int AUX>
+struct LdsRun<0, AUX> {
     static __device__ __forceinline__ void go(__amdgpu_buffer_rsrc_t, lds_void_ptr, const uint32_t*, int) {}
 };
 
@@ -987,6 +989,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         int row0, row_end, n0;
         int kb, nkl, slot;  // first k stage (KM = 2: first k row), k stages, partial slot (-1: a whole tile)
         int kend;           // KM = 2: the group's end row
+        bool once;          // PK: the tile's group has one row tile, so its weights are read once
         __amdgpu_buffer_rsrc_t rB, rB1;
         uint32_t va[C::A_PW], vb[C::B_PW];
     };
@@ -1010,6 +1013,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
         t.row0 = tl.row0;
         t.row_end = tl.row_end;
         t.n0 = nt * C::BNM;
+        t.once = tl.row_end - (tl.row0 - tl.pad * BM) <= BM;
         if (a.kspan) {  // the group's own k range (no split pieces are made then)
             const int2 ks = a.kspan[tl.group];
             t.kb = ks.x;
@@ -1120,6 +1124,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_k64_kernel(GArgs a) {
             const int k0 = (t.kb + ks) * 64;
             if (k0 >= kmat) LdsRun<C::B_PW>::go(t.rB1, dst, t.vb, (int)((uint32_t)(k0 - kmat) * ldb));
             else LdsRun<C::B_PW>::go(t.rB, dst, t.vb, (int)((uint32_t)k0 * ldb));
+        } else if constexpr (PK) {
+            // weights that no other tile reads stream past L2 (non-temporal), so
+            // the activation rows that the group's column tiles share stay in it
+            // (the 256-expert layer 5.32 -> 5.25 ms, the Zipf top-1 layer's expert
+            // GEMMs 0.100 -> 0.085 and 0.103 -> 0.092 ms; non-temporal weights for
+            // groups of two row tiles, which read each weight tile twice: 256-expert
+            // layer 5.72 ms)
+            if (t.once) LdsRun<C::B_PW, kCpolNT>::go(t.rB, dst, t.vb, (t.kb + ks) * bstage);
+            else LdsRun<C::B_PW>::go(t.rB, dst, t.vb, (t.kb + ks) * bstage);
         } else {
             LdsRun<C::B_PW>::go(t.rB, dst, t.vb, (t.kb + ks) * bstage);
         }
