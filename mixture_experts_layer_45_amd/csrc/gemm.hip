@@ -1386,7 +1386,29 @@ struct W4Cfg {
     static constexpr int A_BYTES = 256 * 128;  // one stage of activation rows (64 k values each)
     static constexpr int B_BYTES = 256 * 128;  // one stage of weight rows
     static constexpr int LPW = 16;          // loads per wave per stage (8 activation, 8 weight rows x 8)
+    static constexpr int WN = 2;           // waves along the weight rows (2 x 2)
     static_assert(NACC == 16 && NRD == 8, "the hand-laid schedule assumes 16 MFMAs and 8 reads per sub-step");
+};
+
+// The fragment-order kernel's waves: 1 x 4, each wave all 256 rows of the
+// tile and a quarter of its weight rows (gated: 32 gate and the same 32 up
+// columns), so no two waves load the same weight fragment.  Per sub-step a
+// wave reads 8 activation fragments from LDS and takes 2 weight fragments
+// from registers for its 16 MFMAs.
+template <int MODE>
+struct W4PCfg {
+    static constexpr int NMAT = gated_mode(MODE) ? 2 : 1;
+    static constexpr int BNM = gated_mode(MODE) ? 128 : 256;  // output columns per matrix
+    static constexpr int WM = 256;
+    static constexpr int WNM = BNM / 4;
+    static constexpr int TM = WM / 32;
+    static constexpr int TN = WNM / 32;
+    static constexpr int NB = NMAT * TN;  // weight fragments per sub-step
+    static constexpr int NACC = TM * NB;
+    static constexpr int NRD = TM + NB;
+    static constexpr int A_BYTES = 256 * 128;
+    static constexpr int WN = 4;          // waves along the weight rows
+    static_assert(NACC == 16 && NB == 2, "16 MFMAs and 2 weight fragments per sub-step");
 };
 
 template <typename F, int... Is>
@@ -1429,10 +1451,10 @@ __device__ __forceinline__ void w4_store_tile(floatx16 g, const floatx16& u, int
 // (an empty asm with an "a" operand) right before it is copied out: otherwise
 // the compiler copies all 256 accumulators to VGPRs at the end of the k loop
 // and spills.
-template <int MODE>
-__device__ __forceinline__ void w4_epilogue(const floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
-                                            int wm, int wn, int lane, const int32_t* c_rows, int c_nrows) {
-    using C = W4Cfg<MODE>;
+template <typename C, int MODE>
+__device__ __forceinline__ void w4_epilogue_cfg(const floatx16* acc, int row0, int row_end, int n0, int Nout,
+                                                uint8_t* Cp, int wm, int wn, int lane, const int32_t* c_rows,
+                                                int c_nrows) {
     const bool hi = lane >= 32;
 #pragma clang loop unroll(full)
     for (int tm = 0; tm < C::TM; ++tm) {
@@ -1451,6 +1473,12 @@ __device__ __forceinline__ void w4_epilogue(const floatx16* acc, int row0, int r
             }
         }
     }
+}
+
+template <int MODE>
+__device__ __forceinline__ void w4_epilogue(const floatx16* acc, int row0, int row_end, int n0, int Nout, uint8_t* Cp,
+                                            int wm, int wn, int lane, const int32_t* c_rows, int c_nrows) {
+    w4_epilogue_cfg<W4Cfg<MODE>, MODE>(acc, row0, row_end, n0, Nout, Cp, wm, wn, lane, c_rows, c_nrows);
 }
 
 // fp32 partial tile of one piece: accumulator (ai, 4q..4q+3) of thread tid at
@@ -1673,16 +1701,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GArgs a) {
 // weight fragment a wave multiplies is 1 KB of consecutive bytes, so the waves
 // load their weight fragments straight into registers, three sub-steps (48
 // MFMAs) ahead in a ring of four, and LDS holds the activation rows alone
-// (four stages, loaded three stages ahead).  Each weight fragment is then
-// read by the two waves that share its columns (from L2) instead of once into
-// LDS, and LDS traffic per stage drops from 192 to 96 KB.  The MFMAs see the
-// same operands in the same order as on row-major weights, so both kernels
-// give the same bits.  Measured on the top-2 layer: gate/up 3.17 -> 3.07 ms,
-// down 1.62 -> 1.56 ms.
+// (four stages, loaded three stages ahead).  The waves are laid 1 x 4 (each
+// all 256 rows and a quarter of the weight rows, W4PCfg), so every weight
+// fragment is loaded by one wave.  Every output still sums the same products
+// in the same k order as on row-major weights, so both kernels give the same
+// bits.  Measured on the top-2 layer: gate/up 3.17 -> 3.07 ms and down 1.62 ->
+// 1.56 ms with 2 x 2 waves (each weight fragment loaded by two), then 3.10 ->
+// 3.02 ms and 1.56 -> 1.52 ms with 1 x 4.
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    using C = W4Cfg<MODE>;
+    using C = W4PCfg<MODE>;
     constexpr int TM = C::TM, NB = C::NB;
     // activation stages in LDS, loaded NAS - 1 stages ahead (top-2 layer, one
     // box: 3 stages 4.78 ms, 4 stages 4.72 ms, 5 stages 4.84 ms)
@@ -1706,7 +1735,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
     int s = blockIdx.x >> 3;
     if (s >= s_end) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = 0, wn = wave;  // 1 x 4 waves
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int a_dst = wu * 64 * 128;
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, (short)0, (int)a.a_bytes, kBufWord3);
@@ -1813,12 +1842,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
         // stage 0's activations landed (the weights of its first three sub-steps
         // and the later stages' activations may still be in flight; the compiler
         // waits for each weight register before its first MFMA)
-        static_assert(NAS == 4, "the waits below count 12 weight and 8 activation loads per stage");
+        static_assert(NAS == 4, "the waits below count 3 NB weight and 8 activation loads per stage");
         {
             const int ahead = min(NAS - 2, cur.nkl - 1);  // activation stages loaded after stage 0's weights
-            if (ahead >= 2) wait_vmcnt<28>();
-            else if (ahead == 1) wait_vmcnt<20>();
-            else wait_vmcnt<12>();
+            if (ahead >= 2) wait_vmcnt<3 * NB + 16>();
+            else if (ahead == 1) wait_vmcnt<3 * NB + 8>();
+            else wait_vmcnt<3 * NB>();
         }
         __builtin_amdgcn_s_barrier();
         auto kloop = [&](auto NV) __attribute__((always_inline)) {
@@ -1833,7 +1862,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
                         // issued before this stage's last weight loads, which this
                         // stage has already waited for); ha: stage kt + NAS - 1 exists
                         __builtin_amdgcn_s_waitcnt(0xC07F);
-                        wait_vmcnt<(ha ? 8 : 0) + (hn ? 8 : 0)>();
+                        wait_vmcnt<(ha ? 8 : 0) + (hn ? 2 * NB : 0)>();
                         __builtin_amdgcn_s_barrier();
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -1845,7 +1874,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
                     }
                     if constexpr (ha && p >= 16 && p < 32 && p % 2 == 0) lda1(cur, kt + NAS - 1, IntC<(p - 16) / 2>{});
                     // sub-step kk loads the weights of sub-step kk + 3
-                    if constexpr (i >= 8 && i % 2 == 0 && (kk == 0 || hn))
+                    if constexpr (i >= 8 && i % 2 == 0 && (i - 8) / 2 < NB && (kk == 0 || hn))
                         ldb1(cur, 4 * kt + kk + 3, bR[(kk + 3) % 4], IntC<(i - 8) / 2>{});
                     __builtin_amdgcn_sched_barrier(0);
                 });
@@ -1857,11 +1886,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
             stage(nkl - 1, IntC<0>{}, IntC<0>{});
         };
         const int nvb = __builtin_amdgcn_readfirstlane(min(max((cur.row_end - cur.row0 - wm * C::WM + 31) / 32, 0), TM));
+        static_assert(TM == 8, "row-block counts 0..8");
         if (nvb == TM) kloop(IntC<TM>{});
         else if (nvb == 0) kloop(IntC<0>{});
         else if (nvb == 1) kloop(IntC<1>{});
         else if (nvb == 2) kloop(IntC<2>{});
-        else kloop(IntC<3>{});
+        else if (nvb == 3) kloop(IntC<3>{});
+        else if (nvb == 4) kloop(IntC<4>{});
+        else if (nvb == 5) kloop(IntC<5>{});
+        else if (nvb == 6) kloop(IntC<6>{});
+        else kloop(IntC<7>{});
         const int s_next = s + per;
         const bool more = s_next < s_end;
         Tile nxt;
@@ -1870,9 +1904,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
             prologue(nxt);
         }
         if (cur.slot >= 0)
-            w4_store_partial<MODE>(acc, a.partial, cur.slot, tid);
+            w4_store_partial<MODE>(acc, a.partial, cur.slot, tid);  // the same slot layout (NACC = 16)
         else
-            w4_epilogue<MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane, a.c_rows, a.c_nrows);
+            w4_epilogue_cfg<C, MODE>(acc, cur.row0, cur.row_end, cur.n0, Nout, (uint8_t*)a.C, wm, wn, lane, a.c_rows,
+                                     a.c_nrows);
         if (!more) break;
         cur = nxt;
         s = s_next;
@@ -1881,15 +1916,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4p_kernel(GArgs a) {
 #endif
 }
 
-// The split tail tiles of the 4-wave kernel (ungated products: the gated one
+// The split tail tiles of the 4-wave kernels (ungated products: the gated one
 // is never split): each (XCD, tail tile) block sums the tile's pieces in piece
 // order and runs the epilogue.  1024 threads: thread t takes the accumulators
-// of the 4-wave kernel's thread t % 256 in its activation row block t / 256.
-template <int MODE>
+// of the 4-wave kernel's thread t % 256 in its activation row blocks
+// RB (t / 256) .. RB (t / 256) + RB - 1, RB = TM / 4 (C: that kernel's waves).
+template <int MODE, typename C = W4Cfg<MODE>>
 __global__ __launch_bounds__(1024) void gemm_w4_tail_kernel(GArgs a, int per) {
-    using C = W4Cfg<MODE>;
     static_assert(!gated_mode(MODE), "the gated product keeps whole tiles");
-    static_assert(C::TM * 256 == 1024, "one activation row block per 256 threads");
+    constexpr int RB = C::TM / 4;
+    static_assert(RB * 4 == C::TM, "the row blocks split evenly over four thread groups");
     const int xcd = blockIdx.x / kTailSlots, jt = blockIdx.x % kTailSlots;
     const int nk = a.K / 64;
     const int n_m = a.tiles[a.m_tiles].group;
@@ -1902,8 +1938,8 @@ __global__ __launch_bounds__(1024) void gemm_w4_tail_kernel(GArgs a, int per) {
     if (S < 2 || jt >= r_tail) return;
     int mt, nt;
     const GemmTile tl = sched_decode(tx0 + Tx - r_tail + jt, n_m, a.n_tiles, a.tiles, 256, mt, nt, sched_width(a));
-    const int tid = threadIdx.x & 255, tm = threadIdx.x >> 8, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x & 255, grp = threadIdx.x >> 8, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const bool hi = lane >= 32;
     const floatx4* P0 = (const floatx4*)a.partial + (size_t)(xcd * kTailSlots + jt * S) * (C::NACC * 4 * 256);
     auto sum_tile = [&](int ai) {
@@ -1922,12 +1958,17 @@ __global__ __launch_bounds__(1024) void gemm_w4_tail_kernel(GArgs a, int per) {
         }
         return v;
     };
-    const int row = tl.row0 + wm * C::WM + tm * 32 + (lane & 31);
-    const int crow = row < tl.row_end ? c_row(a.c_rows, a.c_nrows, row) : row;
 #pragma unroll
-    for (int tn = 0; tn < C::TN; ++tn) {
-        const floatx16 g = sum_tile(tm * C::TN + tn);
-        w4_store_tile<MODE>(g, g, row, tl.row_end, crow, nt * C::BNM + wn * C::WNM + tn * 32, a.Nout, (uint8_t*)a.C, hi);
+    for (int r = 0; r < RB; ++r) {
+        const int tm = grp * RB + r;
+        const int row = tl.row0 + wm * C::WM + tm * 32 + (lane & 31);
+        const int crow = row < tl.row_end ? c_row(a.c_rows, a.c_nrows, row) : row;
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+            const floatx16 g = sum_tile(tm * C::TN + tn);
+            w4_store_tile<MODE>(g, g, row, tl.row_end, crow, nt * C::BNM + wn * C::WNM + tn * 32, a.Nout, (uint8_t*)a.C,
+                                hi);
+        }
     }
 }
 
@@ -2045,7 +2086,11 @@ static hipError_t run_w4(GArgs g, hipStream_t st) {
     hipError_t err = hipGetLastError();
     if constexpr (!gated_mode(MODE)) {
         if (err == hipSuccess && g.partial) {
-            hipLaunchKernelGGL((gemm_w4_tail_kernel<MODE>), dim3(8 * kTailSlots), dim3(1024), 0, st, g, pb / 8);
+            if (g.b_packed)
+                hipLaunchKernelGGL((gemm_w4_tail_kernel<MODE, W4PCfg<MODE>>), dim3(8 * kTailSlots), dim3(1024), 0, st,
+                                   g, pb / 8);
+            else
+                hipLaunchKernelGGL((gemm_w4_tail_kernel<MODE>), dim3(8 * kTailSlots), dim3(1024), 0, st, g, pb / 8);
             err = hipGetLastError();
         }
     }
