@@ -2100,6 +2100,12 @@ static hipError_t run_w4(GArgs g, hipStream_t st) {
 // tile's first stage and epilogue, which short-K tiles repeat often (the
 // multi-head layer's K = 512 gate/up GEMM: 0.75 -> 0.80 ms on it)
 constexpr int kW4MinK = 2048;
+// the fragment-order kernel (weights in registers, four activation stages)
+// from K = 1024 for the ungated products: the multi-head layer's down GEMM
+// 0.34 -> 0.325 ms (at K = 512 its gate/up GEMM went 0.66 -> 0.71 ms).  Gated
+// products keep the 64-wide kernel below 2048, whose split tail tiles the
+// 4-wave kernel would not split (both layouts then sum in one order).
+constexpr int kW4PMinK = 1024;
 
 template <int BM, int MODE>
 static hipError_t run_bf16(GArgs g, hipStream_t st) {
@@ -2113,7 +2119,8 @@ static hipError_t run_bf16(GArgs g, hipStream_t st) {
     const bool offsets_fit = g.a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
     // 256-row tiles with a long K (a multiple of 64): the 4-wave kernel
     if constexpr (BM == 256) {
-        if (offsets_fit && g.K % 64 == 0 && g.K >= kW4MinK && g.Nout % 8 == 0 && ((uintptr_t)g.C & 15) == 0 && !g.kspan)
+        if (offsets_fit && g.K % 64 == 0 && g.K >= (g.b_packed && !gated_mode(MODE) ? kW4PMinK : kW4MinK) && g.Nout % 8 == 0 &&
+            ((uintptr_t)g.C & 15) == 0 && !g.kspan)
             return run_w4<MODE>(g, st);
     }
     // otherwise the 64-wide-stage kernel whenever K allows it (K a multiple of
