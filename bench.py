@@ -284,6 +284,9 @@ def shard_bench(args):
         cfg = dict(b, T=N, h=d, H=1, E=G, K=1, n_shared=0, has_wo=0, logit_bias=None, select_bias=None, **DENSE)
         log(f"[bench] shard {sname}: {G} groups x {rows} rows, d={d}, f={cfg['f']}")
         inp = inputs.make_inputs(cfg, "cuda", seed=0)
+        if not args.row_major:  # as the layer is timed: expert weights in fragment order
+            inp = moe.pack_weights(inp)
+            cfg = dict(cfg, packed=1)
         desc = moe.desc_from_cfg(cfg)
         offsets = torch.arange(0, N + 1, rows, dtype=torch.int32, device="cuda")
         dt = inputs.torch_dtype(cfg)
@@ -301,7 +304,8 @@ def shard_bench(args):
         n_act = 2 if cfg["act"] == "swiglu" else 1
         flops = 2.0 * N * d * cfg["f"] * (n_act + 1)
         tfs = flops / (ms * 1e-3) / 1e12
-        res.append({"shard": sname, "groups": G, "rows_per_group": rows, "d": d, "f": cfg["f"], "ffn_ms": ms,
+        res.append({"shard": sname, "weights": "row-major" if args.row_major else "fragment order",
+                    "groups": G, "rows_per_group": rows, "d": d, "f": cfg["f"], "ffn_ms": ms,
                     "tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS})
         del inp, h_tmp, y_perm, ws
         torch.cuda.empty_cache()
