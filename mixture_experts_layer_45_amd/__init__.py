@@ -158,6 +158,9 @@ def moe_pack_weights(w, w_packed, stream=None):
     fragment order."""
     if w.dim() < 2 or w.shape != w_packed.shape or w.dtype != w_packed.dtype:
         raise ValueError("w and w_packed must have one shape [..., n_out, k] and one dtype")
+    import torch
+    if w.dtype != torch.bfloat16:
+        raise ValueError("fragment order is defined for bf16 weights")
     n_out, k = int(w.shape[-2]), int(w.shape[-1])
     n_mat = w.numel() // (n_out * k) if n_out * k else 0
     _check(lib().moe_pack_weights(_ptr(w), _ptr(w_packed), int(n_mat), n_out, k, _stream(stream)))
