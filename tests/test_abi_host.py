@@ -160,6 +160,14 @@ def test_pack_weights_validates_before_launch():
     assert "aligned" in L.moe_last_error().decode()
 
 
+def test_pack_binding_refuses_other_dtypes_and_shapes():
+    import torch
+    with pytest.raises(ValueError):
+        moe.moe_pack_weights(torch.zeros(2, 32, 16), torch.zeros(2, 32, 16))  # fp32
+    with pytest.raises(ValueError):
+        moe.moe_pack_weights(torch.zeros(2, 32, 16, dtype=torch.bfloat16), torch.zeros(2, 16, 32, dtype=torch.bfloat16))
+
+
 def test_permute_noalloc_validates_before_launch():
     L = _ffi.lib()
     one = C.c_void_p(4096)
