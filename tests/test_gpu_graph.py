@@ -58,12 +58,17 @@ def _capture(fn):
     return g
 
 
+@pytest.mark.parametrize("packed", [0, 1], ids=["row_major", "fragment_order"])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_forward_graph_replays_match_eager(case):
+def test_forward_graph_replays_match_eager(case, packed):
     name, over = CASES[case]
     cfg = inputs.variant(name, **over)
-    G.log(f"[graph] forward {case}")
+    G.log(f"[graph] forward {case} packed={packed}")
     inp = G.dev_inputs(cfg)
+    if packed:  # the expert weights in fragment order, as bench.py times the layer
+        cfg = dict(cfg, packed=1)
+        inp = moe.pack_weights(inp)
+        torch.cuda.synchronize()
     x_a = inp["x"].clone()
     x_b = G.dev_inputs(cfg, seed=5)["x"]
     d = moe.desc_from_cfg(cfg)
